@@ -1,0 +1,248 @@
+"""Float64 CPU oracle for the gated delta-rule state step (test infrastructure).
+
+Only the test-suite, the smoke check and the CPU-baseline leg of the benchmark
+import this package.  The HIP library never uses it; the two share no code.
+Every routine here is a thin ctypes wrapper around ``oracle.c``, which cites the
+passage each function follows.  Array arguments are converted (exactly) to the
+C types the functions take: float64 for recurrence values, the stored integer
+or FP16 bit patterns for the packed formats.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+          "-shared", "-fvisibility=hidden", "-Wall", "-Wextra"]
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so (plain gcc, no GPU code)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        _lib = ctypes.CDLL(_LIB)
+        _declare(_lib)
+    return _lib
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_L = ctypes.c_long
+
+
+def _declare(L):
+    L.orc_gdn_step.argtypes = [_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
+    L.orc_kda_step.argtypes = L.orc_gdn_step.argtypes
+    L.orc_replay.argtypes = [_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P]
+    L.orc_half_to_double.argtypes = [ctypes.c_uint16]
+    L.orc_half_to_double.restype = ctypes.c_double
+    L.orc_double_to_half.argtypes = [ctypes.c_double]
+    L.orc_double_to_half.restype = ctypes.c_uint16
+    L.orc_quantize_row_int8.argtypes = [_P, _I, _P, _P]
+    L.orc_damp_quantize.argtypes = [_P, _I, _I, _I, _I, _P, _I, _P, _P, _P]
+    L.orc_damp_dequantize.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _I, _P]
+    L.orc_damp_step.argtypes = [_P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I,
+                                _P, _P, _P, _P, _I, _P, _P]
+    L.orc_dasc_plan.argtypes = [_P, _I, _I, _P, _P]
+    L.orc_dasc_plan.restype = _I
+    L.orc_dasc_pack.argtypes = [_P, _L, _I, _I, _I, _L, _P, _P, _I, _P, _P, _I, _P, _I]
+    L.orc_dasc_restore.argtypes = [_P, _I, _I, _P, _P, _I, _I, _L, _P, _P, _I, _P, _L, _I]
+
+
+def _f64(x):
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _i32(x):
+    return None if x is None else np.ascontiguousarray(x, dtype=np.int32)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _need_f64_inplace(a, name):
+    if not (isinstance(a, np.ndarray) and a.dtype == np.float64 and a.flags.c_contiguous):
+        raise TypeError(f"{name} must be a C-contiguous float64 array (updated in place)")
+
+
+def delta_step(state, q, k, v, alpha, beta, *, per_channel, slot=None, want_out=True):
+    """One GDN (per_channel=False) or KDA (per_channel=True) step.
+
+    state: float64 [S, H, dk, dv], updated in place.  q, k [B, H, dk]; v [B, H, dv];
+    alpha [B, H] or [B, H, dk]; beta [B, H].  Returns out [B, H, dv] (float64);
+    rows of skipped requests are NaN.
+    """
+    _need_f64_inplace(state, "state")
+    S, H, dk, dv = state.shape
+    q, k, v, alpha, beta = map(_f64, (q, k, v, alpha, beta))
+    B = q.shape[0]
+    slot = _i32(slot)
+    out = np.full((B, H, dv), np.nan) if want_out else None
+    fn = lib().orc_kda_step if per_channel else lib().orc_gdn_step
+    fn(_ptr(state), S, _ptr(slot), B, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+       _ptr(beta), _ptr(out))
+    return out
+
+
+def gdn_step(state, q, k, v, alpha, beta, slot=None, want_out=True):
+    return delta_step(state, q, k, v, alpha, beta, per_channel=False, slot=slot,
+                      want_out=want_out)
+
+
+def kda_step(state, q, k, v, alpha, beta, slot=None, want_out=True):
+    return delta_step(state, q, k, v, alpha, beta, per_channel=True, slot=slot,
+                      want_out=want_out)
+
+
+def replay(state, q, k, v, alpha, beta, n_accept, *, per_channel, slot=None, want_out=True):
+    """Advance each request's state by its first n_accept[b] draft tokens.
+
+    q, k [B, K, H, dk]; v [B, K, H, dv]; alpha [B, K, H] or [B, K, H, dk];
+    beta [B, K, H].  Returns out [B, K, H, dv] with NaN where t >= n_b.
+    """
+    _need_f64_inplace(state, "state")
+    S, H, dk, dv = state.shape
+    q, k, v, alpha, beta = map(_f64, (q, k, v, alpha, beta))
+    B, K = q.shape[:2]
+    slot = _i32(slot)
+    n_accept = _i32(n_accept)
+    out = np.full((B, K, H, dv), np.nan) if want_out else None
+    lib().orc_replay(_ptr(state), S, _ptr(slot), B, H, dk, dv, K, _ptr(q), _ptr(k), _ptr(v),
+                     _ptr(alpha), int(bool(per_channel)), _ptr(beta), _ptr(n_accept), _ptr(out))
+    return out
+
+
+# --------------------------------------------------------------------- FP16
+
+def half_to_double(bits):
+    bits = np.asarray(bits, dtype=np.uint16)
+    f = lib().orc_half_to_double
+    return np.array([f(int(b)) for b in bits.ravel()], dtype=np.float64).reshape(bits.shape)
+
+
+def double_to_half(x):
+    x = np.asarray(x, dtype=np.float64)
+    f = lib().orc_double_to_half
+    return np.array([f(float(v)) for v in x.ravel()], dtype=np.uint16).reshape(x.shape)
+
+
+def quantize_row_int8(x):
+    """Returns (codes int8 [n], scale float32) for one row."""
+    x = _f64(x)
+    codes = np.zeros(x.shape[0], dtype=np.int8)
+    scale = np.zeros(1, dtype=np.float32)
+    lib().orc_quantize_row_int8(_ptr(x), x.shape[0], _ptr(codes), _ptr(scale))
+    return codes, scale[0]
+
+
+# --------------------------------------------------------------------- DAMP
+
+def damp_alloc(S, H, dk, dv, K_hi):
+    return (np.zeros((S, H, K_hi, dv), np.uint16), np.zeros((S, H, dk - K_hi, dv), np.int8),
+            np.zeros((S, H, dk - K_hi), np.float32))
+
+
+def damp_quantize(state, key_perm, K_hi):
+    state = _f64(state)
+    S, H, dk, dv = state.shape
+    hi, lo, sc = damp_alloc(S, H, dk, dv, K_hi)
+    kp = _i32(key_perm)
+    lib().orc_damp_quantize(_ptr(state), S, H, dk, dv, _ptr(kp), K_hi, _ptr(hi), _ptr(lo),
+                            _ptr(sc))
+    return hi, lo, sc
+
+
+def damp_dequantize(hi, lo, sc, key_perm, K_hi, dk):
+    S, H = sc.shape[:2]
+    dv = lo.shape[-1] if lo.size else hi.shape[-1]
+    hi = np.ascontiguousarray(hi, np.uint16)
+    lo = np.ascontiguousarray(lo, np.int8)
+    sc = np.ascontiguousarray(sc, np.float32)
+    kp = _i32(key_perm)
+    out = np.zeros((S, H, dk, dv), np.float64)
+    lib().orc_damp_dequantize(_ptr(hi), _ptr(lo), _ptr(sc), S, H, dk, dv, _ptr(kp), K_hi,
+                              _ptr(out))
+    return out
+
+
+def damp_step(hi, lo, sc, key_perm, K_hi, q, k, v, alpha, beta, *, per_channel, slot=None,
+              want_out=True):
+    """One step of the quantised recurrence on the packed state (in place)."""
+    for a, dt, nm in ((hi, np.uint16, "hi"), (lo, np.int8, "lo"), (sc, np.float32, "scale")):
+        if not (isinstance(a, np.ndarray) and a.dtype == dt and a.flags.c_contiguous):
+            raise TypeError(f"{nm} must be a C-contiguous {np.dtype(dt).name} array")
+    S, H = sc.shape[:2]
+    q, k, v, alpha, beta = map(_f64, (q, k, v, alpha, beta))
+    B, _, dk = q.shape
+    dv = v.shape[-1]
+    kp = _i32(key_perm)
+    slot = _i32(slot)
+    out = np.full((B, H, dv), np.nan) if want_out else None
+    lib().orc_damp_step(_ptr(hi), _ptr(lo), _ptr(sc), S, _ptr(kp), K_hi, _ptr(slot), B, H, dk,
+                        dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), int(bool(per_channel)),
+                        _ptr(beta), _ptr(out))
+    return out
+
+
+# --------------------------------------------------------------------- dasc
+
+def dasc_plan(mask):
+    """mask uint8 [L, n_units] -> (offsets int32 [L+1], unit_index int32 [R_total])."""
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    L, n = mask.shape
+    offsets = np.zeros(L + 1, np.int32)
+    idx = np.zeros(max(1, L * n), np.int32)
+    R = lib().orc_dasc_plan(_ptr(mask), L, n, _ptr(offsets), _ptr(idx))
+    return offsets, idx[:R].copy()
+
+
+def dasc_pack(active, offsets, unit_index, src_slot, dst_slot, S_ckpt):
+    """active uint8 [L, S_act, n_units, unit_bytes] -> packed [S_ckpt, R_total, unit_bytes]
+    (slots not named in dst_slot stay zero)."""
+    active = np.ascontiguousarray(active, np.uint8)
+    L, S_act, n_units, ub = active.shape
+    offsets, unit_index = _i32(offsets), _i32(unit_index)
+    R = int(offsets[-1])
+    src, dst = _i32(src_slot), _i32(dst_slot)
+    packed = np.zeros((S_ckpt, R, ub), np.uint8)
+    lib().orc_dasc_pack(_ptr(active), S_act * n_units * ub, S_act, L, n_units, ub,
+                        _ptr(offsets), _ptr(unit_index), R, _ptr(src), _ptr(dst), len(src),
+                        _ptr(packed), S_ckpt)
+    return packed
+
+
+def dasc_restore(packed, offsets, unit_index, L, n_units, src_slot, dst_slot, active_out):
+    """Restore into active_out uint8 [L, S_dst, n_units, unit_bytes] (in place)."""
+    if not (isinstance(active_out, np.ndarray) and active_out.dtype == np.uint8
+            and active_out.flags.c_contiguous):
+        raise TypeError("active_out must be a C-contiguous uint8 array")
+    packed = np.ascontiguousarray(packed, np.uint8)
+    S_ckpt, R, ub = packed.shape
+    _, S_dst, n_u, ub2 = active_out.shape
+    assert n_u == n_units and ub2 == ub
+    offsets, unit_index = _i32(offsets), _i32(unit_index)
+    src, dst = _i32(src_slot), _i32(dst_slot)
+    lib().orc_dasc_restore(_ptr(packed), S_ckpt, R, _ptr(offsets), _ptr(unit_index), L,
+                           n_units, ub, _ptr(src), _ptr(dst), len(src), _ptr(active_out),
+                           S_dst * n_units * ub, S_dst)
+    return active_out

@@ -1,0 +1,419 @@
+/*
+ * Reference oracle for the gated delta-rule recurrent-state step and the state
+ * formats around it.  TEST INFRASTRUCTURE ONLY: the product path (the HIP
+ * library) never links, loads or calls this file.  Only the test-suite, the
+ * smoke check and the CPU-baseline leg of the benchmark use it.
+ *
+ * Rules this file keeps:
+ *   - plain sequential C, float64 for all recurrence arithmetic, sums taken in
+ *     increasing index order, built without fast-math and without FP
+ *     contraction (-ffp-contract=off), so every line can be checked by eye
+ *     against the equation it cites;
+ *   - where the pages fix a narrower precision (the INT8 quantiser's maximum,
+ *     division and rounding are FP32; the stored scale is FP32; the
+ *     high-precision rows are FP16), that precision is used here too;
+ *   - no blocking, fusion or reordering beyond what the cited definition says.
+ *
+ * Sources (page title, section / equation):
+ *   [DAMP]  "DAMP: Decay-Aware Mixed-Precision Recurrent-State Quantization"
+ *   [dasc]  "dasc: Decay-Aware State Compression for Hybrid Linear-Attention
+ *            Serving"
+ *   [K3]    "Serving recurrent attention" (long-form explainer on Kimi K3),
+ *           part "Speculative decoding without state snapshots"
+ *
+ * State orientation: one head's state is S in R^{dk x dv}, row u = key channel
+ * u, as in [DAMP] §3.1.  [dasc] §3.1 Eq. (1) writes the transpose (dv x dk);
+ * transposing that equation gives [DAMP] Eq. (2) exactly.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_API __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------------------ */
+/* One head, one token: [DAMP] §3.1 Eq. (1)-(2).                              */
+/*                                                                            */
+/*   S_t = (I - beta k k^T) Lambda S_{t-1} + beta k v^T ,   o_t = S_t^T q      */
+/*                                                                            */
+/* Lambda = diag(a_0 .. a_{dk-1}); GDN passes the same a for every channel,   */
+/* KDA one a per key channel ([DAMP] §3.1, [dasc] §3.1 Eq. (1)).             */
+/* Expanding the product: with S' = Lambda S_{t-1},                          */
+/*   (I - beta k k^T) S' + beta k v^T = S' + k (beta (v - S'^T k))^T,         */
+/* so the step is: decay, delta r = S'^T k, u = beta (v - r), rank-1 write    */
+/* S = S' + k u^T, and the readout of the UPDATED state ([DAMP] Eq. (1)).    */
+/* ------------------------------------------------------------------------ */
+static void orc_step_head(double *S, int dk, int dv, const double *q,
+                          const double *k, const double *v, const double *a,
+                          double beta, double *o /* may be NULL */)
+{
+    /* decay: S'[i][j] = a_i * S[i][j] */
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j)
+            S[(long)i * dv + j] = a[i] * S[(long)i * dv + j];
+
+    /* delta correction and rank-1 write, one value column j at a time:
+       r_j = sum_i k_i S'[i][j]  (increasing i);  u_j = beta (v_j - r_j);
+       S[i][j] = S'[i][j] + k_i u_j */
+    for (int j = 0; j < dv; ++j) {
+        double r = 0.0;
+        for (int i = 0; i < dk; ++i)
+            r = r + k[i] * S[(long)i * dv + j];
+        double u = beta * (v[j] - r);
+        for (int i = 0; i < dk; ++i)
+            S[(long)i * dv + j] = S[(long)i * dv + j] + k[i] * u;
+    }
+
+    /* readout from the updated state: o_j = sum_i q_i S[i][j] */
+    if (o) {
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i)
+                acc = acc + q[i] * S[(long)i * dv + j];
+            o[j] = acc;
+        }
+    }
+}
+
+/* Map request b to its state slot: identity when slot == NULL; a negative or
+   out-of-range entry means "padding request, skip". */
+static long orc_slot(const int32_t *slot, int b, int n_slots)
+{
+    long s = slot ? (long)slot[b] : (long)b;
+    if (s < 0 || s >= n_slots) return -1;
+    return s;
+}
+
+/* GDN decode step over a batch ([DAMP] §3.1 Eq. (2), scalar decay per head).
+   state  [n_slots, H, dk, dv];  q, k [B, H, dk];  v [B, H, dv];
+   alpha  [B, H];  beta [B, H];  out [B, H, dv] (rows of skipped requests are
+   left untouched; out may be NULL). */
+ORC_API void orc_gdn_step(double *state, int n_slots, const int32_t *slot, int B,
+                          int H, int dk, int dv, const double *q, const double *k,
+                          const double *v, const double *alpha, const double *beta,
+                          double *out)
+{
+    double *a = (double *)malloc(sizeof(double) * dk);
+    for (int b = 0; b < B; ++b) {
+        long s = orc_slot(slot, b, n_slots);
+        if (s < 0) continue;
+        for (int h = 0; h < H; ++h) {
+            long bh = (long)b * H + h;
+            for (int i = 0; i < dk; ++i) a[i] = alpha[bh];
+            orc_step_head(state + (s * H + h) * (long)dk * dv, dk, dv, q + bh * dk,
+                          k + bh * dk, v + bh * dv, a, beta[bh],
+                          out ? out + bh * dv : NULL);
+        }
+    }
+    free(a);
+}
+
+/* KDA decode step over a batch ([DAMP] §3.1 Eq. (2) with
+   Lambda = diag(exp g) = diag(alpha); [dasc] §3.1 Eq. (1)).
+   Same layout as orc_gdn_step except alpha [B, H, dk]. */
+ORC_API void orc_kda_step(double *state, int n_slots, const int32_t *slot, int B,
+                          int H, int dk, int dv, const double *q, const double *k,
+                          const double *v, const double *alpha, const double *beta,
+                          double *out)
+{
+    for (int b = 0; b < B; ++b) {
+        long s = orc_slot(slot, b, n_slots);
+        if (s < 0) continue;
+        for (int h = 0; h < H; ++h) {
+            long bh = (long)b * H + h;
+            orc_step_head(state + (s * H + h) * (long)dk * dv, dk, dv, q + bh * dk,
+                          k + bh * dk, v + bh * dv, alpha + bh * dk, beta[bh],
+                          out ? out + bh * dv : NULL);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Replay of accepted draft projections ([K3], "Speculative decoding without  */
+/* state snapshots"): the verify pass cached the projected inputs of K draft  */
+/* tokens; once n_b of them are accepted, the state is advanced by exactly    */
+/* those n_b tokens, in draft order, with the ordinary step.  n_b is clamped  */
+/* to [0, K].                                                                 */
+/*   q, k [B, K, H, dk];  v [B, K, H, dv];  alpha [B, K, H] (GDN) or         */
+/*   [B, K, H, dk] (KDA, per_channel != 0);  beta [B, K, H];                 */
+/*   out [B, K, H, dv] or NULL; rows t >= n_b are left untouched.            */
+/* ------------------------------------------------------------------------ */
+ORC_API void orc_replay(double *state, int n_slots, const int32_t *slot, int B,
+                        int H, int dk, int dv, int K, const double *q,
+                        const double *k, const double *v, const double *alpha,
+                        int per_channel, const double *beta,
+                        const int32_t *n_accept, double *out)
+{
+    double *a = (double *)malloc(sizeof(double) * dk);
+    for (int b = 0; b < B; ++b) {
+        long s = orc_slot(slot, b, n_slots);
+        if (s < 0) continue;
+        int n = n_accept[b];
+        if (n < 0) n = 0;
+        if (n > K) n = K;
+        for (int t = 0; t < n; ++t) {
+            for (int h = 0; h < H; ++h) {
+                long bth = ((long)b * K + t) * H + h;
+                for (int i = 0; i < dk; ++i)
+                    a[i] = per_channel ? alpha[bth * dk + i] : alpha[bth];
+                orc_step_head(state + (s * H + h) * (long)dk * dv, dk, dv,
+                              q + bth * dk, k + bth * dk, v + bth * dv, a,
+                              beta[bth], out ? out + bth * dv : NULL);
+            }
+        }
+    }
+    free(a);
+}
+
+/* ------------------------------------------------------------------------ */
+/* IEEE-754 binary16, written from the format's definition (1 sign bit,      */
+/* 5 exponent bits with bias 15, 10 fraction bits, subnormals, round to      */
+/* nearest with ties to even).  Used for the FP16 rows of the mixed-precision */
+/* state ([DAMP] §5.2).                                                       */
+/* ------------------------------------------------------------------------ */
+ORC_API double orc_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)f, -24); /* subnormal: f * 2^-24 */
+    else if (e == 31)
+        mag = f ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(1024 + f), e - 25); /* (1 + f/1024) 2^(e-15) */
+    return sign ? -mag : mag;
+}
+
+ORC_API uint16_t orc_double_to_half(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    if (isnan(x)) return (uint16_t)(sign | 0x7e00);
+    double a = fabs(x);
+    /* 65504 is the largest finite half; the midpoint to the next binade
+       (65536) is 65520, which ties to the even neighbour, i.e. infinity. */
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7c00);
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range: value = m * 2^-24, m in [0, 1024] after rounding */
+        double m = nearbyint(ldexp(a, 24));
+        return (uint16_t)(sign | (uint16_t)m); /* m == 1024 encodes 2^-14 */
+    }
+    int e;
+    double f = frexp(a, &e);           /* a = f 2^e, f in [0.5, 1)        */
+    double m = nearbyint(ldexp(f, 11)); /* significand with 10 fraction bits */
+    int E = e - 1;                     /* a = (m / 1024) 2^E              */
+    if (m == 2048.0) { m = 1024.0; E += 1; }
+    if (E > 15) return (uint16_t)(sign | 0x7c00);
+    return (uint16_t)(sign | ((E + 15) << 10) | ((int)m - 1024));
+}
+
+/* ------------------------------------------------------------------------ */
+/* Symmetric INT8 row quantiser: [DAMP] §3.2 Eq. (5)-(6) with b = 8, made     */
+/* concrete by [dasc] App. E.1 Eq. (8): codes in [-127, 127], no zero point,  */
+/* scale floored at 1e-8, and the maximum, the division and the rounding      */
+/* computed in FP32 with the scale stored in FP32.  round() is taken as       */
+/* round-half-to-even (the IEEE default; the pages do not name the mode).     */
+/* ------------------------------------------------------------------------ */
+ORC_API void orc_quantize_row_int8(const double *x, int n, int8_t *code, float *scale)
+{
+    float amax = 0.0f;
+    for (int j = 0; j < n; ++j) {
+        float xf = (float)x[j];
+        float ax = fabsf(xf);
+        if (ax > amax) amax = ax;
+    }
+    float s = fmaxf(amax, 1e-8f) / 127.0f;
+    for (int j = 0; j < n; ++j) {
+        float y = (float)x[j] / s;
+        float r = nearbyintf(y);
+        if (r > 127.0f) r = 127.0f;
+        if (r < -127.0f) r = -127.0f;
+        code[j] = (int8_t)r;
+    }
+    *scale = s;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Mixed-precision packed state ([DAMP] §5.2, App. A.4): for each head the   */
+/* rows are reordered by key_perm so that packed row r holds key channel     */
+/* key_perm[h*dk + r]; rows r < K_hi are stored as FP16 in `hi`              */
+/* [S, H, K_hi, dv], rows r >= K_hi as INT8 codes in `lo`                    */
+/* [S, H, dk-K_hi, dv] with one FP32 scale per row in `scale`                */
+/* [S, H, dk-K_hi].  key_perm == NULL means identity order.                  */
+/* ------------------------------------------------------------------------ */
+static int orc_perm(const int32_t *key_perm, int h, int dk, int r)
+{
+    return key_perm ? key_perm[(long)h * dk + r] : r;
+}
+
+/* Reconstruct one head (hi/lo/scale point at that head's rows) into a
+   float64 dk x dv matrix in original channel order: an FP16 value becomes
+   its exact value, an INT8 code c with row scale s becomes c * s. */
+static void orc_damp_unpack_head(const uint16_t *hi, const int8_t *lo,
+                                 const float *scale, const int32_t *key_perm, int h,
+                                 int K_hi, int dk, int dv, double *S)
+{
+    for (int r = 0; r < dk; ++r) {
+        int u = orc_perm(key_perm, h, dk, r);
+        for (int j = 0; j < dv; ++j) {
+            double x;
+            if (r < K_hi)
+                x = orc_half_to_double(hi[(long)r * dv + j]);
+            else
+                x = (double)lo[(long)(r - K_hi) * dv + j] * (double)scale[r - K_hi];
+            S[(long)u * dv + j] = x;
+        }
+    }
+}
+
+/* Store one head: FP16 rows round the float64 value to the nearest half
+   (ties to even); INT8 rows use the row quantiser above. */
+static void orc_damp_pack_head(const double *S, const int32_t *key_perm, int h,
+                               int K_hi, int dk, int dv, uint16_t *hi, int8_t *lo,
+                               float *scale)
+{
+    for (int r = 0; r < dk; ++r) {
+        int u = orc_perm(key_perm, h, dk, r);
+        const double *row = S + (long)u * dv;
+        if (r < K_hi) {
+            for (int j = 0; j < dv; ++j)
+                hi[(long)r * dv + j] = orc_double_to_half(row[j]);
+        } else {
+            orc_quantize_row_int8(row, dv, lo + (long)(r - K_hi) * dv,
+                                  scale + (r - K_hi));
+        }
+    }
+}
+
+ORC_API void orc_damp_quantize(const double *state, int S, int H, int dk, int dv,
+                               const int32_t *key_perm, int K_hi, uint16_t *hi,
+                               int8_t *lo, float *scale)
+{
+    int nlo = dk - K_hi;
+    for (long sh = 0; sh < (long)S * H; ++sh) {
+        int h = (int)(sh % H);
+        orc_damp_pack_head(state + sh * dk * dv, key_perm, h, K_hi, dk, dv,
+                           hi + sh * K_hi * dv, lo + sh * nlo * dv, scale + sh * nlo);
+    }
+}
+
+ORC_API void orc_damp_dequantize(const uint16_t *hi, const int8_t *lo,
+                                 const float *scale, int S, int H, int dk, int dv,
+                                 const int32_t *key_perm, int K_hi, double *state)
+{
+    int nlo = dk - K_hi;
+    for (long sh = 0; sh < (long)S * H; ++sh) {
+        int h = (int)(sh % H);
+        orc_damp_unpack_head(hi + sh * K_hi * dv, lo + sh * nlo * dv, scale + sh * nlo,
+                             key_perm, h, K_hi, dk, dv, state + sh * dk * dv);
+    }
+}
+
+/* Quantised recurrence, [DAMP] §3.3 Eq. (7): S^q_t = Q(A_t S^q_{t-1} +
+   beta k v^T).  Reconstruct the stored state, run the float64 step of
+   Eq. (2), take the readout from the updated state before it is stored
+   again (App. A.4: update and readout in full precision, then requantise),
+   then store it back in the packed format.
+   alpha is [B, H] (decay_per_channel == 0, GDN) or [B, H, dk] (KDA), always in
+   original channel order, like q and k. */
+ORC_API void orc_damp_step(uint16_t *hi, int8_t *lo, float *scale, int n_slots,
+                           const int32_t *key_perm, int K_hi, const int32_t *slot,
+                           int B, int H, int dk, int dv, const double *q,
+                           const double *k, const double *v, const double *alpha,
+                           int decay_per_channel, const double *beta, double *out)
+{
+    int nlo = dk - K_hi;
+    double *S = (double *)malloc(sizeof(double) * dk * dv);
+    double *a = (double *)malloc(sizeof(double) * dk);
+    for (int b = 0; b < B; ++b) {
+        long s = orc_slot(slot, b, n_slots);
+        if (s < 0) continue;
+        for (int h = 0; h < H; ++h) {
+            long bh = (long)b * H + h;
+            long sh = s * H + h;
+            for (int i = 0; i < dk; ++i)
+                a[i] = decay_per_channel ? alpha[bh * dk + i] : alpha[bh];
+            orc_damp_unpack_head(hi + sh * K_hi * dv, lo + sh * nlo * dv,
+                                 scale + sh * nlo, key_perm, h, K_hi, dk, dv, S);
+            orc_step_head(S, dk, dv, q + bh * dk, k + bh * dk, v + bh * dv, a,
+                          beta[bh], out ? out + bh * dv : NULL);
+            orc_damp_pack_head(S, key_perm, h, K_hi, dk, dv, hi + sh * K_hi * dv,
+                               lo + sh * nlo * dv, scale + sh * nlo);
+        }
+    }
+    free(a);
+    free(S);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Ragged state checkpoints ([dasc] §4.1 and App. B, "Ragged (Scheme 2)").   */
+/* A unit is unit_bytes contiguous bytes: a whole head state for GDN, one    */
+/* key channel's dv values for KDA.  Layer l keeps r_l = sum of its mask;     */
+/* offsets o_0 = 0, o_{l+1} = o_l + r_l (0-based layers), and layer l owns    */
+/* flat positions [o_l, o_{l+1}).  Inside a layer, retained units are listed  */
+/* in ascending unit id (the pages do not fix the order).                     */
+/* ------------------------------------------------------------------------ */
+ORC_API int orc_dasc_plan(const uint8_t *mask, int L, int n_units, int32_t *offsets,
+                          int32_t *unit_index)
+{
+    int pos = 0;
+    offsets[0] = 0;
+    for (int l = 0; l < L; ++l) {
+        for (int u = 0; u < n_units; ++u)
+            if (mask[(long)l * n_units + u]) unit_index[pos++] = u;
+        offsets[l + 1] = pos;
+    }
+    return pos;
+}
+
+/* Store path ([dasc] App. B.1 "Runtime store", single-rank part): for each
+   pair n, copy every retained unit of active slot src_slot[n] into checkpoint
+   slot dst_slot[n] at its ragged position.  Layer l's active state is
+   [S_act, n_units, unit_bytes] starting layer_stride_bytes * l into `active`;
+   the checkpoint buffer is [S_ckpt, R_total, unit_bytes]. */
+ORC_API void orc_dasc_pack(const uint8_t *active, long layer_stride_bytes, int S_act,
+                           int L, int n_units, long unit_bytes, const int32_t *offsets,
+                           const int32_t *unit_index, int R_total,
+                           const int32_t *src_slot, const int32_t *dst_slot, int N,
+                           uint8_t *packed, int S_ckpt)
+{
+    (void)S_act;
+    (void)S_ckpt;
+    for (int n = 0; n < N; ++n) {
+        for (int l = 0; l < L; ++l) {
+            for (int p = offsets[l]; p < offsets[l + 1]; ++p) {
+                const uint8_t *src = active + (long)l * layer_stride_bytes +
+                                     ((long)src_slot[n] * n_units + unit_index[p]) * unit_bytes;
+                uint8_t *dst = packed + ((long)dst_slot[n] * R_total + p) * unit_bytes;
+                memcpy(dst, src, (size_t)unit_bytes);
+            }
+        }
+    }
+}
+
+/* Load path, no refresh ([dasc] §4.2 dasc-nr; App. B.2 "Insertion and
+   reuse"): the retained units are restored exactly and every omitted unit of
+   the destination slot reads as zero; the checkpoint itself is only read
+   ([K3] "copy the immutable checkpoint before updating"). */
+ORC_API void orc_dasc_restore(const uint8_t *packed, int S_ckpt, int R_total,
+                              const int32_t *offsets, const int32_t *unit_index, int L,
+                              int n_units, long unit_bytes, const int32_t *src_slot,
+                              const int32_t *dst_slot, int N, uint8_t *active_out,
+                              long layer_stride_bytes, int S_dst)
+{
+    (void)S_ckpt;
+    (void)S_dst;
+    for (int n = 0; n < N; ++n) {
+        for (int l = 0; l < L; ++l) {
+            uint8_t *layer = active_out + (long)l * layer_stride_bytes +
+                             (long)dst_slot[n] * n_units * unit_bytes;
+            memset(layer, 0, (size_t)(n_units * unit_bytes));
+            for (int p = offsets[l]; p < offsets[l + 1]; ++p) {
+                const uint8_t *src = packed + ((long)src_slot[n] * R_total + p) * unit_bytes;
+                memcpy(layer + (long)unit_index[p] * unit_bytes, src, (size_t)unit_bytes);
+            }
+        }
+    }
+}

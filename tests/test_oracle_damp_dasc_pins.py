@@ -1,0 +1,281 @@
+"""Pins for the oracle's mixed-precision (DAMP) codec and step and its ragged
+checkpoint (dasc) pack / restore.
+
+Sources: DAMP paper section 3.2 Eq. (5)-(6), section 3.3 Eq. (7)-(12), section 5.2
+and App. A.1 / A.4; dasc paper section 4.1 Eq. (6), section 4.2, App. B (Scheme 2)
+and App. E.1 Eq. (8).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import synth
+
+rng = np.random.default_rng
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- FP16
+
+def test_fp16_roundtrip_lossless_for_every_finite_half(orc):
+    bits = np.arange(65536, dtype=np.uint16)
+    vals = bits.view(np.float16)
+    finite = bits[np.isfinite(vals)]
+    assert finite.size == 63488
+    back = orc.double_to_half(orc.half_to_double(finite))
+    # -0 and +0 keep their sign bit
+    assert np.array_equal(back, finite)
+    np.testing.assert_array_equal(orc.half_to_double(finite), finite.view(np.float16).astype(np.float64))
+
+
+def test_fp16_rounding_matches_numpy_including_ties(orc):
+    """numpy's float64 -> float16 cast is an independent correctly rounded implementation."""
+    g = rng(20)
+    x = np.concatenate([
+        g.standard_normal(4000) * 10.0 ** g.integers(-9, 5, 4000),
+        # exact midpoints between neighbouring halves (ties -> even)
+        (np.arange(0, 2048, dtype=np.float64) + 0.5) * 2.0 ** -24,
+        (np.arange(1024, 2048, dtype=np.float64) + 0.5) * 2.0 ** -10,
+        np.array([65504.0, 65519.99, 65520.0, 2 ** -14, 2 ** -24, 2 ** -25, 2 ** -25 * 1.0001]),
+    ])
+    x = np.concatenate([x, -x])
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(orc.double_to_half(x), ref)
+
+
+# ---------------------------------------------------------------- INT8 rows
+
+def test_int8_row_quantiser_properties(orc):
+    g = rng(21)
+    for trial in range(200):
+        n = 128
+        x = g.standard_normal(n) * 10.0 ** g.uniform(-6, 2)
+        codes, s = orc.quantize_row_int8(x)
+        x32 = x.astype(np.float32)
+        amax = np.abs(x32).max()
+        assert s == np.float32(np.float32(amax) / np.float32(127))
+        assert np.abs(codes.astype(np.int32)).max() <= 127
+        # the row's largest magnitude maps to +-127
+        j = int(np.argmax(np.abs(x32)))
+        assert abs(int(codes[j])) == 127 and np.sign(codes[j]) == np.sign(x32[j])
+        # reconstruction error at most half a step (plus fp32 rounding of the division)
+        err = np.abs(x32.astype(np.float64) - codes.astype(np.float64) * np.float64(s))
+        assert err.max() <= 0.5 * s * (1 + 1e-6)
+        # codes are round-half-even of the fp32 quotient
+        qt = (x32 / np.float32(s)).astype(np.float32)
+        assert np.array_equal(codes, np.clip(np.rint(qt), -127, 127).astype(np.int8))
+
+
+def test_int8_exact_ties_round_to_even(orc):
+    """With the row maximum at 127 * 2^e the scale is exactly 2^e, so (k + 1/2) 2^e is an
+    exact tie; round() is read as the IEEE default, ties to even."""
+    for e in (-12, -3, 0):
+        halves = np.array([0.5, 1.5, 2.5, 3.5, 126.5, -0.5, -1.5, -2.5, -125.5])
+        x = np.concatenate([[127.0], halves]) * 2.0 ** e
+        codes, s = orc.quantize_row_int8(x)
+        assert s == np.float32(2.0 ** e)
+        assert codes.tolist() == [127, 0, 2, 2, 4, 126, 0, -2, -2, -126]
+
+
+def test_int8_zero_row_uses_scale_floor(orc):
+    codes, s = orc.quantize_row_int8(np.zeros(128))
+    assert not codes.any()
+    assert s == np.float32(np.float32(1e-8) / np.float32(127))
+
+
+def test_int8_quantiser_is_idempotent_on_reconstructed_rows(orc):
+    g = rng(22)
+    for _ in range(100):
+        x = g.standard_normal(128)
+        c1, s1 = orc.quantize_row_int8(x)
+        c2, s2 = orc.quantize_row_int8(c1.astype(np.float64) * np.float64(s1))
+        assert np.array_equal(c1, c2)
+        assert abs(float(s2) - float(s1)) <= float(np.spacing(np.float32(s1)))
+
+
+# ---------------------------------------------------------------- packed layout
+
+def test_damp_quantize_dequantize_layout(orc):
+    """Packed row r of head h holds key channel key_perm[h, r]; rows < K_hi are FP16."""
+    g = rng(23)
+    S_, H, dk, dv, K_hi = 2, 3, 16, 8, 4
+    state = g.standard_normal((S_, H, dk, dv))
+    perm = np.stack([g.permutation(dk) for _ in range(H)]).astype(np.int32)
+    hi, lo, sc = orc.damp_quantize(state, perm, K_hi)
+    back = orc.damp_dequantize(hi, lo, sc, perm, K_hi, dk)
+    for s in range(S_):
+        for h in range(H):
+            for r in range(dk):
+                u = perm[h, r]
+                if r < K_hi:
+                    ref16 = state[s, h, u].astype(np.float16)
+                    assert np.array_equal(hi[s, h, r], ref16.view(np.uint16))
+                    np.testing.assert_array_equal(back[s, h, u], ref16.astype(np.float64))
+                else:
+                    c, sc1 = orc.quantize_row_int8(state[s, h, u])
+                    assert np.array_equal(lo[s, h, r - K_hi], c) and sc[s, h, r - K_hi] == sc1
+                    np.testing.assert_array_equal(back[s, h, u], c * np.float64(sc1))
+
+
+def _step_inputs(g, B, H, dk, dv):
+    q = g.standard_normal((B, H, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = g.standard_normal((B, H, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = g.standard_normal((B, H, dv))
+    alpha = np.exp(-np.logaddexp(0, g.normal(-4, 2, (B, H, dk))))
+    beta = 1 / (1 + np.exp(-g.standard_normal((B, H))))
+    return q, k, v, alpha, beta
+
+
+def test_damp_all_fp16_rows_is_an_fp16_state_recurrence(orc):
+    """K_hi = dk: every step is the float64 update followed by FP16 rounding (numpy's cast)."""
+    g = rng(24)
+    B, H, dk, dv = 2, 2, 16, 16
+    S = g.standard_normal((B, H, dk, dv)) * 0.05
+    S = S.astype(np.float16).astype(np.float64)
+    perm = np.tile(np.arange(dk, dtype=np.int32), (H, 1))
+    hi, lo, sc = orc.damp_quantize(S, perm, dk)
+    for _ in range(6):
+        q, k, v, alpha, beta = _step_inputs(g, B, H, dk, dv)
+        o = orc.damp_step(hi, lo, sc, perm, dk, q, k, v, alpha, beta, per_channel=True)
+        o_ref = orc.kda_step(S, q, k, v, alpha, beta)
+        S = S.astype(np.float16).astype(np.float64)
+        np.testing.assert_array_equal(hi.view(np.float16).astype(np.float64), S)
+        np.testing.assert_array_equal(o, o_ref)
+
+
+def test_damp_all_int8_rows_meet_quantiser_bounds(orc):
+    """K_hi = 0: every stored row is the symmetric INT8 code of the updated float64 row."""
+    g = rng(25)
+    B, H, dk, dv = 2, 2, 16, 32
+    S = g.standard_normal((B, H, dk, dv)) * 0.05
+    hi, lo, sc = orc.damp_quantize(S, None, 0)
+    for _ in range(3):
+        deq = orc.damp_dequantize(hi, lo, sc, None, 0, dk)
+        q, k, v, alpha, beta = _step_inputs(g, B, H, dk, dv)
+        orc.damp_step(hi, lo, sc, None, 0, q, k, v, alpha, beta, per_channel=True)
+        orc.kda_step(deq, q, k, v, alpha, beta)  # the exact updated state before storing
+        x32 = deq.astype(np.float32)
+        amax = np.abs(x32).max(-1)
+        assert np.array_equal(sc, (np.maximum(amax, np.float32(1e-8)) / np.float32(127)))
+        err = np.abs(x32 - lo.astype(np.float64) * sc[..., None].astype(np.float64))
+        assert (err <= 0.5 * sc[..., None] * (1 + 1e-6)).all()
+
+
+def test_damp_trajectory_obeys_error_propagation_identity(orc):
+    """DAMP Eq. (8)-(12): with S the unquantised trajectory and S^q the stored one,
+    DeltaS_t = A_t DeltaS_{t-1} + R_t, where R_t = S^q_t - (A_t S^q_{t-1} + beta k v^T)."""
+    g = rng(26)
+    B, H, dk, dv, K_hi = 1, 2, 32, 32, 4
+    S = g.standard_normal((B, H, dk, dv)) * 0.05
+    perm = np.stack([g.permutation(dk) for _ in range(H)]).astype(np.int32)
+    hi, lo, sc = orc.damp_quantize(S, perm, K_hi)
+    Sq_prev = orc.damp_dequantize(hi, lo, sc, perm, K_hi, dk)
+    S = Sq_prev.copy()  # both trajectories start from the same reconstructed state
+    dS_prev = np.zeros_like(S)
+    for _ in range(5):
+        q, k, v, alpha, beta = _step_inputs(g, B, H, dk, dv)
+        orc.damp_step(hi, lo, sc, perm, K_hi, q, k, v, alpha, beta, per_channel=True)
+        orc.kda_step(S, q, k, v, alpha, beta)
+        Sq = orc.damp_dequantize(hi, lo, sc, perm, K_hi, dk)
+        for h in range(H):
+            A = (np.eye(dk) - beta[0, h] * np.outer(k[0, h], k[0, h])) @ np.diag(alpha[0, h])
+            R = Sq[0, h] - (A @ Sq_prev[0, h] + beta[0, h] * np.outer(k[0, h], v[0, h]))
+            np.testing.assert_allclose(Sq[0, h] - S[0, h], A @ dS_prev[0, h] + R, rtol=0,
+                                       atol=1e-14)
+            # R_t is a pure storage error: bounded by half an INT8 step or an FP16 ulp per row
+            assert np.abs(R).max() <= 0.51 * max(sc[0, h].max(), 1e-3 * np.abs(Sq[0, h]).max())
+        dS_prev = Sq - S
+        Sq_prev = Sq
+
+
+def _bits_per_value(dk, dv, K_hi, group):
+    """Storage bits per state value: FP16 rows, INT8 rows, FP32 scales per `group` values."""
+    bits = K_hi * dv * 16 + (dk - K_hi) * (dv * 8 + (dv // group) * 32)
+    return bits / (dk * dv)
+
+
+def test_storage_cost_matches_page_figures():
+    """DAMP reports 9.9 bits per value and a 69.1% cut vs FP32 for 16 FP16 key channels
+    and INT8 with one FP32 scale per 32 values (abstract, section 6.2 and App. A.1);
+    the per-row-scale layout of the serving workload costs 9.21875 bits."""
+    with open(os.path.join(GOLDEN, "damp_storage_figures.json")) as f:
+        gold = json.load(f)
+    b32 = _bits_per_value(128, 128, gold["K_hi"], 32)
+    assert round(b32, 1) == gold["bits_per_value"]
+    assert round(100 * (1 - b32 / 32), 1) == gold["storage_reduction_pct"]
+    assert _bits_per_value(128, 128, 16, 128) == 9.21875
+
+
+# ---------------------------------------------------------------- dasc
+
+def _active(g, L, S_, n_units, ub):
+    return g.integers(0, 256, size=(L, S_, n_units, ub), dtype=np.uint8)
+
+
+def test_dasc_plan_offsets_are_ragged_prefix_sums(orc):
+    g = rng(30)
+    mask = (g.random((5, 37)) < 0.4).astype(np.uint8)
+    mask[2] = 0  # an empty layer
+    offsets, idx = orc.dasc_plan(mask)
+    r = mask.sum(1)
+    assert offsets[0] == 0 and np.array_equal(np.diff(offsets), r)
+    assert offsets[-1] == r.sum() == idx.size
+    for l in range(5):
+        assert np.array_equal(idx[offsets[l]:offsets[l + 1]], np.flatnonzero(mask[l]))
+
+
+def test_dasc_restore_of_pack_keeps_retained_and_zeroes_the_rest(orc):
+    g = rng(31)
+    L, S_, n_units, ub = 3, 6, 10, 32
+    active = _active(g, L, S_, n_units, ub)
+    mask = (g.random((L, n_units)) < 0.5).astype(np.uint8)
+    offsets, idx = orc.dasc_plan(mask)
+    src = np.array([5, 0, 3], np.int32)
+    ck = np.array([1, 2, 0], np.int32)
+    packed = orc.dasc_pack(active, offsets, idx, src, ck, S_ckpt=3)
+    assert packed.shape == (3, mask.sum(), ub)
+    out = g.integers(0, 256, size=(L, 4, n_units, ub), dtype=np.uint8)
+    before = out.copy()
+    dst = np.array([2, 0, 3], np.int32)
+    orc.dasc_restore(packed, offsets, idx, L, n_units, ck, dst, out)
+    for n in range(3):
+        for l in range(L):
+            keep = mask[l].astype(bool)
+            assert np.array_equal(out[l, dst[n], keep], active[l, src[n], keep])
+            assert not out[l, dst[n], ~keep].any()
+    assert np.array_equal(out[:, 1], before[:, 1])  # slot not named is untouched
+
+
+def test_dasc_full_mask_is_a_copy_and_empty_mask_zero_fills(orc):
+    g = rng(32)
+    L, S_, n_units, ub = 2, 3, 4, 16
+    active = _active(g, L, S_, n_units, ub)
+    src = np.arange(3, dtype=np.int32)
+    for full in (True, False):
+        mask = np.full((L, n_units), 1 if full else 0, np.uint8)
+        offsets, idx = orc.dasc_plan(mask)
+        packed = orc.dasc_pack(active, offsets, idx, src, src, S_ckpt=3)
+        out = np.full_like(active, 0xAB)
+        orc.dasc_restore(packed, offsets, idx, L, n_units, src, src, out)
+        if full:
+            assert np.array_equal(out, active)
+        else:
+            assert packed.size == 0 and not out.any()
+
+
+def test_dasc_compression_ratios_closed_form(orc):
+    """dasc Eq. (6) and App. B: C_temp^rag = sum n_l / sum r_l, C_temp^pad = sum n_l /(L R_max),
+    and the ragged gain R_max / r_bar, for the checkpoint workload's seeded masks."""
+    cfg = synth.CONFIGS["dasc_gdn"]
+    mask = synth.dasc_masks(cfg)
+    offsets, _ = orc.dasc_plan(mask)
+    r = np.diff(offsets)
+    L, n = mask.shape
+    assert offsets[-1] == 64 and r.min() >= 8 and r.max() <= 24
+    c_rag = L * n / offsets[-1]
+    c_pad = L * n / (L * r.max())
+    assert c_rag == 2.0
+    assert np.isclose(c_rag / c_pad, r.max() / r.mean())
