@@ -1,0 +1,287 @@
+"""Python binding of libhla.so, the gfx950 HIP library declared in include/hla.h.
+
+Argument marshalling only: every function here checks tensor dtypes, devices and
+shapes, passes raw device pointers, sizes and the current HIP stream to the C
+entry point of the same name, and raises on a non-zero status.  All arithmetic
+runs in the library's kernels.  There is no CPU fallback: if libhla.so is not
+built, every call raises.
+
+PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from ._build import LIB as LIB_PATH
+
+HLA_F32, HLA_BF16 = 0, 1
+DECAY_SCALAR, DECAY_VECTOR = 0, 1
+DEVERR_SLOT, DEVERR_ACCEPT, DEVERR_PLAN = 1, 2, 4
+
+# ctypes signature of every entry point in include/hla.h
+_P, _I, _L = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+SIGNATURES = {
+    "hla_status_str": ([_I], ctypes.c_char_p),
+    "hla_version": ([], _I),
+    "gdn_step": ([_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _I, _P, _P], _I),
+    "kda_step": ([_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _I, _P, _P], _I),
+    "damp_step": ([_P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P,
+                   _I, _P, _P], _I),
+    "damp_quantize": ([_P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P], _I),
+    "damp_dequantize": ([_P, _P, _P, _I, _I, _I, _I, _P, _I, _P, _P], _I),
+    "dasc_plan": ([_P, _I, _I, _P, _P, _I, _P, _P], _I),
+    "dasc_pack": ([_P, _L, _I, _I, _I, _L, _P, _P, _I, _P, _P, _I, _P, _I, _P, _P], _I),
+    "dasc_restore": ([_P, _I, _I, _P, _I, _I, _L, _P, _P, _I, _P, _L, _I, _P, _P], _I),
+    "replay_accepted": ([_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, _P, _I,
+                         _P, _P], _I),
+}
+
+
+class HLAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: status {status} ({status_str(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libhla.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.argtypes, f.restype = args, res
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().hla_status_str(status).decode()
+
+
+def _call(name: str, *args) -> None:
+    rc = getattr(lib(), name)(*args)
+    if rc != 0:
+        raise HLAError(name, rc)
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtypes, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
+    return t
+
+
+def _code(dtype) -> int:
+    torch = _torch()
+    return {torch.float32: HLA_F32, torch.bfloat16: HLA_BF16}[dtype]
+
+
+def _in_dtypes():
+    torch = _torch()
+    return (torch.float32, torch.bfloat16)
+
+
+def _i32():
+    return (_torch().int32,)
+
+
+def _f32():
+    return (_torch().float32,)
+
+
+def _opt_out(out, shape, device, want_out):
+    torch = _torch()
+    if out is None and want_out:
+        out = torch.empty(shape, dtype=torch.float32, device=device)
+    if out is not None:
+        _dev(out, "out", _in_dtypes(), len(shape))
+    return out
+
+
+def _step(name, state, q, k, v, alpha, beta, out, slot, err_flag, stream, want_out):
+    _dev(state, "state", _f32(), 4)
+    S, H, dk, dv = state.shape
+    _dev(q, "q", _in_dtypes(), 3)
+    B = q.shape[0]
+    _dev(k, "k", (q.dtype,), 3)
+    _dev(v, "v", (q.dtype,), 3)
+    _dev(alpha, "alpha", _f32())
+    _dev(beta, "beta", _f32(), 2)
+    if slot is not None:
+        _dev(slot, "slot", _i32(), 1)
+    if err_flag is not None:
+        _dev(err_flag, "err_flag", _i32())
+    out = _opt_out(out, (B, H, dv), state.device, want_out)
+    _call(name, _ptr(state), S, _ptr(slot), B, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
+          _code(q.dtype), _ptr(alpha), _ptr(beta), _ptr(out),
+          _code(out.dtype) if out is not None else HLA_F32, _ptr(err_flag), _stream(stream))
+    return out
+
+
+def gdn_step(state, q, k, v, alpha, beta, out=None, slot=None, err_flag=None, stream=None,
+             want_out=True):
+    """GDN decode step in place on `state` [S,H,dk,dv] fp32; returns o [B,H,dv]."""
+    return _step("gdn_step", state, q, k, v, alpha, beta, out, slot, err_flag, stream, want_out)
+
+
+def kda_step(state, q, k, v, alpha, beta, out=None, slot=None, err_flag=None, stream=None,
+             want_out=True):
+    """KDA decode step (alpha [B,H,dk]) in place on `state`; returns o [B,H,dv]."""
+    return _step("kda_step", state, q, k, v, alpha, beta, out, slot, err_flag, stream, want_out)
+
+
+def replay_accepted(state, q, k, v, alpha, beta, n_accept, decay_kind, out=None, slot=None,
+                    err_flag=None, stream=None, want_out=True):
+    """Replay the first n_accept[b] of K cached draft projections into each state."""
+    _dev(state, "state", _f32(), 4)
+    S, H, dk, dv = state.shape
+    _dev(q, "q", _in_dtypes(), 4)
+    B, K = q.shape[:2]
+    _dev(k, "k", (q.dtype,), 4)
+    _dev(v, "v", (q.dtype,), 4)
+    _dev(alpha, "alpha", _f32())
+    _dev(beta, "beta", _f32(), 3)
+    _dev(n_accept, "n_accept", _i32(), 1)
+    if slot is not None:
+        _dev(slot, "slot", _i32(), 1)
+    if err_flag is not None:
+        _dev(err_flag, "err_flag", _i32())
+    out = _opt_out(out, (B, K, H, dv), state.device, want_out)
+    _call("replay_accepted", _ptr(state), S, _ptr(slot), B, H, dk, dv, K, _ptr(q), _ptr(k),
+          _ptr(v), _code(q.dtype), _ptr(alpha), int(decay_kind), _ptr(beta), _ptr(n_accept),
+          _ptr(out), _code(out.dtype) if out is not None else HLA_F32, _ptr(err_flag),
+          _stream(stream))
+    return out
+
+
+def damp_step(hi, lo, lo_scale, key_perm, K_hi, q, k, v, alpha, decay_kind, beta, out=None,
+              slot=None, err_flag=None, stream=None, want_out=True):
+    """One fused dequantise -> update -> requantise step on the packed state (in place)."""
+    torch = _torch()
+    _dev(hi, "hi", (torch.int16, torch.uint16, torch.float16), 4)
+    _dev(lo, "lo", (torch.int8,), 4)
+    _dev(lo_scale, "lo_scale", _f32(), 3)
+    S, H, _, dv = hi.shape
+    _dev(q, "q", _in_dtypes(), 3)
+    B, _, dk = q.shape
+    _dev(k, "k", (q.dtype,), 3)
+    _dev(v, "v", (q.dtype,), 3)
+    _dev(alpha, "alpha", _f32())
+    _dev(beta, "beta", _f32(), 2)
+    if key_perm is not None:
+        _dev(key_perm, "key_perm", _i32(), 2)
+    if slot is not None:
+        _dev(slot, "slot", _i32(), 1)
+    if err_flag is not None:
+        _dev(err_flag, "err_flag", _i32())
+    if lo.shape[2] != dk - K_hi or hi.shape[2] != K_hi:
+        raise ValueError("hi/lo row counts do not match K_hi and dk")
+    out = _opt_out(out, (B, H, dv), hi.device, want_out)
+    _call("damp_step", _ptr(hi), _ptr(lo), _ptr(lo_scale), S, _ptr(key_perm), K_hi, _ptr(slot),
+          B, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _code(q.dtype), _ptr(alpha), int(decay_kind),
+          _ptr(beta), _ptr(out), _code(out.dtype) if out is not None else HLA_F32,
+          _ptr(err_flag), _stream(stream))
+    return out
+
+
+def damp_alloc(S, H, dk, dv, K_hi, device="cuda"):
+    torch = _torch()
+    return (torch.empty((S, H, K_hi, dv), dtype=torch.int16, device=device),
+            torch.empty((S, H, dk - K_hi, dv), dtype=torch.int8, device=device),
+            torch.empty((S, H, dk - K_hi), dtype=torch.float32, device=device))
+
+
+def damp_quantize(state, key_perm, K_hi, hi=None, lo=None, lo_scale=None, stream=None):
+    _dev(state, "state", _f32(), 4)
+    S, H, dk, dv = state.shape
+    if hi is None:
+        hi, lo, lo_scale = damp_alloc(S, H, dk, dv, K_hi, state.device)
+    if key_perm is not None:
+        _dev(key_perm, "key_perm", _i32(), 2)
+    _call("damp_quantize", _ptr(state), S, H, dk, dv, _ptr(key_perm), K_hi, _ptr(hi), _ptr(lo),
+          _ptr(lo_scale), _stream(stream))
+    return hi, lo, lo_scale
+
+
+def damp_dequantize(hi, lo, lo_scale, key_perm, K_hi, dk, out=None, stream=None):
+    torch = _torch()
+    S, H, _, dv = hi.shape
+    if out is None:
+        out = torch.empty((S, H, dk, dv), dtype=torch.float32, device=hi.device)
+    _dev(out, "state", _f32(), 4)
+    if key_perm is not None:
+        _dev(key_perm, "key_perm", _i32(), 2)
+    _call("damp_dequantize", _ptr(hi), _ptr(lo), _ptr(lo_scale), S, H, dk, dv, _ptr(key_perm),
+          K_hi, _ptr(out), _stream(stream))
+    return out
+
+
+def dasc_plan(mask):
+    """Host plan from a uint8 numpy mask [L, n_units]: (offsets, unit_index, unit_pos, R_total)
+    as numpy int32 arrays."""
+    import numpy as np
+
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    L, n = mask.shape
+    offsets = np.zeros(L + 1, np.int32)
+    unit_index = np.zeros(max(1, L * n), np.int32)
+    unit_pos = np.zeros(L * n, np.int32)
+    R = ctypes.c_int32(0)
+    _call("dasc_plan", mask.ctypes.data, L, n, offsets.ctypes.data, unit_index.ctypes.data,
+          unit_index.size, unit_pos.ctypes.data, ctypes.byref(R))
+    return offsets, unit_index[:R.value].copy(), unit_pos.reshape(L, n), R.value
+
+
+def dasc_pack(active, layer_stride_bytes, S_act, L, n_units, unit_bytes, offsets, unit_index,
+              R_total, src_slot, dst_slot, packed, S_ckpt, err_flag=None, stream=None):
+    """Byte-level pack; `active` and `packed` are device tensors (any dtype)."""
+    for t, nm in ((offsets, "offsets"), (src_slot, "src_slot"), (dst_slot, "dst_slot")):
+        _dev(t, nm, _i32(), 1)
+    _call("dasc_pack", _ptr(active), int(layer_stride_bytes), S_act, L, n_units, int(unit_bytes),
+          _ptr(offsets), _ptr(unit_index) if unit_index.numel() else None, R_total,
+          _ptr(src_slot), _ptr(dst_slot), src_slot.numel(), _ptr(packed), S_ckpt,
+          _ptr(err_flag), _stream(stream))
+
+
+def dasc_restore(packed, S_ckpt, R_total, unit_pos, L, n_units, unit_bytes, src_slot, dst_slot,
+                 active_out, layer_stride_bytes, S_dst, err_flag=None, stream=None):
+    for t, nm in ((src_slot, "src_slot"), (dst_slot, "dst_slot")):
+        _dev(t, nm, _i32(), 1)
+    _dev(unit_pos, "unit_pos", _i32())
+    _call("dasc_restore", _ptr(packed), S_ckpt, R_total, _ptr(unit_pos), L, n_units,
+          int(unit_bytes), _ptr(src_slot), _ptr(dst_slot), src_slot.numel(), _ptr(active_out),
+          int(layer_stride_bytes), S_dst, _ptr(err_flag), _stream(stream))

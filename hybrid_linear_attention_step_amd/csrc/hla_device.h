@@ -1,0 +1,160 @@
+// Device-side helpers shared by the gfx950 kernels: element conversions,
+// 16-byte vector loads/stores and wave64 cross-lane reductions built from DPP
+// and the gfx950 permlane swaps (no LDS round trip, no ds_bpermute).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hla {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------ conversions
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float half_bits_to_f32(uint32_t bits16)
+{
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)bits16);
+}
+
+// float -> binary16 bits, round to nearest even (v_cvt_f16_f32 in the default
+// rounding mode).
+__device__ __forceinline__ uint32_t f32_to_half_bits(float f)
+{
+    return (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)f);
+}
+
+// ------------------------------------------------------------ loads / stores
+
+template <typename T>
+__device__ __forceinline__ T ld_nt(const T *p) { return __builtin_nontemporal_load(p); }
+
+template <typename T>
+__device__ __forceinline__ void st_nt(T *p, T v) { __builtin_nontemporal_store(v, p); }
+
+// Load N consecutive input elements (fp32 or bf16 bits) as float.  The
+// address must be 16-byte aligned; N a multiple of 4 (fp32) or 8 (bf16).
+template <int N>
+__device__ __forceinline__ void load_in(const float *p, float (&d)[N])
+{
+    static_assert(N % 4 == 0, "fp32 rows load in 16-byte pieces");
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+        f32x4 t = reinterpret_cast<const f32x4 *>(p)[i];
+        d[4 * i + 0] = t.x; d[4 * i + 1] = t.y; d[4 * i + 2] = t.z; d[4 * i + 3] = t.w;
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void load_in(const uint16_t *p, float (&d)[N])
+{
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+        for (int i = 0; i < N / 8; ++i) {
+            u32x4 t = reinterpret_cast<const u32x4 *>(p)[i];
+            d[8 * i + 0] = bf16_lo(t.x); d[8 * i + 1] = bf16_hi(t.x);
+            d[8 * i + 2] = bf16_lo(t.y); d[8 * i + 3] = bf16_hi(t.y);
+            d[8 * i + 4] = bf16_lo(t.z); d[8 * i + 5] = bf16_hi(t.z);
+            d[8 * i + 6] = bf16_lo(t.w); d[8 * i + 7] = bf16_hi(t.w);
+        }
+    } else {
+        static_assert(N == 4, "bf16 rows load in 8- or 16-byte pieces");
+        u32x2 t = *reinterpret_cast<const u32x2 *>(p);
+        d[0] = bf16_lo(t.x); d[1] = bf16_hi(t.x); d[2] = bf16_lo(t.y); d[3] = bf16_hi(t.y);
+    }
+}
+
+__device__ __forceinline__ float load_one(const float *p) { return *p; }
+__device__ __forceinline__ float load_one(const uint16_t *p) { return __uint_as_float((uint32_t)*p << 16); }
+
+// Store 4 consecutive outputs (fp32: 16 bytes, bf16: 8 bytes).
+__device__ __forceinline__ void store_out4(float *p, const float (&o)[4])
+{
+    f32x4 t = {o[0], o[1], o[2], o[3]};
+    *reinterpret_cast<f32x4 *>(p) = t;
+}
+__device__ __forceinline__ void store_out4(uint16_t *p, const float (&o)[4])
+{
+    u32x2 t = {f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16),
+               f32_to_bf16(o[2]) | (f32_to_bf16(o[3]) << 16)};
+    *reinterpret_cast<u32x2 *>(p) = t;
+}
+__device__ __forceinline__ void store_one(float *p, float o) { *p = o; }
+__device__ __forceinline__ void store_one(uint16_t *p, float o) { *p = (uint16_t)f32_to_bf16(o); }
+
+// ------------------------------------------------------------ lane exchange
+
+// DPP controls (gfx9 encoding).
+enum : int {
+    DPP_QUAD_XOR1 = 0xB1,     // quad_perm [1,0,3,2]
+    DPP_QUAD_XOR2 = 0x4E,     // quad_perm [2,3,0,1]
+    DPP_ROW_ROR8 = 0x128,     // rotate right by 8 within a 16-lane row == xor 8
+    DPP_ROW_MIRROR = 0x140,   // lane i <- lane 15-i within a row
+    DPP_ROW_HALF_MIRROR = 0x141 // lane i <- lane 7-i within each 8-lane half row
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum of lanes l and l^16 in every lane (gfx950 v_permlane16_swap: odd 16-lane
+// rows of the first operand trade places with even rows of the second).  The
+// operands are added in the same order in both lanes, so the pair holds
+// bitwise-identical sums.
+__device__ __forceinline__ float sum_xor16(float x)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor8(float x)
+{
+    // lane l reads l^8; fp add is commutative so both lanes get the same bits
+    return x + dpp<DPP_ROW_ROR8>(x);
+}
+
+// Sum over lane bits FIRST..5 (i.e. over the 64 >> FIRST lane groups that
+// share the low FIRST bits); every participating lane receives the total.
+template <int FIRST>
+__device__ __forceinline__ float sum_lane_bits(float x)
+{
+    static_assert(FIRST >= 3 && FIRST <= 6, "reductions start at lane bit 3, 4 or 5");
+    if constexpr (FIRST <= 3) x = sum_xor8(x);
+    if constexpr (FIRST <= 4) x = sum_xor16(x);
+    if constexpr (FIRST <= 5) x = sum_xor32(x);
+    return x;
+}
+
+// Maximum over the low NB lane bits (NB = 3: groups of 8 lanes, 4: groups
+// of 16).  max is exact, so any pairing pattern gives the same result.
+template <int NB>
+__device__ __forceinline__ float max_low_lane_bits(float x)
+{
+    static_assert(NB == 3 || NB == 4, "row groups of 8 or 16 lanes");
+    x = fmaxf(x, dpp<DPP_QUAD_XOR1>(x));
+    x = fmaxf(x, dpp<DPP_QUAD_XOR2>(x));
+    x = fmaxf(x, dpp<DPP_ROW_HALF_MIRROR>(x));
+    if constexpr (NB == 4) x = fmaxf(x, dpp<DPP_ROW_MIRROR>(x));
+    return x;
+}
+
+} // namespace hla

@@ -1,0 +1,194 @@
+// Host-only parts of the C ABI: status strings, argument validation and the
+// ragged checkpoint plan.  Nothing here calls the HIP runtime.
+#include <limits.h>
+#include <string.h>
+
+#include "hla.h"
+#include "hla_internal.h"
+
+namespace hla {
+
+static const size_t kMaxIndex = (size_t)INT_MAX;
+
+int check_step(const StepArgs &a, bool replay)
+{
+    if (a.B < 0 || a.H <= 0 || a.n_slots < 0) return HLA_ERR_SHAPE;
+    if (replay && (a.K < 1 || a.K > 16)) return HLA_ERR_SHAPE;
+    if (!dtype_ok(a.in_dtype) || !dtype_ok(a.out_dtype)) return HLA_ERR_DTYPE;
+    if (a.decay != HLA_DECAY_SCALAR && a.decay != HLA_DECAY_VECTOR) return HLA_ERR_DTYPE;
+    if (a.B == 0) return HLA_OK;
+    if (!a.state || !a.q || !a.k || !a.v || !a.alpha || !a.beta) return HLA_ERR_NULL;
+    if (replay && !a.n_accept) return HLA_ERR_NULL;
+    if (!a.slot && a.n_slots < a.B) return HLA_ERR_SHAPE;
+    if (!head_dim_ok(a.dk) || !head_dim_ok(a.dv)) return HLA_ERR_UNSUPPORTED;
+    if ((size_t)a.B * a.H > kMaxIndex) return HLA_ERR_SHAPE;
+    if (!aligned16(a.state) || !aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v) ||
+        (a.out && !aligned16(a.out)) || (a.decay == HLA_DECAY_VECTOR && !aligned16(a.alpha)))
+        return HLA_ERR_ALIGN;
+
+    const size_t tok = (size_t)a.B * a.K * a.H;  // (request, token, head) triples
+    const size_t es = dtype_bytes(a.in_dtype);
+    Range state{a.state, (size_t)a.n_slots * a.H * a.dk * a.dv * sizeof(float)};
+    Range out{a.out, tok * a.dv * dtype_bytes(a.out_dtype)};
+    Range ins[] = {
+        {a.q, tok * a.dk * es},
+        {a.k, tok * a.dk * es},
+        {a.v, tok * a.dv * es},
+        {a.alpha, tok * (a.decay == HLA_DECAY_VECTOR ? a.dk : 1) * sizeof(float)},
+        {a.beta, tok * sizeof(float)},
+        {a.slot, (size_t)a.B * sizeof(int32_t)},
+        {a.n_accept, (size_t)a.B * sizeof(int32_t)},
+    };
+    for (const Range &r : ins)
+        if (overlaps(state, r) || overlaps(out, r)) return HLA_ERR_ALIAS;
+    if (overlaps(state, out)) return HLA_ERR_ALIAS;
+    return HLA_OK;
+}
+
+int check_damp(const DampArgs &a)
+{
+    if (a.B < 0 || a.H <= 0 || a.n_slots < 0) return HLA_ERR_SHAPE;
+    if (!dtype_ok(a.in_dtype) || !dtype_ok(a.out_dtype)) return HLA_ERR_DTYPE;
+    if (a.decay != HLA_DECAY_SCALAR && a.decay != HLA_DECAY_VECTOR) return HLA_ERR_DTYPE;
+    if (a.B == 0) return HLA_OK;
+    if (!head_dim_ok(a.dk) || !head_dim_ok(a.dv)) return HLA_ERR_UNSUPPORTED;
+    if (a.K_hi < 0 || a.K_hi > a.dk) return HLA_ERR_SHAPE;
+    const int nlo = a.dk - a.K_hi;
+    if ((a.K_hi > 0 && !a.hi) || (nlo > 0 && (!a.lo || !a.lo_scale)) || !a.q || !a.k || !a.v ||
+        !a.alpha || !a.beta)
+        return HLA_ERR_NULL;
+    if (!a.slot && a.n_slots < a.B) return HLA_ERR_SHAPE;
+    if ((size_t)a.B * a.H > kMaxIndex) return HLA_ERR_SHAPE;
+    if ((a.hi && !aligned16(a.hi)) || (a.lo && !aligned16(a.lo)) || !aligned16(a.q) ||
+        !aligned16(a.k) || !aligned16(a.v) || (a.out && !aligned16(a.out)))
+        return HLA_ERR_ALIGN;
+    const size_t sh = (size_t)a.n_slots * a.H;
+    const size_t bh = (size_t)a.B * a.H;
+    const size_t es = dtype_bytes(a.in_dtype);
+    Range outs[] = {
+        {a.hi, sh * a.K_hi * a.dv * 2},
+        {a.lo, sh * nlo * a.dv},
+        {a.lo_scale, sh * nlo * sizeof(float)},
+        {a.out, bh * a.dv * dtype_bytes(a.out_dtype)},
+    };
+    Range ins[] = {
+        {a.q, bh * a.dk * es},
+        {a.k, bh * a.dk * es},
+        {a.v, bh * a.dv * es},
+        {a.alpha, bh * (a.decay == HLA_DECAY_VECTOR ? a.dk : 1) * sizeof(float)},
+        {a.beta, bh * sizeof(float)},
+        {a.slot, (size_t)a.B * sizeof(int32_t)},
+        {a.key_perm, (size_t)a.H * a.dk * sizeof(int32_t)},
+    };
+    for (int i = 0; i < 4; ++i) {
+        for (const Range &r : ins)
+            if (overlaps(outs[i], r)) return HLA_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], outs[j])) return HLA_ERR_ALIAS;
+    }
+    return HLA_OK;
+}
+
+int check_damp_codec(const void *state, int n_slots, int H, int dk, int dv, int K_hi,
+                     const void *hi, const void *lo, const void *lo_scale)
+{
+    if (n_slots < 0 || H <= 0) return HLA_ERR_SHAPE;
+    if (n_slots == 0) return HLA_OK;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return HLA_ERR_UNSUPPORTED;
+    if (K_hi < 0 || K_hi > dk) return HLA_ERR_SHAPE;
+    const int nlo = dk - K_hi;
+    if (!state || (K_hi > 0 && !hi) || (nlo > 0 && (!lo || !lo_scale))) return HLA_ERR_NULL;
+    if ((size_t)n_slots * H > kMaxIndex) return HLA_ERR_SHAPE;
+    if (!aligned16(state) || (hi && !aligned16(hi)) || (lo && !aligned16(lo)))
+        return HLA_ERR_ALIGN;
+    const size_t sh = (size_t)n_slots * H;
+    Range st{state, sh * dk * dv * sizeof(float)};
+    Range packed[] = {{hi, sh * K_hi * dv * 2}, {lo, sh * nlo * dv}, {lo_scale, sh * nlo * 4}};
+    for (int i = 0; i < 3; ++i) {
+        if (overlaps(st, packed[i])) return HLA_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(packed[i], packed[j])) return HLA_ERR_ALIAS;
+    }
+    return HLA_OK;
+}
+
+int check_dasc(const void *active, int64_t layer_stride_bytes, int S_act, int L, int n_units,
+               int64_t unit_bytes, const void *table_a, const void *table_b, int R_total,
+               const int32_t *src_slot, const int32_t *dst_slot, int N, const void *packed,
+               int S_ckpt)
+{
+    if (N < 0 || L <= 0 || n_units <= 0 || S_act < 0 || S_ckpt < 0 || R_total < 0 ||
+        unit_bytes <= 0 || layer_stride_bytes < 0)
+        return HLA_ERR_SHAPE;
+    if (R_total > (int64_t)L * n_units) return HLA_ERR_PLAN;
+    if (N == 0) return HLA_OK;
+    if (!active || !packed || !table_a || (R_total > 0 && !table_b) || !src_slot || !dst_slot)
+        return HLA_ERR_NULL;
+    if (unit_bytes % 16 != 0 || layer_stride_bytes % 16 != 0) return HLA_ERR_ALIGN;
+    if (!aligned16(active) || !aligned16(packed)) return HLA_ERR_ALIGN;
+    const int64_t layer_bytes = (int64_t)S_act * n_units * unit_bytes;
+    if (L > 1 && layer_stride_bytes < layer_bytes) return HLA_ERR_SHAPE;
+    // per-pair vector counts must fit the kernels' 32-bit indexing
+    const int64_t unit_vecs = unit_bytes / 16;
+    const int64_t per_pair = unit_vecs * (int64_t)L * n_units;
+    if (per_pair > (int64_t)INT_MAX || unit_vecs > (int64_t)INT_MAX) return HLA_ERR_SHAPE;
+    Range act{active, (size_t)((L - 1) * layer_stride_bytes + layer_bytes)};
+    Range pk{packed, (size_t)S_ckpt * R_total * unit_bytes};
+    if (overlaps(act, pk)) return HLA_ERR_ALIAS;
+    return HLA_OK;
+}
+
+} // namespace hla
+
+extern "C" {
+
+const char *hla_status_str(int status)
+{
+    switch (status) {
+    case HLA_OK: return "ok";
+    case HLA_ERR_NULL: return "a required pointer is NULL";
+    case HLA_ERR_SHAPE: return "invalid size or shape";
+    case HLA_ERR_ALIGN: return "pointer or size not 16-byte aligned";
+    case HLA_ERR_DTYPE: return "unknown dtype or decay kind";
+    case HLA_ERR_PLAN: return "inconsistent checkpoint plan";
+    case HLA_ERR_ALIAS: return "an output buffer overlaps an input";
+    case HLA_ERR_UNSUPPORTED: return "head size not supported (dk, dv must be 64 or 128)";
+    case HLA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int hla_version(void) { return 100; }
+
+// Ragged plan ([dasc] App. B, Scheme 2): r_l retained units per layer,
+// o_0 = 0, o_{l+1} = o_l + r_l, retained units of layer l at flat positions
+// [o_l, o_{l+1}) in ascending unit id; unit_pos inverts the map (-1 = omitted).
+int dasc_plan(const uint8_t *mask, int L, int n_units, int32_t *offsets, int32_t *unit_index,
+              int cap, int32_t *unit_pos, int32_t *R_total)
+{
+    if (!mask || !offsets || !R_total || (cap > 0 && !unit_index)) return HLA_ERR_NULL;
+    if (L <= 0 || n_units <= 0 || cap < 0) return HLA_ERR_SHAPE;
+    if ((int64_t)L * n_units > (int64_t)INT_MAX) return HLA_ERR_SHAPE;
+    int64_t total = 0;
+    for (int64_t i = 0; i < (int64_t)L * n_units; ++i) total += mask[i] ? 1 : 0;
+    if (total > cap) return HLA_ERR_PLAN;
+    int32_t pos = 0;
+    offsets[0] = 0;
+    for (int l = 0; l < L; ++l) {
+        for (int u = 0; u < n_units; ++u) {
+            const int64_t g = (int64_t)l * n_units + u;
+            if (mask[g]) {
+                unit_index[pos] = u;
+                if (unit_pos) unit_pos[g] = pos;
+                ++pos;
+            } else if (unit_pos) {
+                unit_pos[g] = -1;
+            }
+        }
+        offsets[l + 1] = pos;
+    }
+    *R_total = pos;
+    return HLA_OK;
+}
+
+} // extern "C"

@@ -1,0 +1,78 @@
+// Host-side argument checking shared by the launchers.  Pure C++: nothing in
+// here touches the GPU, so every error path can be exercised without one.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "hla.h"
+
+namespace hla {
+
+struct Range {
+    const void *p;
+    size_t bytes;
+};
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool overlaps(Range a, Range b)
+{
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+inline bool head_dim_ok(int d) { return d == 64 || d == 128; }
+inline bool dtype_ok(int t) { return t == HLA_F32 || t == HLA_BF16; }
+inline size_t dtype_bytes(int t) { return t == HLA_BF16 ? 2 : 4; }
+
+// Everything the step / replay launchers need, in one place.
+struct StepArgs {
+    float *state;
+    int n_slots;
+    const int32_t *slot;
+    int B, H, dk, dv;
+    int K;  // tokens per request: 1 for a step, the draft count for replay
+    const void *q, *k, *v;
+    int in_dtype;
+    const float *alpha;
+    int decay;
+    const float *beta;
+    const int32_t *n_accept;  // replay only
+    void *out;
+    int out_dtype;
+};
+
+// Returns HLA_OK or the first error found.  `replay` selects the replay
+// rules (n_accept required, 1 <= K <= 16).
+int check_step(const StepArgs &a, bool replay);
+
+struct DampArgs {
+    uint16_t *hi;
+    int8_t *lo;
+    float *lo_scale;
+    int n_slots;
+    const int32_t *key_perm;
+    int K_hi;
+    const int32_t *slot;
+    int B, H, dk, dv;
+    const void *q, *k, *v;
+    int in_dtype;
+    const float *alpha;
+    int decay;
+    const float *beta;
+    void *out;
+    int out_dtype;
+};
+
+int check_damp(const DampArgs &a);
+int check_damp_codec(const void *state, int n_slots, int H, int dk, int dv, int K_hi,
+                     const void *hi, const void *lo, const void *lo_scale);
+
+int check_dasc(const void *active, int64_t layer_stride_bytes, int S_act, int L, int n_units,
+               int64_t unit_bytes, const void *table_a, const void *table_b, int R_total,
+               const int32_t *src_slot, const int32_t *dst_slot, int N, const void *packed,
+               int S_ckpt);
+
+} // namespace hla

@@ -1,0 +1,271 @@
+// gfx950 kernels for the FP32 gated delta-rule step (GDN scalar decay, KDA
+// per-key-channel decay) and for the replay of accepted draft tokens.
+//
+// Operation ("DAMP: Decay-Aware Mixed-Precision Recurrent-State
+// Quantization", §3.1 Eq. (1)-(2)), per (request, head), state S in dk x dv:
+//     S' = Lambda S,  u = beta (v - S'^T k),  S = S' + k u^T,  o = S^T q.
+//
+// Work decomposition.  Every column j of the state is independent: r_j =
+// (S'^T k)_j and the readout o_j = (S^T q)_j are sums over rows (key
+// channels) of column j only.  So one wave64 owns a dk x 32 column slice of
+// one head and needs nothing from any other wave:
+//   lane = 8 * rg + cg;  cg in 0..7 picks 4 adjacent columns (one 16-byte
+//   float4), rg in 0..7 picks a block of dk/8 consecutive rows.
+// Each 16-byte load/store instruction of the wave covers 8 rows x 128
+// contiguous bytes, so every HBM access is a full 128-byte line.  The tile
+// (dk/8 x 4 floats per lane, 64 for dk = 128) stays in registers from the
+// load to the store: the state is read once and written once per step.
+// Column sums over the 8 row blocks use DPP row_ror:8 and the gfx950
+// v_permlane16_swap / v_permlane32_swap (lane bits 3, 4, 5) - no LDS.
+// The readout is formed in the same pass: o = S'^T q + (q.k) u, which equals
+// S^T q for S = S' + k u^T.
+// A workgroup is the dv/32 waves of one head; they share only the small
+// q/k/alpha rows, which hit in the CU's caches.
+#include <hip/hip_runtime.h>
+
+#include "hla.h"
+#include "hla_device.h"
+#include "hla_internal.h"
+
+namespace hla {
+
+template <int DK>
+struct RowInputs {
+    static constexpr int RPL = DK / 8;  // rows per lane
+};
+
+// One token's update of a lane's tile.  x[m][c] is row (rg*RPL + m), column
+// (slice + 4*cg + c).  kk, qq, aa are this lane's rows of k, q and the decay
+// (aa[0] for a scalar decay).  Returns the readout for the lane's 4 columns
+// (valid in every lane).  Shared by the step and the replay kernels so that
+// a replay is bitwise identical to the same number of single steps.
+template <int RPL, bool VEC>
+__device__ __forceinline__ void tile_token(float (&x)[RPL][4], const float (&kk)[RPL],
+                                           const float (&qq)[RPL], const float *aa, float beta,
+                                           const float (&vv)[4], float (&o)[4])
+{
+    float r[4] = {0.f, 0.f, 0.f, 0.f};
+    float p[4] = {0.f, 0.f, 0.f, 0.f};
+    float qk = 0.f;
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+        const float a = VEC ? aa[m] : aa[0];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            x[m][c] = x[m][c] * a;                 // S' = Lambda S
+            r[c] = fmaf(kk[m], x[m][c], r[c]);     // partial (S'^T k)_j
+            p[c] = fmaf(qq[m], x[m][c], p[c]);     // partial (S'^T q)_j
+        }
+        qk = fmaf(qq[m], kk[m], qk);
+    }
+    // Sum the 8 row blocks: lane bits 3..5.
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        r[c] = sum_lane_bits<3>(r[c]);
+        p[c] = sum_lane_bits<3>(p[c]);
+    }
+    qk = sum_lane_bits<3>(qk);
+    float u[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        u[c] = beta * (vv[c] - r[c]);   // u = beta (v - S'^T k)
+        o[c] = fmaf(qk, u[c], p[c]);    // o = S'^T q + (q.k) u = S^T q
+    }
+#pragma unroll
+    for (int m = 0; m < RPL; ++m)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            x[m][c] = fmaf(kk[m], u[c], x[m][c]);  // S = S' + k u^T
+}
+
+template <int RPL>
+__device__ __forceinline__ void tile_load(const float *S, int DV, float (&x)[RPL][4])
+{
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+        f32x4 t = ld_nt(reinterpret_cast<const f32x4 *>(S + (size_t)m * DV));
+        x[m][0] = t.x; x[m][1] = t.y; x[m][2] = t.z; x[m][3] = t.w;
+    }
+}
+
+template <int RPL>
+__device__ __forceinline__ void tile_store(float *S, int DV, const float (&x)[RPL][4])
+{
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+        f32x4 t = {x[m][0], x[m][1], x[m][2], x[m][3]};
+        st_nt(reinterpret_cast<f32x4 *>(S + (size_t)m * DV), t);
+    }
+}
+
+// Load one token's per-lane inputs: rows [row0, row0+RPL) of q, k (and of a
+// vector decay), the lane's 4 columns of v, and beta.
+template <int DK, int DV, typename TIn, bool VEC>
+__device__ __forceinline__ void token_inputs(const TIn *q, const TIn *k, const TIn *v,
+                                             const float *alpha, const float *beta, size_t tok,
+                                             int row0, int col0, float (&qq)[DK / 8],
+                                             float (&kk)[DK / 8], float (&aa)[VEC ? DK / 8 : 1],
+                                             float (&vv)[4], float &bt)
+{
+    load_in<DK / 8>(k + tok * DK + row0, kk);
+    load_in<DK / 8>(q + tok * DK + row0, qq);
+    if constexpr (VEC)
+        load_in<DK / 8>(alpha + tok * DK + row0, aa);
+    else
+        aa[0] = alpha[tok];
+    load_in<4>(v + tok * DV + col0, vv);
+    bt = beta[tok];
+}
+
+template <int DK, int DV, typename TIn, typename TOut, bool VEC>
+__global__ void __launch_bounds__(2 * DV)
+k_delta_step(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slot, int H,
+             const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
+             const float *__restrict__ alpha, const float *__restrict__ beta,
+             TOut *__restrict__ out, int32_t *__restrict__ err)
+{
+    constexpr int RPL = DK / 8;
+    const int bh = blockIdx.x;
+    const int b = bh / H, h = bh - b * H;
+    const int s = slot ? slot[b] : b;
+    if (s < 0) return;  // padding request
+    if (s >= n_slots) {
+        if (err && threadIdx.x == 0) atomicOr(err, HLA_DEVERR_SLOT);
+        return;
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int cg = lane & 7, rg = lane >> 3;
+    const int col0 = wave * 32 + cg * 4, row0 = rg * RPL;
+    float *S = state + ((size_t)s * H + h) * (DK * DV) + (size_t)row0 * DV + col0;
+
+    float kk[RPL], qq[RPL], aa[VEC ? RPL : 1], vv[4], bt;
+    token_inputs<DK, DV, TIn, VEC>(q, k, v, alpha, beta, (size_t)bh, row0, col0, qq, kk, aa, vv,
+                                   bt);
+    float x[RPL][4];
+    tile_load<RPL>(S, DV, x);
+    float o[4];
+    tile_token<RPL, VEC>(x, kk, qq, aa, bt, vv, o);
+    tile_store<RPL>(S, DV, x);
+    if (out && rg == 0) store_out4(out + (size_t)bh * DV + col0, o);
+}
+
+template <int DK, int DV, typename TIn, typename TOut, bool VEC>
+__global__ void __launch_bounds__(2 * DV)
+k_replay(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slot, int H, int K,
+         const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
+         const float *__restrict__ alpha, const float *__restrict__ beta,
+         const int32_t *__restrict__ n_accept, TOut *__restrict__ out, int32_t *__restrict__ err)
+{
+    constexpr int RPL = DK / 8;
+    const int bh = blockIdx.x;
+    const int b = bh / H, h = bh - b * H;
+    const int s = slot ? slot[b] : b;
+    if (s < 0) return;
+    if (s >= n_slots) {
+        if (err && threadIdx.x == 0) atomicOr(err, HLA_DEVERR_SLOT);
+        return;
+    }
+    int n = n_accept[b];
+    if (n < 0 || n > K) {
+        if (err && threadIdx.x == 0 && h == 0) atomicOr(err, HLA_DEVERR_ACCEPT);
+        n = n < 0 ? 0 : K;
+    }
+    if (n == 0) return;  // nothing accepted: the state is not touched
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int cg = lane & 7, rg = lane >> 3;
+    const int col0 = wave * 32 + cg * 4, row0 = rg * RPL;
+    float *S = state + ((size_t)s * H + h) * (DK * DV) + (size_t)row0 * DV + col0;
+
+    float x[RPL][4];
+    tile_load<RPL>(S, DV, x);
+    for (int t = 0; t < n; ++t) {
+        const size_t tok = ((size_t)b * K + t) * H + h;
+        float kk[RPL], qq[RPL], aa[VEC ? RPL : 1], vv[4], bt;
+        token_inputs<DK, DV, TIn, VEC>(q, k, v, alpha, beta, tok, row0, col0, qq, kk, aa, vv, bt);
+        float o[4];
+        tile_token<RPL, VEC>(x, kk, qq, aa, bt, vv, o);
+        if (out && rg == 0) store_out4(out + tok * DV + col0, o);
+    }
+    tile_store<RPL>(S, DV, x);
+}
+
+// ----------------------------------------------------------------- dispatch
+
+template <int DK, int DV, typename TIn, typename TOut, bool VEC>
+static int launch_typed(const StepArgs &a, bool replay, int32_t *err, hipStream_t st)
+{
+    const dim3 grid((unsigned)((size_t)a.B * a.H)), block(2 * DV);
+    if (replay)
+        hipLaunchKernelGGL((k_replay<DK, DV, TIn, TOut, VEC>), grid, block, 0, st, a.state,
+                           a.n_slots, a.slot, a.H, a.K, (const TIn *)a.q, (const TIn *)a.k,
+                           (const TIn *)a.v, a.alpha, a.beta, a.n_accept, (TOut *)a.out, err);
+    else
+        hipLaunchKernelGGL((k_delta_step<DK, DV, TIn, TOut, VEC>), grid, block, 0, st, a.state,
+                           a.n_slots, a.slot, a.H, (const TIn *)a.q, (const TIn *)a.k,
+                           (const TIn *)a.v, a.alpha, a.beta, (TOut *)a.out, err);
+    return hipGetLastError() == hipSuccess ? HLA_OK : HLA_ERR_LAUNCH;
+}
+
+template <int DK, int DV, typename TIn, typename TOut>
+static int launch_decay(const StepArgs &a, bool replay, int32_t *err, hipStream_t st)
+{
+    return a.decay == HLA_DECAY_VECTOR ? launch_typed<DK, DV, TIn, TOut, true>(a, replay, err, st)
+                                       : launch_typed<DK, DV, TIn, TOut, false>(a, replay, err, st);
+}
+
+template <int DK, int DV>
+static int launch_dtypes(const StepArgs &a, bool replay, int32_t *err, hipStream_t st)
+{
+    const bool in16 = a.in_dtype == HLA_BF16, out16 = a.out_dtype == HLA_BF16;
+    if (in16)
+        return out16 ? launch_decay<DK, DV, uint16_t, uint16_t>(a, replay, err, st)
+                     : launch_decay<DK, DV, uint16_t, float>(a, replay, err, st);
+    return out16 ? launch_decay<DK, DV, float, uint16_t>(a, replay, err, st)
+                 : launch_decay<DK, DV, float, float>(a, replay, err, st);
+}
+
+static int run_step(const StepArgs &a, bool replay, int32_t *err, void *stream)
+{
+    int rc = check_step(a, replay);
+    if (rc != HLA_OK || a.B == 0) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (a.dk == 128 && a.dv == 128) return launch_dtypes<128, 128>(a, replay, err, st);
+    if (a.dk == 128 && a.dv == 64) return launch_dtypes<128, 64>(a, replay, err, st);
+    if (a.dk == 64 && a.dv == 128) return launch_dtypes<64, 128>(a, replay, err, st);
+    return launch_dtypes<64, 64>(a, replay, err, st);
+}
+
+} // namespace hla
+
+extern "C" {
+
+int gdn_step(float *state, int n_slots, const int32_t *slot, int B, int H, int dk, int dv,
+             const void *q, const void *k, const void *v, int in_dtype, const float *alpha,
+             const float *beta, void *out, int out_dtype, int32_t *err_flag, void *stream)
+{
+    hla::StepArgs a{state, n_slots, slot, B, H, dk, dv, 1, q, k, v, in_dtype, alpha,
+                    HLA_DECAY_SCALAR, beta, nullptr, out, out_dtype};
+    return hla::run_step(a, false, err_flag, stream);
+}
+
+int kda_step(float *state, int n_slots, const int32_t *slot, int B, int H, int dk, int dv,
+             const void *q, const void *k, const void *v, int in_dtype, const float *alpha,
+             const float *beta, void *out, int out_dtype, int32_t *err_flag, void *stream)
+{
+    hla::StepArgs a{state, n_slots, slot, B, H, dk, dv, 1, q, k, v, in_dtype, alpha,
+                    HLA_DECAY_VECTOR, beta, nullptr, out, out_dtype};
+    return hla::run_step(a, false, err_flag, stream);
+}
+
+int replay_accepted(float *state, int n_slots, const int32_t *slot, int B, int H, int dk, int dv,
+                    int K, const void *q, const void *k, const void *v, int in_dtype,
+                    const float *alpha, int decay_kind, const float *beta,
+                    const int32_t *n_accept, void *out, int out_dtype, int32_t *err_flag,
+                    void *stream)
+{
+    hla::StepArgs a{state, n_slots, slot, B, H, dk, dv, K, q, k, v, in_dtype, alpha,
+                    decay_kind, beta, n_accept, out, out_dtype};
+    return hla::run_step(a, true, err_flag, stream);
+}
+
+} // extern "C"

@@ -1,0 +1,263 @@
+/*
+ * hla.h -- C ABI of the MI355X (gfx950) library for the gated delta-rule
+ * recurrent-state step used in GDN and KDA decode, its mixed-precision state
+ * variant, ragged state checkpoints, and the replay of accepted draft tokens.
+ *
+ * Pages this interface follows (cited by title and section/equation):
+ *   [DAMP]  "DAMP: Decay-Aware Mixed-Precision Recurrent-State Quantization"
+ *   [dasc]  "dasc: Decay-Aware State Compression for Hybrid Linear-Attention
+ *            Serving"
+ *   [K3]    "Serving recurrent attention" (long-form explainer on Kimi K3)
+ *
+ * Conventions shared by every entry point
+ *   - One head's state is S in R^{dk x dv}, row-major, row u = key channel u
+ *     ([DAMP] §3.1).  A state tensor is [n_slots, H, dk, dv].
+ *   - Every buffer is owned by the caller.  Buffers marked "device" live in
+ *     GPU memory; buffers marked "host" in CPU memory.  The library never
+ *     allocates, frees or synchronises; all work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the legacy default stream) and runs
+ *     asynchronously.
+ *   - The return value is a status (HLA_OK = 0).  Arguments are validated on
+ *     the host before anything is launched; on an error nothing is launched
+ *     and nothing is written.  HLA_ERR_LAUNCH reports a failed launch; faults
+ *     that happen later surface at the caller's next synchronisation.
+ *   - Index tables that live in device memory (slot maps, accepted counts,
+ *     plan tables) cannot be checked on the host without a sync.  Kernels
+ *     never access memory out of bounds because of them: a bad entry is
+ *     skipped (or clamped, where stated) and, when `err_flag` (device int32,
+ *     may be NULL) is given, the matching HLA_DEVERR_* bit is OR-ed into it.
+ *   - Supported head sizes: dk, dv in {64, 128}.  Pointers to vectorised
+ *     buffers must be 16-byte aligned.
+ *   - All entry points are reentrant; the library keeps no mutable global
+ *     state.  Concurrent calls that write the same buffers race.
+ */
+#ifndef HLA_H
+#define HLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Every entry point is exported from the shared library even when it is
+   built with hidden default visibility. */
+#if defined(__GNUC__) || defined(__clang__)
+#define HLA_API __attribute__((visibility("default")))
+#else
+#define HLA_API
+#endif
+
+enum hla_status {
+    HLA_OK = 0,
+    HLA_ERR_NULL = 1,        /* a required pointer is NULL                     */
+    HLA_ERR_SHAPE = 2,       /* a size is negative, zero where not allowed,
+                                or the problem exceeds 32-bit index limits     */
+    HLA_ERR_ALIGN = 3,       /* a vectorised pointer is not 16-byte aligned    */
+    HLA_ERR_DTYPE = 4,       /* unknown dtype or decay-kind code               */
+    HLA_ERR_PLAN = 5,        /* inconsistent host plan (mask/offsets/capacity) */
+    HLA_ERR_ALIAS = 6,       /* an output overlaps an input it must not        */
+    HLA_ERR_UNSUPPORTED = 7, /* valid but not instantiated (e.g. dk = 96)      */
+    HLA_ERR_LAUNCH = 8       /* the kernel launch failed                       */
+};
+
+/* Element types of q, k, v (in_dtype) and of the readout o (out_dtype). */
+enum hla_dtype { HLA_F32 = 0, HLA_BF16 = 1 };
+
+/* Decay granularity: one scalar per head (GDN) or one per key channel (KDA). */
+enum hla_decay { HLA_DECAY_SCALAR = 0, HLA_DECAY_VECTOR = 1 };
+
+/* Bits OR-ed into *err_flag by kernels that meet a bad device-side index. */
+enum hla_device_error {
+    HLA_DEVERR_SLOT = 1,    /* slot / src / dst index >= its bound: pair skipped */
+    HLA_DEVERR_ACCEPT = 2,  /* n_accept outside [0, K]: clamped                  */
+    HLA_DEVERR_PLAN = 4     /* plan table entry out of range: unit skipped       */
+};
+
+/* Static, NUL-terminated description of a status code.  Thread-safe. */
+HLA_API const char *hla_status_str(int status);
+
+/* Library ABI version (major * 100 + minor). */
+HLA_API int hla_version(void);
+
+/* -------------------------------------------------------------------------
+ * gdn_step -- one GDN decode step for a batch of requests, in place.
+ *
+ * Computes, for every request b with a state slot and every head h
+ * ([DAMP] §3.1 Eq. (1)-(2); [dasc] §3.1 Eq. (1), transposed):
+ *     S' = alpha S                    (scalar decay per head)
+ *     u  = beta (v - S'^T k)          (delta correction, in R^dv)
+ *     S  = S' + k u^T                 (written back into the slot)
+ *     o  = S^T q                      (readout of the updated state)
+ *
+ * state   device float32 [n_slots, H, dk, dv], read and written.
+ * slot    device int32 [B] mapping request b to its state slot, or NULL for
+ *         the identity (then n_slots >= B).  A negative entry marks a padding
+ *         request: nothing is read or written for it (its rows of `out` are
+ *         left untouched).  An entry >= n_slots is skipped likewise and sets
+ *         HLA_DEVERR_SLOT.
+ * q, k    device [B, H, dk] of in_dtype; v device [B, H, dv] of in_dtype.
+ *         q and k are expected to be l2-normalised per head ([DAMP] §3.1);
+ *         the kernel does not normalise them.
+ * alpha   device float32 [B, H], the decay factors in (0, 1].
+ * beta    device float32 [B, H], the delta-rule strengths in (0, 1).
+ * out     device [B, H, dv] of out_dtype, or NULL for no readout.
+ * Errors: NULL, SHAPE, ALIGN (state, q, k, v, out), DTYPE, UNSUPPORTED,
+ *         ALIAS (out or state overlapping an input), LAUNCH.
+ * ---------------------------------------------------------------------- */
+HLA_API int gdn_step(float *state, int n_slots, const int32_t *slot, int B, int H, int dk,
+             int dv, const void *q, const void *k, const void *v, int in_dtype,
+             const float *alpha, const float *beta, void *out, int out_dtype,
+             int32_t *err_flag, void *stream);
+
+/* -------------------------------------------------------------------------
+ * kda_step -- one KDA decode step: as gdn_step, but the decay is a vector
+ * over key channels, Lambda = diag(alpha_0 .. alpha_{dk-1}) = diag(exp g),
+ * so row u of the state is multiplied by alpha_u ([DAMP] §3.1 Eq. (2);
+ * [dasc] §3.1 Eq. (1)).
+ *
+ * alpha   device float32 [B, H, dk] (16-byte aligned).  All other arguments
+ *         as gdn_step.
+ * ---------------------------------------------------------------------- */
+HLA_API int kda_step(float *state, int n_slots, const int32_t *slot, int B, int H, int dk,
+             int dv, const void *q, const void *k, const void *v, int in_dtype,
+             const float *alpha, const float *beta, void *out, int out_dtype,
+             int32_t *err_flag, void *stream);
+
+/* -------------------------------------------------------------------------
+ * Mixed-precision packed state ([DAMP] §5.2 and App. A.4).  For each slot and
+ * head the dk key-channel rows are reordered by a static plan so that packed
+ * row r holds key channel key_perm[h*dk + r]; rows r < K_hi are stored in
+ * FP16, rows r >= K_hi as symmetric INT8 codes with one FP32 scale per row:
+ *     hi        device uint16 (IEEE binary16 bits) [n_slots, H, K_hi, dv]
+ *     lo        device int8                        [n_slots, H, dk-K_hi, dv]
+ *     lo_scale  device float32                     [n_slots, H, dk-K_hi]
+ * The INT8 row quantiser is [DAMP] §3.2 Eq. (5)-(6) with b = 8 as made
+ * concrete in [dasc] App. E.1 Eq. (8): a = max_j |x_j|,
+ * s = max(a, 1e-8) / 127, c = clip(round(x / s), -127, 127), computed in
+ * FP32, s stored in FP32, round = nearest-even.  FP16 rows are rounded to
+ * nearest-even.  key_perm is device int32 [H, dk], a permutation of 0..dk-1
+ * per head, or NULL for the identity (the pages fold the order into the
+ * projection weights, [DAMP] §5.2).  0 <= K_hi <= dk.
+ * ---------------------------------------------------------------------- */
+
+/* damp_step -- one decode step on the packed state, in place ([DAMP] §3.3
+ * Eq. (7), S^q_t = Q(A_t S^q_{t-1} + beta k v^T), fused as in App. A.4):
+ * reconstruct each row (FP16 value, or code * scale), run the gdn_step /
+ * kda_step update and readout in FP32, then requantise every INT8 row with a
+ * freshly computed scale and round every FP16 row, and write all three
+ * regions back.  The readout o is taken from the FP32 updated state before
+ * it is requantised.
+ *
+ * q, k, alpha (when decay_kind == HLA_DECAY_VECTOR) are indexed by ORIGINAL
+ * key channel, [B, H, dk]; the kernel gathers them through key_perm.
+ * alpha is [B, H] for HLA_DECAY_SCALAR.  slot, v, beta, out, err_flag as
+ * gdn_step.
+ * Errors: as gdn_step, plus SHAPE for K_hi outside [0, dk].
+ */
+HLA_API int damp_step(uint16_t *hi, int8_t *lo, float *lo_scale, int n_slots,
+              const int32_t *key_perm, int K_hi, const int32_t *slot, int B, int H,
+              int dk, int dv, const void *q, const void *k, const void *v, int in_dtype,
+              const float *alpha, int decay_kind, const float *beta, void *out,
+              int out_dtype, int32_t *err_flag, void *stream);
+
+/* damp_quantize -- pack an FP32 state [n_slots, H, dk, dv] (device) into the
+ * three regions above with the same quantiser.  The FP32 input is only read.
+ */
+HLA_API int damp_quantize(const float *state, int n_slots, int H, int dk, int dv,
+                  const int32_t *key_perm, int K_hi, uint16_t *hi, int8_t *lo,
+                  float *lo_scale, void *stream);
+
+/* damp_dequantize -- reconstruct the FP32 state (original channel order) from
+ * the packed regions: FP16 values exactly, INT8 rows as code * scale. */
+HLA_API int damp_dequantize(const uint16_t *hi, const int8_t *lo, const float *lo_scale,
+                    int n_slots, int H, int dk, int dv, const int32_t *key_perm,
+                    int K_hi, float *state, void *stream);
+
+/* -------------------------------------------------------------------------
+ * Ragged state checkpoints ([dasc] §4.1, §4.2 and App. B "Ragged (Scheme 2)").
+ * A unit is unit_bytes contiguous bytes of one slot's state in one layer: a
+ * whole head for GDN (dk*dv*4 bytes), one key channel's row for KDA (dv*4
+ * bytes).  Layer l of the active state is [S, n_units, unit_bytes] starting
+ * l * layer_stride_bytes into the buffer.  A static mask selects the retained
+ * units; layer l keeps r_l of them, offsets o_0 = 0, o_{l+1} = o_l + r_l, and
+ * its units occupy flat positions [o_l, o_{l+1}) of a checkpoint slot
+ * [R_total, unit_bytes], R_total = sum_l r_l, listed in ascending unit id.
+ * ---------------------------------------------------------------------- */
+
+/* dasc_plan -- HOST-only.  Build the ragged plan once from the mask
+ * ([dasc] App. B.2: masks, offsets and maps are precomputed once).
+ * mask        host uint8 [L, n_units]; nonzero = retained.
+ * offsets     host int32 [L + 1] (written).
+ * unit_index  host int32 [cap] (written: first R_total entries).
+ * unit_pos    host int32 [L * n_units] or NULL (written: flat position of
+ *             each unit, -1 for an omitted unit); dasc_restore uses it.
+ * R_total     host int32 (written).
+ * Errors: NULL, SHAPE, PLAN (cap < R_total). */
+HLA_API int dasc_plan(const uint8_t *mask, int L, int n_units, int32_t *offsets,
+              int32_t *unit_index, int cap, int32_t *unit_pos, int32_t *R_total);
+
+/* dasc_pack -- store path ([dasc] App. B.1 "Runtime store", the single-rank
+ * fused pack): for each pair n < N, copy every retained unit of active slot
+ * src_slot[n] of every layer into checkpoint slot dst_slot[n] at its flat
+ * position.  Bit copy.  The active state is only read.
+ * active      device, layer l at active + l * layer_stride_bytes, each layer
+ *             [S_act, n_units, unit_bytes].
+ * offsets     device int32 [L + 1]; unit_index device int32 [R_total].
+ * src_slot    device int32 [N] (< S_act); dst_slot device int32 [N] (< S_ckpt).
+ * packed      device [S_ckpt, R_total, unit_bytes].
+ * unit_bytes must be a positive multiple of 16; layer_stride_bytes a multiple
+ * of 16 and >= S_act * n_units * unit_bytes.
+ * Errors: NULL, SHAPE, ALIGN, ALIAS (packed overlapping active), LAUNCH. */
+HLA_API int dasc_pack(const void *active, int64_t layer_stride_bytes, int S_act, int L,
+              int n_units, int64_t unit_bytes, const int32_t *offsets,
+              const int32_t *unit_index, int R_total, const int32_t *src_slot,
+              const int32_t *dst_slot, int N, void *packed, int S_ckpt,
+              int32_t *err_flag, void *stream);
+
+/* dasc_restore -- load path without refresh ([dasc] §4.2 dasc-nr; App. B.2
+ * "Insertion and reuse"): for each pair n < N, write EVERY unit of every layer
+ * of private slot dst_slot[n]: a retained unit receives its packed bytes from
+ * checkpoint slot src_slot[n], an omitted unit is zero-filled.  The checkpoint
+ * is only read ([K3]: restore copies the immutable checkpoint into the
+ * request's private running state).
+ * unit_pos    device int32 [L * n_units] from dasc_plan.
+ * active_out  device, layer l at active_out + l * layer_stride_bytes, each
+ *             layer [S_dst, n_units, unit_bytes].
+ * Errors: as dasc_pack. */
+HLA_API int dasc_restore(const void *packed, int S_ckpt, int R_total, const int32_t *unit_pos,
+                 int L, int n_units, int64_t unit_bytes, const int32_t *src_slot,
+                 const int32_t *dst_slot, int N, void *active_out,
+                 int64_t layer_stride_bytes, int S_dst, int32_t *err_flag,
+                 void *stream);
+
+/* -------------------------------------------------------------------------
+ * replay_accepted -- advance each request's state by its accepted draft
+ * tokens only ([K3] "Speculative decoding without state snapshots": the
+ * verify pass caches the projected inputs of the K draft tokens; after
+ * verification the accepted ones are replayed on-chip into the state).
+ * For request b, for t = 0 .. n_b - 1 in order, the gdn_step / kda_step
+ * update is applied with draft projection t; the state is read once and
+ * written once, and not touched at all when n_b = 0.  The bonus token is not
+ * part of this call (it is the next ordinary step).
+ *
+ * q, k     device [B, K, H, dk]; v device [B, K, H, dv] (in_dtype).
+ * alpha    device float32 [B, K, H] (HLA_DECAY_SCALAR) or [B, K, H, dk].
+ * beta     device float32 [B, K, H].
+ * n_accept device int32 [B]; values outside [0, K] are clamped and set
+ *          HLA_DEVERR_ACCEPT.
+ * out      device [B, K, H, dv] of out_dtype or NULL: the readout after each
+ *          replayed token; rows t >= n_b are left untouched.
+ * 1 <= K <= 16.  state, slot, err_flag as gdn_step.
+ * ---------------------------------------------------------------------- */
+HLA_API int replay_accepted(float *state, int n_slots, const int32_t *slot, int B, int H,
+                    int dk, int dv, int K, const void *q, const void *k, const void *v,
+                    int in_dtype, const float *alpha, int decay_kind, const float *beta,
+                    const int32_t *n_accept, void *out, int out_dtype, int32_t *err_flag,
+                    void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HLA_H */

@@ -1,0 +1,185 @@
+"""The C ABI on the CPU: the library loads, exports every entry point that
+include/hla.h declares, and rejects bad arguments on the host before launching
+anything.  No call here reaches a kernel launch (every call is either invalid or
+empty), so these tests need no GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+hla = pytest.importorskip("hybrid_linear_attention_step_amd")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(hla.LIB_PATH):
+        pytest.skip("libhla.so not built (run __graft_entry__.build())")
+    return hla.lib()
+
+
+OK, NULL, SHAPE, ALIGN, DTYPE, PLAN, ALIAS, UNSUP = 0, 1, 2, 3, 4, 5, 6, 7
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            names |= set(re.findall(r"HLA_API\s+[\w\s\*]+?\b(\w+)\s*\(", src))
+    return names
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert {"gdn_step", "kda_step", "damp_step", "dasc_pack", "dasc_restore",
+            "replay_accepted"} <= names
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in hla.SIGNATURES, n
+
+
+def test_status_strings(L):
+    for code in range(9):
+        assert len(hla.status_str(code)) > 0
+    assert hla.status_str(0) == "ok"
+    assert hla.status_str(99) == "unknown status"
+    assert L.hla_version() >= 100
+
+
+# Fake device addresses: never dereferenced, because every call below fails
+# validation (or is empty) before anything is launched.
+class Fake:
+    def __init__(self):
+        self.next = 0x7F0000000000
+
+    def __call__(self, nbytes=1 << 30):
+        p = self.next
+        self.next += (nbytes + 4095) // 4096 * 4096 + 4096
+        return ctypes.c_void_p(p)
+
+
+def _gdn(L, f, **kw):
+    a = dict(state=f(), n_slots=4, slot=None, B=4, H=2, dk=128, dv=128, q=f(), k=f(), v=f(),
+             in_dtype=1, alpha=f(), beta=f(), out=f(), out_dtype=0, err=None, stream=None)
+    a.update(kw)
+    return L.gdn_step(*a.values())
+
+
+def test_step_validation(L):
+    f = Fake()
+    assert _gdn(L, f, state=None) == NULL
+    assert _gdn(L, f, q=None) == NULL
+    assert _gdn(L, f, dk=96) == UNSUP
+    assert _gdn(L, f, dv=256) == UNSUP
+    assert _gdn(L, f, in_dtype=5) == DTYPE
+    assert _gdn(L, f, out_dtype=-1) == DTYPE
+    assert _gdn(L, f, B=-1) == SHAPE
+    assert _gdn(L, f, H=0) == SHAPE
+    assert _gdn(L, f, n_slots=3) == SHAPE  # identity slot map needs n_slots >= B
+    assert _gdn(L, f, q=ctypes.c_void_p(f().value + 4)) == ALIGN
+    assert _gdn(L, f, state=ctypes.c_void_p(f().value + 8)) == ALIGN
+    q = f()
+    assert _gdn(L, f, q=q, out=q) == ALIAS
+    st = f()
+    assert _gdn(L, f, state=st, v=ctypes.c_void_p(st.value + 4096)) == ALIAS
+    assert _gdn(L, f, B=0) == OK  # empty batch: nothing to launch
+
+
+def test_kda_and_replay_validation(L):
+    f = Fake()
+    args = [f(), 4, None, 4, 2, 64, 64, f(), f(), f(), 0]
+    # KDA's per-channel decay is read with 16-byte loads
+    assert L.kda_step(*args, ctypes.c_void_p(f().value + 4), f(), f(), 0, None, None) == ALIGN
+    base = dict(state=f(), n_slots=4, slot=None, B=4, H=2, dk=64, dv=64, K=8, q=f(), k=f(),
+                v=f(), in_dtype=0, alpha=f(), decay=0, beta=f(), n_accept=f(), out=None,
+                out_dtype=0, err=None, stream=None)
+
+    def rp(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.replay_accepted(*a.values())
+
+    assert rp(K=0) == SHAPE and rp(K=17) == SHAPE
+    assert rp(n_accept=None) == NULL
+    assert rp(decay=2) == DTYPE
+    assert rp(B=0) == OK
+
+
+def test_damp_validation(L):
+    f = Fake()
+    base = dict(hi=f(), lo=f(), sc=f(), n_slots=4, perm=None, K_hi=16, slot=None, B=4, H=2,
+                dk=128, dv=128, q=f(), k=f(), v=f(), in_dtype=1, alpha=f(), decay=1, beta=f(),
+                out=f(), out_dtype=0, err=None, stream=None)
+
+    def dm(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.damp_step(*a.values())
+
+    assert dm(K_hi=129) == SHAPE and dm(K_hi=-1) == SHAPE
+    assert dm(hi=None) == NULL
+    # no FP16 rows: hi may be NULL (the misaligned q is reported instead; nothing launches)
+    assert dm(hi=None, K_hi=0, q=ctypes.c_void_p(f().value + 2)) == ALIGN
+    assert dm(lo=None) == NULL
+    assert dm(dk=32) == UNSUP
+    hi = f()
+    assert dm(hi=hi, lo=hi) == ALIAS
+    assert L.damp_quantize(f(), 2, 2, 128, 128, None, 200, f(), f(), f(), None) == SHAPE
+    assert L.damp_dequantize(f(), f(), f(), 2, 2, 100, 128, None, 16, f(), None) == UNSUP
+
+
+def test_dasc_validation(L):
+    f = Fake()
+    base = dict(active=f(), stride=512 * 32 * 65536, S_act=512, L=4, n_units=32,
+                unit_bytes=65536, offsets=f(), unit_index=f(), R_total=64, src=f(), dst=f(),
+                N=8, packed=f(), S_ckpt=8, err=None, stream=None)
+
+    def pk(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.dasc_pack(*a.values())
+
+    assert pk(unit_bytes=24) == ALIGN
+    assert pk(R_total=129) == PLAN
+    assert pk(offsets=None) == NULL
+    assert pk(stride=1024) == SHAPE  # layers would overlap
+    act = f()
+    assert pk(active=act, packed=ctypes.c_void_p(act.value + 65536)) == ALIAS
+    assert pk(N=0) == OK
+    assert L.dasc_restore(f(), 8, 64, None, 4, 32, 65536, f(), f(), 8, f(), 512 * 32 * 65536,
+                          512, None, None) == NULL
+
+
+def test_dasc_plan_matches_oracle(L, orc):
+    g = np.random.default_rng(40)
+    for trial in range(20):
+        Lr, n = int(g.integers(1, 9)), int(g.integers(1, 300))
+        mask = (g.random((Lr, n)) < g.random()).astype(np.uint8)
+        off, idx, pos, R = hla.dasc_plan(mask)
+        o_off, o_idx = orc.dasc_plan(mask)
+        assert R == o_off[-1]
+        assert np.array_equal(off, o_off) and np.array_equal(idx, o_idx)
+        for l in range(Lr):
+            for u in range(n):
+                p = pos[l, u]
+                if mask[l, u]:
+                    assert off[l] <= p < off[l + 1] and idx[p] == u
+                else:
+                    assert p == -1
+
+
+def test_dasc_plan_errors(L):
+    mask = np.ones((2, 5), np.uint8)
+    off = np.zeros(3, np.int32)
+    idx = np.zeros(4, np.int32)
+    R = ctypes.c_int32()
+    assert L.dasc_plan(mask.ctypes.data, 2, 5, off.ctypes.data, idx.ctypes.data, 4, None,
+                       ctypes.byref(R)) == PLAN
+    assert L.dasc_plan(None, 2, 5, off.ctypes.data, idx.ctypes.data, 4, None,
+                       ctypes.byref(R)) == NULL
+    assert L.dasc_plan(mask.ctypes.data, 0, 5, off.ctypes.data, idx.ctypes.data, 4, None,
+                       ctypes.byref(R)) == SHAPE

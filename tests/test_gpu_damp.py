@@ -1,0 +1,209 @@
+"""GPU parity of the mixed-precision state kernels (damp_quantize, damp_dequantize,
+damp_step) against the float64 oracle.
+
+Bars: FP32 scales bit-exact when both sides quantise the same FP32 values; INT8
+codes differ by at most 1 on at most 0.1% of values (the quantiser's FP32 rounding
+decision can land on the other side of a half-integer); the reconstructed state per
+head and the readout within 1e-3 relative (max-norm per head tile).  The step is
+checked teacher-forced (both sides start every step from the same packed state) and
+free-running (the drift statistics are reported)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import (dev, dev_inputs, f64_inputs, gather_heads, host, need_gpu, rel_err_tiles,
+                      sample_heads, torch)
+
+pytestmark = pytest.mark.gpu
+STATE_TOL = 1e-3
+CODE_FRAC = 1e-3
+
+
+def _packed_dev(hi, lo, sc):
+    return dev(hi.view(np.int16)), dev(lo), dev(sc)
+
+
+def _packed_host(hi_d, lo_d, sc_d):
+    return (hi_d.cpu().numpy().view(np.uint16).copy(), lo_d.cpu().numpy().copy(),
+            sc_d.cpu().numpy().copy())
+
+
+def _code_stats(lo_g, lo_o):
+    d = np.abs(lo_g.astype(np.int32) - lo_o.astype(np.int32))
+    return (float((d > 0).mean()) if d.size else 0.0), (int(d.max()) if d.size else 0)
+
+
+def _perm(rng, H, dk):
+    return np.stack([rng.permutation(dk) for _ in range(H)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("dk,dv,K_hi", [(128, 128, 16), (64, 64, 5), (128, 64, 0), (64, 128, 64)])
+def test_quantize_and_dequantize(dk, dv, K_hi):
+    hla = need_gpu()
+    rng = np.random.default_rng(dk + dv + K_hi)
+    S_, H = 3, 4
+    state = (rng.standard_normal((S_, H, dk, dv)) * 0.05).astype(np.float32)
+    state[0, 0, 3] = 0.0                    # a zero row: scale floor
+    state[1, 2, 7, 5] = 40.0                # an outlier
+    perm = _perm(rng, H, dk)
+    hi_d, lo_d, sc_d = hla.damp_quantize(dev(state), dev(perm), K_hi)
+    hi_g, lo_g, sc_g = _packed_host(hi_d, lo_d, sc_d)
+    hi_o, lo_o, sc_o = oracle.damp_quantize(state.astype(np.float64), perm, K_hi)
+    assert np.array_equal(hi_g, hi_o)       # FP16 rows: same RNE from the same FP32 value
+    assert np.array_equal(sc_g, sc_o)       # scale = fl(max / 127), bit-exact
+    frac, dmax = _code_stats(lo_g, lo_o)
+    assert dmax <= 1 and frac <= CODE_FRAC
+    back = host(hla.damp_dequantize(hi_d, lo_d, sc_d, dev(perm), K_hi, dk))
+    ref = oracle.damp_dequantize(hi_g, lo_g, sc_g, perm, K_hi, dk)
+    assert rel_err_tiles(back, ref) <= 1e-6
+
+
+def _teacher_forced(hla, cfg, perm, steps, slot=None, n_slots=None):
+    rng = np.random.default_rng(cfg.seed)
+    n_slots = cfg.B if n_slots is None else n_slots
+    S0 = synth.initial_state(cfg, S=n_slots).astype(np.float64)
+    hi, lo, sc = oracle.damp_quantize(S0, perm, cfg.K_hi)
+    per = cfg.decay == "vector"
+    worst = dict(frac=0.0, dmax=0, state=0.0, out=0.0)
+    for step in range(steps):
+        x = synth.step_inputs(cfg, step)
+        hi_d, lo_d, sc_d = _packed_dev(hi, lo, sc)
+        xd = dev_inputs(x, cfg.in_dtype)
+        out = torch.full((cfg.B, cfg.H, cfg.dv), 3.0, device="cuda")
+        hla.damp_step(hi_d, lo_d, sc_d, dev(perm) if perm is not None else None, cfg.K_hi,
+                      xd["q"], xd["k"], xd["v"], xd["alpha"], 1 if per else 0, xd["beta"],
+                      out=out, slot=None if slot is None else dev(slot))
+        x64 = f64_inputs(x, cfg.in_dtype)
+        o_ref = oracle.damp_step(hi, lo, sc, perm, cfg.K_hi, x64["q"], x64["k"], x64["v"],
+                                 x64["alpha"], x64["beta"], per_channel=per, slot=slot)
+        hi_g, lo_g, sc_g = _packed_host(hi_d, lo_d, sc_d)
+        frac, dmax = _code_stats(lo_g, lo)
+        s_g = oracle.damp_dequantize(hi_g, lo_g, sc_g, perm, cfg.K_hi, cfg.dk)
+        s_o = oracle.damp_dequantize(hi, lo, sc, perm, cfg.K_hi, cfg.dk)
+        live = np.ones(cfg.B, bool) if slot is None else slot >= 0
+        o = host(out)
+        worst["frac"] = max(worst["frac"], frac)
+        worst["dmax"] = max(worst["dmax"], dmax)
+        worst["state"] = max(worst["state"], rel_err_tiles(s_g, s_o))
+        worst["out"] = max(worst["out"], rel_err_tiles(o[live], o_ref[live], 1))
+        assert (o[~live] == 3.0).all()
+    return worst
+
+
+@pytest.mark.parametrize("decay", ["vector", "scalar"])
+@pytest.mark.parametrize("dk,dv,K_hi,use_perm", [
+    (128, 128, 16, True), (128, 128, 16, False), (64, 64, 5, True), (128, 64, 0, True),
+    (64, 128, 64, True), (128, 128, 128, False), (128, 128, 37, True)])
+def test_step_teacher_forced(decay, dk, dv, K_hi, use_perm):
+    hla = need_gpu()
+    base = synth.CONFIGS["damp_kda"]
+    cfg = synth.shrink(base, B=5, H=3, dk=dk, dv=dv, K_hi=K_hi, decay=decay,
+                       seed=base.seed + dk + dv + K_hi)
+    perm = _perm(np.random.default_rng(K_hi), cfg.H, dk) if use_perm else None
+    slot = np.array([3, -1, 0, 5, 1], np.int32)
+    w = _teacher_forced(hla, cfg, perm, steps=4, slot=slot, n_slots=6)
+    print(w)
+    assert w["dmax"] <= 1 and w["frac"] <= CODE_FRAC
+    assert w["state"] <= STATE_TOL and w["out"] <= STATE_TOL
+
+
+def test_workload_plan_teacher_forced():
+    """The mixed-precision workload's own plan (16 FP16 rows per head biased to slow
+    decay), 32 heads, bf16 inputs, per-channel decay."""
+    hla = need_gpu()
+    cfg = synth.shrink(synth.CONFIGS["damp_kda"], B=8)
+    w = _teacher_forced(hla, cfg, synth.damp_key_perm(cfg), steps=4)
+    print(w)
+    assert w["dmax"] <= 1 and w["frac"] <= CODE_FRAC
+    assert w["state"] <= STATE_TOL and w["out"] <= STATE_TOL
+
+
+def test_free_running_32_steps_report():
+    """Both sides run 32 steps from the same packed state without re-synchronising; the
+    reconstructed state stays within the bar and the code statistics are reported."""
+    hla = need_gpu()
+    cfg = synth.shrink(synth.CONFIGS["damp_kda"], B=4)
+    perm = synth.damp_key_perm(cfg)
+    S0 = synth.initial_state(cfg).astype(np.float64)
+    hi, lo, sc = oracle.damp_quantize(S0, perm, cfg.K_hi)
+    hi_d, lo_d, sc_d = _packed_dev(hi, lo, sc)
+    perm_d = dev(perm)
+    report = {}
+    for step in range(32):
+        x = synth.step_inputs(cfg, step)
+        xd = dev_inputs(x, cfg.in_dtype)
+        o = hla.damp_step(hi_d, lo_d, sc_d, perm_d, cfg.K_hi, xd["q"], xd["k"], xd["v"],
+                          xd["alpha"], 1, xd["beta"])
+        x64 = f64_inputs(x, cfg.in_dtype)
+        o_ref = oracle.damp_step(hi, lo, sc, perm, cfg.K_hi, x64["q"], x64["k"], x64["v"],
+                                 x64["alpha"], x64["beta"], per_channel=True)
+        if step in (0, 7, 31):
+            hi_g, lo_g, sc_g = _packed_host(hi_d, lo_d, sc_d)
+            frac, dmax = _code_stats(lo_g, lo)
+            st = rel_err_tiles(oracle.damp_dequantize(hi_g, lo_g, sc_g, perm, cfg.K_hi, cfg.dk),
+                               oracle.damp_dequantize(hi, lo, sc, perm, cfg.K_hi, cfg.dk))
+            report[step + 1] = dict(code_frac=frac, code_dmax=dmax, state=st,
+                                    out=rel_err_tiles(host(o), o_ref, 1))
+    print(report)
+    for r in report.values():
+        assert r["state"] <= STATE_TOL and r["out"] <= STATE_TOL
+
+
+def test_serving_shape_sampled_heads_teacher_forced():
+    """Batch 256 x 32 heads in the benchmark's launch configuration: before each of 3
+    steps the packed state of 48 sampled heads is read back, the oracle takes the same
+    step from it, and the GPU's result for those heads is compared."""
+    hla = need_gpu()
+    cfg = synth.CONFIGS["damp_kda"]
+    perm = synth.damp_key_perm(cfg)
+    S0 = dev(synth.initial_state(cfg))
+    hi_d, lo_d, sc_d = hla.damp_quantize(S0, dev(perm), cfg.K_hi)
+    del S0
+    pairs = sample_heads(np.random.default_rng(9), cfg.B, cfg.H, 48)
+    bi = torch.tensor([b for b, _ in pairs], device="cuda")
+    hh = torch.tensor([h for _, h in pairs], device="cuda")
+    perm_d = dev(perm)
+    for step in range(3):
+        x = synth.step_inputs(cfg, step)
+        hi_s, lo_s, sc_s = (hi_d[bi, hh][:, None].cpu().numpy().view(np.uint16).copy(),
+                            lo_d[bi, hh][:, None].cpu().numpy().copy(),
+                            sc_d[bi, hh][:, None].cpu().numpy().copy())
+        xd = dev_inputs(x, cfg.in_dtype)
+        o = hla.damp_step(hi_d, lo_d, sc_d, perm_d, cfg.K_hi, xd["q"], xd["k"], xd["v"],
+                          xd["alpha"], 1, xd["beta"])
+        xs = gather_heads(f64_inputs(x, cfg.in_dtype), pairs)
+        # the oracle takes one head per sample, each with its own head's plan
+        o_ref = np.zeros((len(pairs), cfg.dv))
+        for i, (b, h) in enumerate(pairs):
+            hs, ls, ss = hi_s[i:i + 1].copy(), lo_s[i:i + 1].copy(), sc_s[i:i + 1].copy()
+            xi = {n: xs[n][i:i + 1] for n in xs}
+            o_ref[i] = oracle.damp_step(hs, ls, ss, perm[h:h + 1], cfg.K_hi, xi["q"], xi["k"],
+                                        xi["v"], xi["alpha"], xi["beta"], per_channel=True)[0, 0]
+            hi_s[i], lo_s[i], sc_s[i] = hs[0], ls[0], ss[0]
+        hi_g = hi_d[bi, hh][:, None].cpu().numpy().view(np.uint16)
+        lo_g = lo_d[bi, hh][:, None].cpu().numpy()
+        sc_g = sc_d[bi, hh][:, None].cpu().numpy()
+        frac, dmax = _code_stats(lo_g, lo_s)
+        assert dmax <= 1 and frac <= CODE_FRAC
+        for i, (b, h) in enumerate(pairs):
+            s_g = oracle.damp_dequantize(hi_g[i:i + 1], lo_g[i:i + 1], sc_g[i:i + 1],
+                                         perm[h:h + 1], cfg.K_hi, cfg.dk)
+            s_o = oracle.damp_dequantize(hi_s[i:i + 1], lo_s[i:i + 1], sc_s[i:i + 1],
+                                         perm[h:h + 1], cfg.K_hi, cfg.dk)
+            assert rel_err_tiles(s_g, s_o) <= STATE_TOL
+        assert rel_err_tiles(host(o[bi, hh]), o_ref, 1) <= STATE_TOL
+
+
+def test_bad_plan_entry_sets_flag():
+    hla = need_gpu()
+    cfg = synth.shrink(synth.CONFIGS["damp_kda"], B=2, H=2)
+    perm = np.tile(np.arange(cfg.dk, dtype=np.int32), (cfg.H, 1))
+    perm[1, 3] = 500
+    hi_d, lo_d, sc_d = hla.damp_quantize(dev(synth.initial_state(cfg)), None, cfg.K_hi)
+    xd = dev_inputs(synth.step_inputs(cfg, 0), cfg.in_dtype)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hla.damp_step(hi_d, lo_d, sc_d, dev(perm), cfg.K_hi, xd["q"], xd["k"], xd["v"], xd["alpha"],
+                  1, xd["beta"], err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == hla.DEVERR_PLAN

@@ -1,0 +1,144 @@
+"""GPU parity of gdn_step / kda_step (through the C ABI) against the float64 oracle.
+
+Tolerance (FP32 state and outputs): per head tile, max|gpu - oracle| <= 1e-5 *
+max|oracle| after every step, up to 32 steps."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import (dev, dev_inputs, f64_inputs, gather_heads, host, need_gpu, rel_err_tiles,
+                      sample_heads, torch)
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+def _run(hla, kind, st, x_dev, **kw):
+    fn = hla.kda_step if kind == "kda" else hla.gdn_step
+    return fn(st, x_dev["q"], x_dev["k"], x_dev["v"], x_dev["alpha"], x_dev["beta"], **kw)
+
+
+def _orc(kind, S64, x64, **kw):
+    fn = oracle.kda_step if kind == "kda" else oracle.gdn_step
+    return fn(S64, x64["q"], x64["k"], x64["v"], x64["alpha"], x64["beta"], **kw)
+
+
+def test_gdn_toy_workload_32_steps():
+    hla = need_gpu()
+    cfg = synth.CONFIGS["gdn_toy"]
+    S64 = synth.initial_state(cfg).astype(np.float64)
+    st = dev(synth.initial_state(cfg))
+    worst_s = worst_o = 0.0
+    for step in range(cfg.steps):
+        x = synth.step_inputs(cfg, step)
+        o = _run(hla, "gdn", st, dev_inputs(x, cfg.in_dtype))
+        o_ref = _orc("gdn", S64, f64_inputs(x, cfg.in_dtype))
+        worst_o = max(worst_o, rel_err_tiles(host(o), o_ref, 1))
+        worst_s = max(worst_s, rel_err_tiles(host(st), S64))
+    print(f"toy: worst state err {worst_s:.2e}, out err {worst_o:.2e}")
+    assert worst_s <= TOL and worst_o <= TOL
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_ragged_batch_with_slot_map(kind, in_dtype, dk, dv):
+    """Odd batch and head counts, a permuted slot map with a padding request, every
+    instantiated head shape, both input dtypes; slots no request names stay untouched."""
+    hla = need_gpu()
+    base = synth.CONFIGS["kda_serving" if kind == "kda" else "gdn_serving"]
+    cfg = synth.shrink(base, B=5, H=3, dk=dk, dv=dv, in_dtype=in_dtype, seed=base.seed + dk + dv)
+    n_slots = 7
+    slot = np.array([6, -1, 2, 0, 4], np.int32)
+    S0 = synth.initial_state(cfg, S=n_slots)
+    S64 = S0.astype(np.float64)
+    st = dev(S0)
+    slot_d = dev(slot)
+    for step in range(8):
+        x = synth.step_inputs(cfg, step)
+        xd = dev_inputs(x, in_dtype)
+        out = torch.full((cfg.B, cfg.H, dv), 7.0, device="cuda")
+        _run(hla, kind, st, xd, out=out, slot=slot_d)
+        o_ref = _orc(kind, S64, f64_inputs(x, in_dtype), slot=slot)
+        o = host(out)
+        live = slot >= 0
+        assert rel_err_tiles(o[live], o_ref[live], 1) <= TOL
+        assert (o[~live] == 7.0).all()  # padding request: out untouched
+        assert rel_err_tiles(host(st), S64) <= TOL
+    got = host(st)
+    for s in (1, 3, 5):
+        assert np.array_equal(got[s], S0[s])
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_bf16_readout(kind):
+    hla = need_gpu()
+    cfg = synth.shrink(synth.CONFIGS[f"{kind}_serving"], B=4, H=8)
+    S64 = synth.initial_state(cfg).astype(np.float64)
+    st = dev(synth.initial_state(cfg))
+    for step in range(3):
+        x = synth.step_inputs(cfg, step)
+        out = torch.empty((cfg.B, cfg.H, cfg.dv), dtype=torch.bfloat16, device="cuda")
+        _run(hla, kind, st, dev_inputs(x, cfg.in_dtype), out=out)
+        o_ref = _orc(kind, S64, f64_inputs(x, cfg.in_dtype))
+        o = host(out)
+        bound = 2.0 ** -8 * np.abs(o_ref) + TOL * np.abs(o_ref).max(axis=-1, keepdims=True)
+        assert (np.abs(o - o_ref) <= bound).all()
+
+
+@pytest.mark.parametrize("name", ["gdn_serving", "kda_serving"])
+def test_serving_shape_sampled_heads_32_steps(name):
+    """Batch 256 x 32 heads x 128 x 128 in the benchmark's launch configuration; 64 sampled
+    heads are followed by the oracle through 32 consecutive steps (state and readout)."""
+    hla = need_gpu()
+    cfg = synth.CONFIGS[name]
+    rng = np.random.default_rng(77)
+    pairs = sample_heads(rng, cfg.B, cfg.H, 64)
+    S0 = synth.initial_state(cfg)
+    st = dev(S0)
+    S64 = np.stack([S0[b, h:h + 1] for b, h in pairs]).astype(np.float64)  # [64, 1, dk, dv]
+    bi = torch.tensor([b for b, _ in pairs], device="cuda")
+    hi = torch.tensor([h for _, h in pairs], device="cuda")
+    out = torch.empty((cfg.B, cfg.H, cfg.dv), device="cuda")
+    worst_s = worst_o = 0.0
+    for step in range(32):
+        x = synth.step_inputs(cfg, step)
+        _run(hla, name[:3], st, dev_inputs(x, cfg.in_dtype), out=out)
+        xs = gather_heads(f64_inputs(x, cfg.in_dtype), pairs)
+        o_ref = _orc(name[:3], S64, xs)
+        worst_o = max(worst_o, rel_err_tiles(host(out[bi, hi]), o_ref[:, 0], 1))
+        if step in (0, 7, 31):
+            worst_s = max(worst_s, rel_err_tiles(host(st[bi, hi]), S64[:, 0]))
+    print(f"{name}: worst state err {worst_s:.2e}, out err {worst_o:.2e}")
+    assert worst_s <= TOL and worst_o <= TOL
+
+
+def test_out_of_range_slot_sets_flag_and_is_skipped():
+    hla = need_gpu()
+    cfg = synth.shrink(synth.CONFIGS["gdn_serving"], B=3, H=2)
+    S0 = synth.initial_state(cfg, S=2)
+    st = dev(S0)
+    x = dev_inputs(synth.step_inputs(cfg, 0), cfg.in_dtype)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hla.gdn_step(st, x["q"], x["k"], x["v"], x["alpha"], x["beta"],
+                 slot=dev(np.array([1, 9, -1], np.int32)), err_flag=err)
+    assert int(err.item()) == hla.DEVERR_SLOT
+    got = host(st)
+    assert np.array_equal(got[0], S0[0]) and not np.array_equal(got[1], S0[1])
+    err.zero_()
+    hla.gdn_step(st, x["q"], x["k"], x["v"], x["alpha"], x["beta"],
+                 slot=dev(np.array([0, 1, -1], np.int32)), err_flag=err)
+    assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_bitwise_deterministic(kind):
+    hla = need_gpu()
+    cfg = synth.shrink(synth.CONFIGS[f"{kind}_serving"], B=16)
+    S0 = synth.initial_state(cfg)
+    x = dev_inputs(synth.step_inputs(cfg, 0), cfg.in_dtype)
+    a, b = dev(S0), dev(S0)
+    oa = _run(hla, kind, a, x)
+    ob = _run(hla, kind, b, x)
+    assert torch.equal(a, b) and torch.equal(oa, ob)
