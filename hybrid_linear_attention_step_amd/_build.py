@@ -24,7 +24,7 @@ FLAGS = [
     "-ffp-contract=off",
     # no packed-FP32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", f"-I{INCLUDE}", f"-I{CSRC}",
+    "-Wall", "-Wno-pass-failed", f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
 

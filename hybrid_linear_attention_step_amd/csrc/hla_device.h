@@ -144,17 +144,57 @@ __device__ __forceinline__ float sum_lane_bits(float x)
     return x;
 }
 
-// Maximum over the low NB lane bits (NB = 3: groups of 8 lanes, 4: groups
-// of 16).  max is exact, so any pairing pattern gives the same result.
+// Reduce-scatter of 8 column partials over lane bits 4 and 5 (4 row groups of
+// 16 lanes): one v_permlane16_swap pairs column c of the even 16-lane rows with
+// column c + 4 of the odd rows, so a single add leaves the even rows holding
+// column c and the odd rows column c + 4 (no copies); v_permlane32_swap then
+// does the same between lane halves for columns c and c + 2.  Afterwards lane
+// l holds, in o[0..1], the full 4-row-group sums of its columns
+// 4 * bit4(l) + 2 * bit5(l) + {0, 1}.  Sums are ((g0 + g1) + (g2 + g3)).
+__device__ __forceinline__ void reduce_scatter_rows4(const float (&a)[8], float (&o)[2])
+{
+    float s1[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[c]), __float_as_uint(a[c + 4]),
+                                                  false, false);
+        s1[c] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(s1[c]),
+                                                  __float_as_uint(s1[c + 2]), false, false);
+        o[c] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+}
+
+// Column offset (within the lane's 8) of o[0] after reduce_scatter_rows4.
+__device__ __forceinline__ int reduce_scatter_rows4_col(int lane)
+{
+    return 4 * ((lane >> 4) & 1) + 2 * ((lane >> 5) & 1);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
+
+// Maximum of non-negative finite floats over the low NB lane bits (NB = 3:
+// groups of 8 lanes, 4: groups of 16).  Non-negative IEEE floats order like
+// their bit patterns as unsigned integers, so the reduction runs on v_max_u32
+// with the DPP lane exchange fused into it (no NaN canonicalisation).  max is
+// exact, so any pairing pattern gives the same result.
 template <int NB>
 __device__ __forceinline__ float max_low_lane_bits(float x)
 {
     static_assert(NB == 3 || NB == 4, "row groups of 8 or 16 lanes");
-    x = fmaxf(x, dpp<DPP_QUAD_XOR1>(x));
-    x = fmaxf(x, dpp<DPP_QUAD_XOR2>(x));
-    x = fmaxf(x, dpp<DPP_ROW_HALF_MIRROR>(x));
-    if constexpr (NB == 4) x = fmaxf(x, dpp<DPP_ROW_MIRROR>(x));
-    return x;
+    uint32_t u = __float_as_uint(x);
+    u = max(u, dpp_u32<DPP_QUAD_XOR1>(u));
+    u = max(u, dpp_u32<DPP_QUAD_XOR2>(u));
+    u = max(u, dpp_u32<DPP_ROW_HALF_MIRROR>(u));
+    if constexpr (NB == 4) u = max(u, dpp_u32<DPP_ROW_MIRROR>(u));
+    return __uint_as_float(u);
 }
 
 } // namespace hla

@@ -29,11 +29,6 @@
 
 namespace hla {
 
-template <int DK>
-struct RowInputs {
-    static constexpr int RPL = DK / 8;  // rows per lane
-};
-
 // One token's update of a lane's tile.  x[m][c] is row (rg*RPL + m), column
 // (slice + 4*cg + c).  kk, qq, aa are this lane's rows of k, q and the decay
 // (aa[0] for a scalar decay).  Returns the readout for the lane's 4 columns
@@ -98,23 +93,90 @@ __device__ __forceinline__ void tile_store(float *S, int DV, const float (&x)[RP
     }
 }
 
-// Load one token's per-lane inputs: rows [row0, row0+RPL) of q, k (and of a
-// vector decay), the lane's 4 columns of v, and beta.
+// One token's per-lane inputs as loaded (raw 16-byte words): rows
+// [row0, row0+RPL) of q, k and of a vector decay, the lane's 4 columns of v,
+// the scalar decay and beta.  Loading and converting are separate steps so
+// that the bf16 unpacking (which waits for the data) can be scheduled after
+// the state loads have been issued.
+template <int DK, typename TIn, bool VEC>
+struct TokenRaw {
+    static constexpr int RPL = DK / 8;
+    static constexpr int QW = RPL * (int)sizeof(TIn) / 16;  // 16-byte words per row block
+    u32x4 k[QW], q[QW];
+    u32x4 a[VEC ? RPL / 4 : 1];
+    u32x2 v2;  // bf16 v
+    u32x4 v4;  // fp32 v
+    float a0, b0;
+};
+
 template <int DK, int DV, typename TIn, bool VEC>
-__device__ __forceinline__ void token_inputs(const TIn *q, const TIn *k, const TIn *v,
-                                             const float *alpha, const float *beta, size_t tok,
-                                             int row0, int col0, float (&qq)[DK / 8],
-                                             float (&kk)[DK / 8], float (&aa)[VEC ? DK / 8 : 1],
-                                             float (&vv)[4], float &bt)
+__device__ __forceinline__ void token_load(const TIn *q, const TIn *k, const TIn *v,
+                                           const float *alpha, const float *beta, size_t tok,
+                                           int row0, int col0, TokenRaw<DK, TIn, VEC> &R)
 {
-    load_in<DK / 8>(k + tok * DK + row0, kk);
-    load_in<DK / 8>(q + tok * DK + row0, qq);
-    if constexpr (VEC)
-        load_in<DK / 8>(alpha + tok * DK + row0, aa);
+    using TR = TokenRaw<DK, TIn, VEC>;
+    const u32x4 *kp = reinterpret_cast<const u32x4 *>(k + tok * DK + row0);
+    const u32x4 *qp = reinterpret_cast<const u32x4 *>(q + tok * DK + row0);
+#pragma unroll
+    for (int i = 0; i < TR::QW; ++i) {
+        R.k[i] = kp[i];
+        R.q[i] = qp[i];
+    }
+    if constexpr (VEC) {
+        const u32x4 *ap = reinterpret_cast<const u32x4 *>(alpha + tok * DK + row0);
+#pragma unroll
+        for (int i = 0; i < TR::RPL / 4; ++i) R.a[i] = ap[i];
+    } else {
+        R.a0 = alpha[tok];
+    }
+    if constexpr (sizeof(TIn) == 2)
+        R.v2 = *reinterpret_cast<const u32x2 *>(v + tok * DV + col0);
     else
-        aa[0] = alpha[tok];
-    load_in<4>(v + tok * DV + col0, vv);
-    bt = beta[tok];
+        R.v4 = *reinterpret_cast<const u32x4 *>(v + tok * DV + col0);
+    R.b0 = beta[tok];
+}
+
+template <int DK, typename TIn, bool VEC>
+__device__ __forceinline__ void token_convert(const TokenRaw<DK, TIn, VEC> &R, float (&qq)[DK / 8],
+                                              float (&kk)[DK / 8], float (&aa)[VEC ? DK / 8 : 1],
+                                              float (&vv)[4], float &bt)
+{
+    using TR = TokenRaw<DK, TIn, VEC>;
+#pragma unroll
+    for (int i = 0; i < TR::QW; ++i) {
+        if constexpr (sizeof(TIn) == 2) {
+            const uint32_t kw[4] = {R.k[i].x, R.k[i].y, R.k[i].z, R.k[i].w};
+            const uint32_t qw[4] = {R.q[i].x, R.q[i].y, R.q[i].z, R.q[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                kk[8 * i + 2 * j] = bf16_lo(kw[j]);
+                kk[8 * i + 2 * j + 1] = bf16_hi(kw[j]);
+                qq[8 * i + 2 * j] = bf16_lo(qw[j]);
+                qq[8 * i + 2 * j + 1] = bf16_hi(qw[j]);
+            }
+        } else {
+            kk[4 * i + 0] = __uint_as_float(R.k[i].x); kk[4 * i + 1] = __uint_as_float(R.k[i].y);
+            kk[4 * i + 2] = __uint_as_float(R.k[i].z); kk[4 * i + 3] = __uint_as_float(R.k[i].w);
+            qq[4 * i + 0] = __uint_as_float(R.q[i].x); qq[4 * i + 1] = __uint_as_float(R.q[i].y);
+            qq[4 * i + 2] = __uint_as_float(R.q[i].z); qq[4 * i + 3] = __uint_as_float(R.q[i].w);
+        }
+    }
+    if constexpr (VEC) {
+#pragma unroll
+        for (int i = 0; i < TR::RPL / 4; ++i) {
+            aa[4 * i + 0] = __uint_as_float(R.a[i].x); aa[4 * i + 1] = __uint_as_float(R.a[i].y);
+            aa[4 * i + 2] = __uint_as_float(R.a[i].z); aa[4 * i + 3] = __uint_as_float(R.a[i].w);
+        }
+    } else {
+        aa[0] = R.a0;
+    }
+    if constexpr (sizeof(TIn) == 2) {
+        vv[0] = bf16_lo(R.v2.x); vv[1] = bf16_hi(R.v2.x); vv[2] = bf16_lo(R.v2.y); vv[3] = bf16_hi(R.v2.y);
+    } else {
+        vv[0] = __uint_as_float(R.v4.x); vv[1] = __uint_as_float(R.v4.y);
+        vv[2] = __uint_as_float(R.v4.z); vv[3] = __uint_as_float(R.v4.w);
+    }
+    bt = R.b0;
 }
 
 template <int DK, int DV, typename TIn, typename TOut, bool VEC>
@@ -138,11 +200,12 @@ k_delta_step(float *__restrict__ state, int n_slots, const int32_t *__restrict__
     const int col0 = wave * 32 + cg * 4, row0 = rg * RPL;
     float *S = state + ((size_t)s * H + h) * (DK * DV) + (size_t)row0 * DV + col0;
 
-    float kk[RPL], qq[RPL], aa[VEC ? RPL : 1], vv[4], bt;
-    token_inputs<DK, DV, TIn, VEC>(q, k, v, alpha, beta, (size_t)bh, row0, col0, qq, kk, aa, vv,
-                                   bt);
+    TokenRaw<DK, TIn, VEC> raw;
+    token_load<DK, DV, TIn, VEC>(q, k, v, alpha, beta, (size_t)bh, row0, col0, raw);
     float x[RPL][4];
     tile_load<RPL>(S, DV, x);
+    float kk[RPL], qq[RPL], aa[VEC ? RPL : 1], vv[4], bt;
+    token_convert<DK, TIn, VEC>(raw, qq, kk, aa, vv, bt);
     float o[4];
     tile_token<RPL, VEC>(x, kk, qq, aa, bt, vv, o);
     tile_store<RPL>(S, DV, x);
@@ -180,8 +243,10 @@ k_replay(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
     tile_load<RPL>(S, DV, x);
     for (int t = 0; t < n; ++t) {
         const size_t tok = ((size_t)b * K + t) * H + h;
+        TokenRaw<DK, TIn, VEC> raw;
+        token_load<DK, DV, TIn, VEC>(q, k, v, alpha, beta, tok, row0, col0, raw);
         float kk[RPL], qq[RPL], aa[VEC ? RPL : 1], vv[4], bt;
-        token_inputs<DK, DV, TIn, VEC>(q, k, v, alpha, beta, tok, row0, col0, qq, kk, aa, vv, bt);
+        token_convert<DK, TIn, VEC>(raw, qq, kk, aa, vv, bt);
         float o[4];
         tile_token<RPL, VEC>(x, kk, qq, aa, bt, vv, o);
         if (out && rg == 0) store_out4(out + tok * DV + col0, o);

@@ -1,12 +1,17 @@
 """GPU parity of the mixed-precision state kernels (damp_quantize, damp_dequantize,
 damp_step) against the float64 oracle.
 
-Bars: FP32 scales bit-exact when both sides quantise the same FP32 values; INT8
-codes differ by at most 1 on at most 0.1% of values (the quantiser's FP32 rounding
-decision can land on the other side of a half-integer); the reconstructed state per
-head and the readout within 1e-3 relative (max-norm per head tile).  The step is
-checked teacher-forced (both sides start every step from the same packed state) and
-free-running (the drift statistics are reported)."""
+Bars: FP32 scales bit-exact when both sides quantise the same FP32 values (else
+within 1e-5 relative: the row maximum comes from an FP32 update on the GPU and a
+float64 one in the oracle); INT8 codes differ by at most 1 on at most 0.1% of values
+(the quantiser's FP32 rounding decision can land on the other side of a
+half-integer); FP16 rows differ by at most one FP16 ulp; every reconstructed value
+within one code step of the oracle's; the reconstructed state within 1e-3 relative in
+Frobenius norm per head (a single legitimate 1-code flip is a whole quantisation step,
+up to 1/127 of the row maximum, so a max-norm bar of 1e-3 could not hold); the
+readout within 1e-3 of max|o| per head.  The step is checked teacher-forced (both
+sides start every step from the same packed state) and free-running (the statistics
+are reported)."""
 import numpy as np
 import pytest
 
@@ -32,6 +37,42 @@ def _packed_host(hi_d, lo_d, sc_d):
 def _code_stats(lo_g, lo_o):
     d = np.abs(lo_g.astype(np.int32) - lo_o.astype(np.int32))
     return (float((d > 0).mean()) if d.size else 0.0), (int(d.max()) if d.size else 0)
+
+
+def _state_bars(g, o, perm, K_hi, dk):
+    """Compare two packed states (hi, lo, scale) and return the worst statistics."""
+    hi_g, lo_g, sc_g = g
+    hi_o, lo_o, sc_o = o
+    frac, dmax = _code_stats(lo_g, lo_o)
+    scale_rel = float((np.abs(sc_g.astype(np.float64) - sc_o) / sc_o).max()) if sc_o.size else 0.0
+    if hi_o.size:
+        a = hi_g.view(np.float16).astype(np.float64)
+        b = hi_o.view(np.float16).astype(np.float64)
+        ulp = np.spacing(np.maximum(np.abs(a), np.abs(b)).astype(np.float16)).astype(np.float64)
+        fp16_ulps = float((np.abs(a - b) / ulp).max())
+    else:
+        fp16_ulps = 0.0
+    if lo_o.size:
+        dq_g = lo_g.astype(np.float64) * sc_g[..., None]
+        dq_o = lo_o.astype(np.float64) * sc_o[..., None]
+        step = np.maximum(sc_g, sc_o)[..., None].astype(np.float64)
+        steps = float((np.abs(dq_g - dq_o) / step).max())
+    else:
+        steps = 0.0
+    s_g = oracle.damp_dequantize(hi_g, lo_g, sc_g, perm, K_hi, dk)
+    s_o = oracle.damp_dequantize(hi_o, lo_o, sc_o, perm, K_hi, dk)
+    d = (s_g - s_o).reshape(s_o.shape[0] * s_o.shape[1], -1)
+    r = s_o.reshape(d.shape)
+    frob = float((np.linalg.norm(d, axis=1) / np.maximum(np.linalg.norm(r, axis=1), 1e-30)).max())
+    return dict(frac=frac, dmax=dmax, scale_rel=scale_rel, fp16_ulps=fp16_ulps,
+                code_steps=steps, state=frob)
+
+
+def _assert_bars(w):
+    assert w["dmax"] <= 1 and w["frac"] <= CODE_FRAC
+    assert w["scale_rel"] <= 1e-5 and w["fp16_ulps"] <= 1.0
+    assert w["code_steps"] <= 1.001
+    assert w["state"] <= STATE_TOL and w["out"] <= STATE_TOL
 
 
 def _perm(rng, H, dk):
@@ -65,7 +106,7 @@ def _teacher_forced(hla, cfg, perm, steps, slot=None, n_slots=None):
     S0 = synth.initial_state(cfg, S=n_slots).astype(np.float64)
     hi, lo, sc = oracle.damp_quantize(S0, perm, cfg.K_hi)
     per = cfg.decay == "vector"
-    worst = dict(frac=0.0, dmax=0, state=0.0, out=0.0)
+    worst = {}
     for step in range(steps):
         x = synth.step_inputs(cfg, step)
         hi_d, lo_d, sc_d = _packed_dev(hi, lo, sc)
@@ -77,16 +118,12 @@ def _teacher_forced(hla, cfg, perm, steps, slot=None, n_slots=None):
         x64 = f64_inputs(x, cfg.in_dtype)
         o_ref = oracle.damp_step(hi, lo, sc, perm, cfg.K_hi, x64["q"], x64["k"], x64["v"],
                                  x64["alpha"], x64["beta"], per_channel=per, slot=slot)
-        hi_g, lo_g, sc_g = _packed_host(hi_d, lo_d, sc_d)
-        frac, dmax = _code_stats(lo_g, lo)
-        s_g = oracle.damp_dequantize(hi_g, lo_g, sc_g, perm, cfg.K_hi, cfg.dk)
-        s_o = oracle.damp_dequantize(hi, lo, sc, perm, cfg.K_hi, cfg.dk)
+        w = _state_bars(_packed_host(hi_d, lo_d, sc_d), (hi, lo, sc), perm, cfg.K_hi, cfg.dk)
         live = np.ones(cfg.B, bool) if slot is None else slot >= 0
         o = host(out)
-        worst["frac"] = max(worst["frac"], frac)
-        worst["dmax"] = max(worst["dmax"], dmax)
-        worst["state"] = max(worst["state"], rel_err_tiles(s_g, s_o))
-        worst["out"] = max(worst["out"], rel_err_tiles(o[live], o_ref[live], 1))
+        w["out"] = rel_err_tiles(o[live], o_ref[live], 1)
+        for key, val in w.items():
+            worst[key] = max(worst.get(key, 0), val)
         assert (o[~live] == 3.0).all()
     return worst
 
@@ -104,8 +141,7 @@ def test_step_teacher_forced(decay, dk, dv, K_hi, use_perm):
     slot = np.array([3, -1, 0, 5, 1], np.int32)
     w = _teacher_forced(hla, cfg, perm, steps=4, slot=slot, n_slots=6)
     print(w)
-    assert w["dmax"] <= 1 and w["frac"] <= CODE_FRAC
-    assert w["state"] <= STATE_TOL and w["out"] <= STATE_TOL
+    _assert_bars(w)
 
 
 def test_workload_plan_teacher_forced():
@@ -115,18 +151,60 @@ def test_workload_plan_teacher_forced():
     cfg = synth.shrink(synth.CONFIGS["damp_kda"], B=8)
     w = _teacher_forced(hla, cfg, synth.damp_key_perm(cfg), steps=4)
     print(w)
-    assert w["dmax"] <= 1 and w["frac"] <= CODE_FRAC
-    assert w["state"] <= STATE_TOL and w["out"] <= STATE_TOL
+    _assert_bars(w)
 
 
-def test_free_running_32_steps_report():
-    """Both sides run 32 steps from the same packed state without re-synchronising; the
-    reconstructed state stays within the bar and the code statistics are reported."""
+def test_many_heads_per_block_teacher_forced():
+    """More heads than resident workgroups (1,280 heads with padding requests), so the
+    persistent kernel walks several heads per workgroup through its double-buffered LDS."""
+    hla = need_gpu()
+    cfg = synth.shrink(synth.CONFIGS["damp_kda"], B=40)
+    slot = np.arange(cfg.B, dtype=np.int32)
+    slot[[3, 17, 38]] = -1
+    w = _teacher_forced(hla, cfg, synth.damp_key_perm(cfg), steps=2, slot=slot)
+    print(w)
+    _assert_bars(w)
+
+
+@pytest.mark.parametrize("K_hi,decay", [(16, 1), (0, 1), (32, 0)])
+def test_scale_buffer_alignment_does_not_change_results(K_hi, decay):
+    """lo_scale only needs 4-byte alignment: a scale buffer 4 bytes off a 16-byte boundary
+    gives the same bits as an aligned one, over 1,280 heads and 3 steps."""
+    hla = need_gpu()
+    cfg = synth.shrink(synth.CONFIGS["damp_kda"], B=40, K_hi=K_hi,
+                       decay="vector" if decay else "scalar")
+    perm = dev(synth.damp_key_perm(synth.shrink(cfg, K_hi=max(K_hi, 1))))
+    hi0, lo0, sc0 = hla.damp_quantize(dev(synth.initial_state(cfg)), perm, K_hi)
+    runs = []
+    for misalign in (0, 1):
+        hi, lo = hi0.clone(), lo0.clone()
+        buf = torch.empty(sc0.numel() + 4, dtype=torch.float32, device="cuda")
+        sc = buf[misalign:misalign + sc0.numel()].view(sc0.shape)
+        sc.copy_(sc0)
+        assert (sc.data_ptr() % 16 == 0) == (misalign == 0)
+        outs = []
+        for step in range(3):
+            xd = dev_inputs(synth.step_inputs(cfg, step), cfg.in_dtype)
+            outs.append(hla.damp_step(hi, lo, sc, perm, K_hi, xd["q"], xd["k"], xd["v"],
+                                      xd["alpha"], decay, xd["beta"]))
+        runs.append((hi, lo, sc.clone(), outs))
+    (h0, l0, s0, o0), (h1, l1, s1, o1) = runs
+    assert torch.equal(h0, h1) and torch.equal(l0, l1) and torch.equal(s0, s1)
+    assert all(torch.equal(a, b) for a, b in zip(o0, o1))
+
+
+def test_free_running_32_steps_drift():
+    """Both sides run 32 steps of the quantised recurrence from the same packed state without
+    re-synchronising.  Individual codes drift apart (a flipped code at a row maximum changes
+    that row's scale, after which the two trajectories round independently: the error
+    accumulation of DAMP section 3.3), so the bar here is statistical: each trajectory's drift
+    from the unquantised FP32 recurrence (DAMP Eq. (8)) is of the same size on both sides."""
     hla = need_gpu()
     cfg = synth.shrink(synth.CONFIGS["damp_kda"], B=4)
     perm = synth.damp_key_perm(cfg)
     S0 = synth.initial_state(cfg).astype(np.float64)
     hi, lo, sc = oracle.damp_quantize(S0, perm, cfg.K_hi)
+    S_fp = oracle.damp_dequantize(hi, lo, sc, perm, cfg.K_hi, cfg.dk)  # same start, unquantised
     hi_d, lo_d, sc_d = _packed_dev(hi, lo, sc)
     perm_d = dev(perm)
     report = {}
@@ -138,16 +216,25 @@ def test_free_running_32_steps_report():
         x64 = f64_inputs(x, cfg.in_dtype)
         o_ref = oracle.damp_step(hi, lo, sc, perm, cfg.K_hi, x64["q"], x64["k"], x64["v"],
                                  x64["alpha"], x64["beta"], per_channel=True)
+        o_fp = oracle.kda_step(S_fp, x64["q"], x64["k"], x64["v"], x64["alpha"], x64["beta"])
         if step in (0, 7, 31):
-            hi_g, lo_g, sc_g = _packed_host(hi_d, lo_d, sc_d)
-            frac, dmax = _code_stats(lo_g, lo)
-            st = rel_err_tiles(oracle.damp_dequantize(hi_g, lo_g, sc_g, perm, cfg.K_hi, cfg.dk),
-                               oracle.damp_dequantize(hi, lo, sc, perm, cfg.K_hi, cfg.dk))
-            report[step + 1] = dict(code_frac=frac, code_dmax=dmax, state=st,
-                                    out=rel_err_tiles(host(o), o_ref, 1))
+            g = _packed_host(hi_d, lo_d, sc_d)
+            w = _state_bars(g, (hi, lo, sc), perm, cfg.K_hi, cfg.dk)
+            s_g = oracle.damp_dequantize(*g, perm, cfg.K_hi, cfg.dk)
+            s_o = oracle.damp_dequantize(hi, lo, sc, perm, cfg.K_hi, cfg.dk)
+            nfp = np.linalg.norm(S_fp)
+            w["drift_gpu"] = float(np.linalg.norm(s_g - S_fp) / nfp)
+            w["drift_oracle"] = float(np.linalg.norm(s_o - S_fp) / nfp)
+            on = np.linalg.norm(o_fp)
+            w["out_drift_gpu"] = float(np.linalg.norm(host(o) - o_fp) / on)
+            w["out_drift_oracle"] = float(np.linalg.norm(o_ref - o_fp) / on)
+            report[step + 1] = w
     print(report)
+    first = dict(report[1], out=0.0)
+    _assert_bars(first)  # one step from the same state is the teacher-forced case
     for r in report.values():
-        assert r["state"] <= STATE_TOL and r["out"] <= STATE_TOL
+        assert r["drift_gpu"] <= 1.5 * r["drift_oracle"] + 1e-4
+        assert r["out_drift_gpu"] <= 1.5 * r["out_drift_oracle"] + 1e-4
 
 
 def test_serving_shape_sampled_heads_teacher_forced():
@@ -181,17 +268,14 @@ def test_serving_shape_sampled_heads_teacher_forced():
             o_ref[i] = oracle.damp_step(hs, ls, ss, perm[h:h + 1], cfg.K_hi, xi["q"], xi["k"],
                                         xi["v"], xi["alpha"], xi["beta"], per_channel=True)[0, 0]
             hi_s[i], lo_s[i], sc_s[i] = hs[0], ls[0], ss[0]
-        hi_g = hi_d[bi, hh][:, None].cpu().numpy().view(np.uint16)
-        lo_g = lo_d[bi, hh][:, None].cpu().numpy()
-        sc_g = sc_d[bi, hh][:, None].cpu().numpy()
-        frac, dmax = _code_stats(lo_g, lo_s)
-        assert dmax <= 1 and frac <= CODE_FRAC
+        g = (hi_d[bi, hh][:, None].cpu().numpy().view(np.uint16),
+             lo_d[bi, hh][:, None].cpu().numpy(), sc_d[bi, hh][:, None].cpu().numpy())
         for i, (b, h) in enumerate(pairs):
-            s_g = oracle.damp_dequantize(hi_g[i:i + 1], lo_g[i:i + 1], sc_g[i:i + 1],
-                                         perm[h:h + 1], cfg.K_hi, cfg.dk)
-            s_o = oracle.damp_dequantize(hi_s[i:i + 1], lo_s[i:i + 1], sc_s[i:i + 1],
-                                         perm[h:h + 1], cfg.K_hi, cfg.dk)
-            assert rel_err_tiles(s_g, s_o) <= STATE_TOL
+            w = _state_bars(tuple(a[i:i + 1] for a in g),
+                            (hi_s[i:i + 1], lo_s[i:i + 1], sc_s[i:i + 1]), perm[h:h + 1],
+                            cfg.K_hi, cfg.dk)
+            w["out"] = 0.0
+            _assert_bars(w)
         assert rel_err_tiles(host(o[bi, hh]), o_ref, 1) <= STATE_TOL
 
 
