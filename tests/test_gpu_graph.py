@@ -1,0 +1,85 @@
+"""The entry points launched under HIP graph capture (as a decode loop runs them) give the
+same results as the same launches issued eagerly: bitwise, on every replay, with eager work
+and synchronisations between the replays."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import dev, dev_inputs, need_gpu, torch
+
+pytestmark = pytest.mark.gpu
+REPLAYS = 4
+
+
+def _check_replays(launch, eager_state, graph_state):
+    """launch(state, i) issues step i on `state`.  The graph holds steps 0 and 1; every
+    replay is compared with the eager state after the same steps."""
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch(graph_state, 0)
+        launch(graph_state, 1)
+    for r in range(REPLAYS):
+        g.replay()
+        launch(eager_state, 0)  # eager work between replays
+        launch(eager_state, 1)
+        torch.cuda.synchronize()
+        for a, b in zip(eager_state, graph_state):
+            assert torch.equal(a, b), f"replay {r} differs from eager"
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_step_graph_replays(kind):
+    hla = need_gpu()
+    base = synth.CONFIGS["kda_serving" if kind == "kda" else "gdn_serving"]
+    cfg = synth.shrink(base, B=9, H=5)
+    fn = hla.kda_step if kind == "kda" else hla.gdn_step
+    xs = [dev_inputs(synth.step_inputs(cfg, s), cfg.in_dtype) for s in range(2)]
+    S0 = synth.initial_state(cfg)
+    st_e, st_g = dev(S0), dev(S0)
+    out_e = torch.empty((cfg.B, cfg.H, cfg.dv), device="cuda")
+    out_g = torch.empty_like(out_e)
+
+    def launch(state, i):
+        x = xs[i]
+        o = out_e if state[0] is st_e else out_g
+        fn(state[0], x["q"], x["k"], x["v"], x["alpha"], x["beta"], out=o)
+
+    _check_replays(launch, [st_e, out_e], [st_g, out_g])
+
+
+def test_damp_graph_replays():
+    hla = need_gpu()
+    cfg = synth.shrink(synth.CONFIGS["damp_kda"], B=6, H=4)
+    perm = dev(synth.damp_key_perm(cfg))
+    S0 = dev(synth.initial_state(cfg))
+    codes_e = list(hla.damp_quantize(S0, perm, cfg.K_hi))
+    codes_g = [c.clone() for c in codes_e]
+    xs = [dev_inputs(synth.step_inputs(cfg, s), cfg.in_dtype) for s in range(2)]
+    out_e = torch.empty((cfg.B, cfg.H, cfg.dv), device="cuda")
+    out_g = torch.empty_like(out_e)
+
+    def launch(state, i):
+        x = xs[i]
+        o = out_e if state[0] is codes_e[0] else out_g
+        hla.damp_step(state[0], state[1], state[2], perm, cfg.K_hi, x["q"], x["k"], x["v"],
+                      x["alpha"], 1, x["beta"], out=o)
+
+    _check_replays(launch, codes_e + [out_e], codes_g + [out_g])
+
+
+def test_replay_accepted_graph_replays():
+    hla = need_gpu()
+    cfg = synth.shrink(synth.CONFIGS["dasc_gdn"], B=7, H=3)
+    x = {k: dev(v) for k, v in synth.replay_inputs(cfg, 0).items()}
+    S0 = synth.initial_state(cfg)
+    st_e, st_g = dev(S0), dev(S0)
+    out_e = torch.zeros((cfg.B, cfg.K, cfg.H, cfg.dv), device="cuda")  # rows past n_accept
+    out_g = torch.zeros_like(out_e)                                    # are left as they are
+
+    def launch(state, i):
+        o = out_e if state[0] is st_e else out_g
+        hla.replay_accepted(state[0], x["q"], x["k"], x["v"], x["alpha"], x["beta"],
+                            x["n_accept"], 0, out=o)
+
+    _check_replays(launch, [st_e, out_e], [st_g, out_g])
