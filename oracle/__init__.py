@@ -58,9 +58,10 @@ def _declare(L):
     L.orc_double_to_half.argtypes = [ctypes.c_double]
     L.orc_double_to_half.restype = ctypes.c_uint16
     L.orc_quantize_row_int8.argtypes = [_P, _I, _P, _P]
-    L.orc_damp_quantize.argtypes = [_P, _I, _I, _I, _I, _P, _I, _P, _P, _P]
-    L.orc_damp_dequantize.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _I, _P]
-    L.orc_damp_step.argtypes = [_P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I,
+    L.orc_damp_quantize.argtypes = [_P, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P]
+    L.orc_damp_dequantize.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P]
+    L.orc_sr_step.argtypes = [_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P]
+    L.orc_damp_step.argtypes = [_P, _P, _P, _I, _P, _I, _I, _P, _P, _P, _I, _I, _I, _I,
                                 _P, _P, _P, _P, _I, _P, _P]
     L.orc_dasc_plan.argtypes = [_P, _I, _I, _P, _P]
     L.orc_dasc_plan.restype = _I
@@ -157,37 +158,67 @@ def quantize_row_int8(x):
 
 # --------------------------------------------------------------------- DAMP
 
-def damp_alloc(S, H, dk, dv, K_hi):
+def _group(group, dv):
+    g = dv if group is None else int(group)
+    if g <= 0 or dv % g:
+        raise ValueError(f"group {g} must divide dv {dv}")
+    return g
+
+
+def _scale_shape(S, H, dk, dv, K_hi, group):
+    """One FP32 scale per INT8 row ([S,H,dk-K_hi]) or per group ([S,H,dk-K_hi,dv/group])."""
+    return (S, H, dk - K_hi) if group == dv else (S, H, dk - K_hi, dv // group)
+
+
+def _sr(val_perm, val_scale):
+    vp = None if val_perm is None else _i32(val_perm)
+    vs = None if val_scale is None else np.ascontiguousarray(val_scale, np.float32)
+    return vp, vs
+
+
+def damp_alloc(S, H, dk, dv, K_hi, group=None):
+    g = _group(group, dv)
     return (np.zeros((S, H, K_hi, dv), np.uint16), np.zeros((S, H, dk - K_hi, dv), np.int8),
-            np.zeros((S, H, dk - K_hi), np.float32))
+            np.zeros(_scale_shape(S, H, dk, dv, K_hi, g), np.float32))
 
 
-def damp_quantize(state, key_perm, K_hi):
+def _group_of(sc, dv):
+    return dv if sc.ndim == 3 else dv // sc.shape[3]
+
+
+def damp_quantize(state, key_perm, K_hi, group=None, val_perm=None, val_scale=None):
+    """state S [S,H,dk,dv] in original coordinates -> packed (hi, lo, scale) of the
+    transformed state T (value permutation val_perm, stored-order scales val_scale)."""
     state = _f64(state)
     S, H, dk, dv = state.shape
-    hi, lo, sc = damp_alloc(S, H, dk, dv, K_hi)
+    g = _group(group, dv)
+    hi, lo, sc = damp_alloc(S, H, dk, dv, K_hi, g)
     kp = _i32(key_perm)
-    lib().orc_damp_quantize(_ptr(state), S, H, dk, dv, _ptr(kp), K_hi, _ptr(hi), _ptr(lo),
-                            _ptr(sc))
+    vp, vs = _sr(val_perm, val_scale)
+    lib().orc_damp_quantize(_ptr(state), S, H, dk, dv, _ptr(kp), K_hi, g, _ptr(vp), _ptr(vs),
+                            _ptr(hi), _ptr(lo), _ptr(sc))
     return hi, lo, sc
 
 
-def damp_dequantize(hi, lo, sc, key_perm, K_hi, dk):
+def damp_dequantize(hi, lo, sc, key_perm, K_hi, dk, val_perm=None, val_scale=None):
     S, H = sc.shape[:2]
     dv = lo.shape[-1] if lo.size else hi.shape[-1]
+    g = _group_of(sc, dv)
     hi = np.ascontiguousarray(hi, np.uint16)
     lo = np.ascontiguousarray(lo, np.int8)
     sc = np.ascontiguousarray(sc, np.float32)
     kp = _i32(key_perm)
+    vp, vs = _sr(val_perm, val_scale)
     out = np.zeros((S, H, dk, dv), np.float64)
-    lib().orc_damp_dequantize(_ptr(hi), _ptr(lo), _ptr(sc), S, H, dk, dv, _ptr(kp), K_hi,
-                              _ptr(out))
+    lib().orc_damp_dequantize(_ptr(hi), _ptr(lo), _ptr(sc), S, H, dk, dv, _ptr(kp), K_hi, g,
+                              _ptr(vp), _ptr(vs), _ptr(out))
     return out
 
 
 def damp_step(hi, lo, sc, key_perm, K_hi, q, k, v, alpha, beta, *, per_channel, slot=None,
-              want_out=True):
-    """One step of the quantised recurrence on the packed state (in place)."""
+              want_out=True, val_perm=None, val_scale=None):
+    """One step of the quantised recurrence on the packed state (in place).  The scale
+    granularity (per row or per group) is read off the shape of `sc`."""
     for a, dt, nm in ((hi, np.uint16, "hi"), (lo, np.int8, "lo"), (sc, np.float32, "scale")):
         if not (isinstance(a, np.ndarray) and a.dtype == dt and a.flags.c_contiguous):
             raise TypeError(f"{nm} must be a C-contiguous {np.dtype(dt).name} array")
@@ -195,12 +226,30 @@ def damp_step(hi, lo, sc, key_perm, K_hi, q, k, v, alpha, beta, *, per_channel, 
     q, k, v, alpha, beta = map(_f64, (q, k, v, alpha, beta))
     B, _, dk = q.shape
     dv = v.shape[-1]
+    g = _group_of(sc, dv)
     kp = _i32(key_perm)
+    vp, vs = _sr(val_perm, val_scale)
     slot = _i32(slot)
     out = np.full((B, H, dv), np.nan) if want_out else None
-    lib().orc_damp_step(_ptr(hi), _ptr(lo), _ptr(sc), S, _ptr(kp), K_hi, _ptr(slot), B, H, dk,
-                        dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), int(bool(per_channel)),
-                        _ptr(beta), _ptr(out))
+    lib().orc_damp_step(_ptr(hi), _ptr(lo), _ptr(sc), S, _ptr(kp), K_hi, g, _ptr(vp),
+                        _ptr(vs), _ptr(slot), B, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
+                        _ptr(alpha), int(bool(per_channel)), _ptr(beta), _ptr(out))
+    return out
+
+
+def sr_step(state, q, k, v, alpha, beta, *, per_channel, val_perm=None, val_scale=None,
+            slot=None, want_out=True):
+    """Float64 transformed step ([DAMP] App. A.3 Eq. (18)) on T, in place, no quantisation."""
+    _need_f64_inplace(state, "state")
+    S, H, dk, dv = state.shape
+    q, k, v, alpha, beta = map(_f64, (q, k, v, alpha, beta))
+    B = q.shape[0]
+    vp, vs = _sr(val_perm, val_scale)
+    slot = _i32(slot)
+    out = np.full((B, H, dv), np.nan) if want_out else None
+    lib().orc_sr_step(_ptr(state), S, _ptr(slot), B, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
+                      _ptr(alpha), int(bool(per_channel)), _ptr(beta), _ptr(vp), _ptr(vs),
+                      _ptr(out))
     return out
 
 

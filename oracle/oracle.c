@@ -236,12 +236,85 @@ ORC_API void orc_quantize_row_int8(const double *x, int n, int8_t *code, float *
 }
 
 /* ------------------------------------------------------------------------ */
-/* Mixed-precision packed state ([DAMP] §5.2, App. A.4): for each head the   */
-/* rows are reordered by key_perm so that packed row r holds key channel     */
-/* key_perm[h*dk + r]; rows r < K_hi are stored as FP16 in `hi`              */
+/* Value scaling and reordering ("SR", [DAMP] App. A.1 and App. A.3         */
+/* Eq. (17)-(18)).  Per head, a value permutation pi and positive scales c   */
+/* define the transformed state T = S D_c^{-1} P_V^T, i.e.                   */
+/*     T[i][j] = S[i][pi(j)] / c'_j ,   c'_j = c_{pi(j)} ,                   */
+/* where c' (`val_scale`, [H, dv] fp32) is given in the transformed (stored) */
+/* value order.  The update runs on T with v' = P_V D_c^{-1} v, i.e.        */
+/* v'_j = v_{pi(j)} / c'_j, and the readout is o'_j = c'_j (T^T q)_j, which  */
+/* equals o_{pi(j)}.  `val_perm` ([H, dv] int32, pi) may be NULL: then v is  */
+/* already in stored value order and o is written in stored order (the page  */
+/* absorbs P_V into the projection weights); otherwise v is read and o is    */
+/* written in original value order.  `val_scale` NULL means c' = 1.          */
+/* The key-channel side of Eq. (17) (P_K) is the packed row order below; the */
+/* oracle keeps rows in original key order while it computes, which is the   */
+/* same arithmetic with the rows relabelled.                                 */
+/* ------------------------------------------------------------------------ */
+static int orc_vperm(const int32_t *val_perm, int h, int dv, int j)
+{
+    return val_perm ? val_perm[(long)h * dv + j] : j;
+}
+
+static double orc_vscale(const float *val_scale, int h, int dv, int j)
+{
+    return val_scale ? (double)val_scale[(long)h * dv + j] : 1.0;
+}
+
+/* Eq. (18) for one head and one token on T (float64, no quantisation). */
+static void orc_sr_step_head(double *T, int dk, int dv, int h, const double *q,
+                             const double *k, const double *v, const double *a,
+                             double beta, const int32_t *val_perm,
+                             const float *val_scale, double *o /* may be NULL */)
+{
+    double *vt = (double *)calloc((size_t)dv, sizeof(double));
+    double *ot = (double *)calloc((size_t)dv, sizeof(double));
+    for (int j = 0; j < dv; ++j)
+        vt[j] = v[orc_vperm(val_perm, h, dv, j)] / orc_vscale(val_scale, h, dv, j);
+    orc_step_head(T, dk, dv, q, k, vt, a, beta, o ? ot : NULL);
+    if (o)
+        for (int j = 0; j < dv; ++j)
+            o[orc_vperm(val_perm, h, dv, j)] = orc_vscale(val_scale, h, dv, j) * ot[j];
+    free(ot);
+    free(vt);
+}
+
+/* Batched Eq. (18) on a float64 transformed state [n_slots, H, dk, dv] (no
+   quantisation): the transformed block is functionally the original one
+   ([DAMP] App. A.3), which the tests check against orc_kda_step. */
+ORC_API void orc_sr_step(double *state, int n_slots, const int32_t *slot, int B, int H,
+                         int dk, int dv, const double *q, const double *k,
+                         const double *v, const double *alpha, int decay_per_channel,
+                         const double *beta, const int32_t *val_perm,
+                         const float *val_scale, double *out)
+{
+    double *a = (double *)malloc(sizeof(double) * dk);
+    for (int b = 0; b < B; ++b) {
+        long s = orc_slot(slot, b, n_slots);
+        if (s < 0) continue;
+        for (int h = 0; h < H; ++h) {
+            long bh = (long)b * H + h;
+            for (int i = 0; i < dk; ++i)
+                a[i] = decay_per_channel ? alpha[bh * dk + i] : alpha[bh];
+            orc_sr_step_head(state + (s * H + h) * (long)dk * dv, dk, dv, h, q + bh * dk,
+                             k + bh * dk, v + bh * dv, a, beta[bh], val_perm, val_scale,
+                             out ? out + bh * dv : NULL);
+        }
+    }
+    free(a);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Mixed-precision packed state ([DAMP] §5.2, App. A.1 and A.4): for each    */
+/* head the rows are reordered by key_perm so that packed row r holds key    */
+/* channel key_perm[h*dk + r]; rows r < K_hi are stored as FP16 in `hi`      */
 /* [S, H, K_hi, dv], rows r >= K_hi as INT8 codes in `lo`                    */
-/* [S, H, dk-K_hi, dv] with one FP32 scale per row in `scale`                */
-/* [S, H, dk-K_hi].  key_perm == NULL means identity order.                  */
+/* [S, H, dk-K_hi, dv] with one FP32 scale per `group` consecutive values of */
+/* the row in `scale` [S, H, dk-K_hi, dv/group] (group = dv: one scale per   */
+/* row, as [DAMP] §3.2 and [dasc] App. E.1; group = 32: App. A.1 / A.4).     */
+/* Every group is quantised on its own by the quantiser above.  The stored  */
+/* values are those of T (value side of Eq. (17)); key_perm == NULL means    */
+/* identity key order.                                                       */
 /* ------------------------------------------------------------------------ */
 static int orc_perm(const int32_t *key_perm, int h, int dk, int r)
 {
@@ -249,12 +322,14 @@ static int orc_perm(const int32_t *key_perm, int h, int dk, int r)
 }
 
 /* Reconstruct one head (hi/lo/scale point at that head's rows) into a
-   float64 dk x dv matrix in original channel order: an FP16 value becomes
-   its exact value, an INT8 code c with row scale s becomes c * s. */
+   float64 dk x dv matrix T, rows in original key order, values in stored
+   order: an FP16 value becomes its exact value, an INT8 code c of group g
+   becomes c * s_g. */
 static void orc_damp_unpack_head(const uint16_t *hi, const int8_t *lo,
                                  const float *scale, const int32_t *key_perm, int h,
-                                 int K_hi, int dk, int dv, double *S)
+                                 int K_hi, int group, int dk, int dv, double *T)
 {
+    int ng = dv / group;
     for (int r = 0; r < dk; ++r) {
         int u = orc_perm(key_perm, h, dk, r);
         for (int j = 0; j < dv; ++j) {
@@ -262,70 +337,96 @@ static void orc_damp_unpack_head(const uint16_t *hi, const int8_t *lo,
             if (r < K_hi)
                 x = orc_half_to_double(hi[(long)r * dv + j]);
             else
-                x = (double)lo[(long)(r - K_hi) * dv + j] * (double)scale[r - K_hi];
-            S[(long)u * dv + j] = x;
+                x = (double)lo[(long)(r - K_hi) * dv + j] *
+                    (double)scale[(long)(r - K_hi) * ng + j / group];
+            T[(long)u * dv + j] = x;
         }
     }
 }
 
-/* Store one head: FP16 rows round the float64 value to the nearest half
-   (ties to even); INT8 rows use the row quantiser above. */
-static void orc_damp_pack_head(const double *S, const int32_t *key_perm, int h,
-                               int K_hi, int dk, int dv, uint16_t *hi, int8_t *lo,
-                               float *scale)
+/* Store one head of T: FP16 rows round the float64 value to the nearest
+   half (ties to even); INT8 rows are quantised group by group. */
+static void orc_damp_pack_head(const double *T, const int32_t *key_perm, int h,
+                               int K_hi, int group, int dk, int dv, uint16_t *hi,
+                               int8_t *lo, float *scale)
 {
+    int ng = dv / group;
     for (int r = 0; r < dk; ++r) {
         int u = orc_perm(key_perm, h, dk, r);
-        const double *row = S + (long)u * dv;
+        const double *row = T + (long)u * dv;
         if (r < K_hi) {
             for (int j = 0; j < dv; ++j)
                 hi[(long)r * dv + j] = orc_double_to_half(row[j]);
         } else {
-            orc_quantize_row_int8(row, dv, lo + (long)(r - K_hi) * dv,
-                                  scale + (r - K_hi));
+            for (int g = 0; g < ng; ++g)
+                orc_quantize_row_int8(row + (long)g * group, group,
+                                      lo + (long)(r - K_hi) * dv + (long)g * group,
+                                      scale + (long)(r - K_hi) * ng + g);
         }
     }
 }
 
+/* state S [S, H, dk, dv] in original coordinates -> packed T (Eq. (17)). */
 ORC_API void orc_damp_quantize(const double *state, int S, int H, int dk, int dv,
-                               const int32_t *key_perm, int K_hi, uint16_t *hi,
-                               int8_t *lo, float *scale)
+                               const int32_t *key_perm, int K_hi, int group,
+                               const int32_t *val_perm, const float *val_scale,
+                               uint16_t *hi, int8_t *lo, float *scale)
 {
-    int nlo = dk - K_hi;
+    int nlo = dk - K_hi, ng = dv / group;
+    double *T = (double *)malloc(sizeof(double) * dk * dv);
     for (long sh = 0; sh < (long)S * H; ++sh) {
         int h = (int)(sh % H);
-        orc_damp_pack_head(state + sh * dk * dv, key_perm, h, K_hi, dk, dv,
-                           hi + sh * K_hi * dv, lo + sh * nlo * dv, scale + sh * nlo);
+        const double *Sh = state + sh * dk * dv;
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                T[(long)i * dv + j] = Sh[(long)i * dv + orc_vperm(val_perm, h, dv, j)] /
+                                      orc_vscale(val_scale, h, dv, j);
+        orc_damp_pack_head(T, key_perm, h, K_hi, group, dk, dv, hi + sh * K_hi * dv,
+                           lo + sh * nlo * dv, scale + sh * nlo * ng);
     }
+    free(T);
 }
 
+/* packed T -> state S in original coordinates: S[i][pi(j)] = T[i][j] c'_j. */
 ORC_API void orc_damp_dequantize(const uint16_t *hi, const int8_t *lo,
                                  const float *scale, int S, int H, int dk, int dv,
-                                 const int32_t *key_perm, int K_hi, double *state)
+                                 const int32_t *key_perm, int K_hi, int group,
+                                 const int32_t *val_perm, const float *val_scale,
+                                 double *state)
 {
-    int nlo = dk - K_hi;
+    int nlo = dk - K_hi, ng = dv / group;
+    double *T = (double *)malloc(sizeof(double) * dk * dv);
     for (long sh = 0; sh < (long)S * H; ++sh) {
         int h = (int)(sh % H);
-        orc_damp_unpack_head(hi + sh * K_hi * dv, lo + sh * nlo * dv, scale + sh * nlo,
-                             key_perm, h, K_hi, dk, dv, state + sh * dk * dv);
+        orc_damp_unpack_head(hi + sh * K_hi * dv, lo + sh * nlo * dv, scale + sh * nlo * ng,
+                             key_perm, h, K_hi, group, dk, dv, T);
+        double *Sh = state + sh * dk * dv;
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                Sh[(long)i * dv + orc_vperm(val_perm, h, dv, j)] =
+                    T[(long)i * dv + j] * orc_vscale(val_scale, h, dv, j);
     }
+    free(T);
 }
 
 /* Quantised recurrence, [DAMP] §3.3 Eq. (7): S^q_t = Q(A_t S^q_{t-1} +
-   beta k v^T).  Reconstruct the stored state, run the float64 step of
-   Eq. (2), take the readout from the updated state before it is stored
-   again (App. A.4: update and readout in full precision, then requantise),
+   beta k v^T), run in the transformed coordinates of App. A.3 Eq. (18).
+   Reconstruct the stored T, run the float64 transformed step, take the
+   readout from the updated T before it is stored again (App. A.4: update and
+   readout in full precision, then requantise with recomputed group scales),
    then store it back in the packed format.
    alpha is [B, H] (decay_per_channel == 0, GDN) or [B, H, dk] (KDA), always in
-   original channel order, like q and k. */
+   original key-channel order, like q and k. */
 ORC_API void orc_damp_step(uint16_t *hi, int8_t *lo, float *scale, int n_slots,
-                           const int32_t *key_perm, int K_hi, const int32_t *slot,
-                           int B, int H, int dk, int dv, const double *q,
-                           const double *k, const double *v, const double *alpha,
-                           int decay_per_channel, const double *beta, double *out)
+                           const int32_t *key_perm, int K_hi, int group,
+                           const int32_t *val_perm, const float *val_scale,
+                           const int32_t *slot, int B, int H, int dk, int dv,
+                           const double *q, const double *k, const double *v,
+                           const double *alpha, int decay_per_channel,
+                           const double *beta, double *out)
 {
-    int nlo = dk - K_hi;
-    double *S = (double *)malloc(sizeof(double) * dk * dv);
+    int nlo = dk - K_hi, ng = dv / group;
+    double *T = (double *)malloc(sizeof(double) * dk * dv);
     double *a = (double *)malloc(sizeof(double) * dk);
     for (int b = 0; b < B; ++b) {
         long s = orc_slot(slot, b, n_slots);
@@ -336,15 +437,16 @@ ORC_API void orc_damp_step(uint16_t *hi, int8_t *lo, float *scale, int n_slots,
             for (int i = 0; i < dk; ++i)
                 a[i] = decay_per_channel ? alpha[bh * dk + i] : alpha[bh];
             orc_damp_unpack_head(hi + sh * K_hi * dv, lo + sh * nlo * dv,
-                                 scale + sh * nlo, key_perm, h, K_hi, dk, dv, S);
-            orc_step_head(S, dk, dv, q + bh * dk, k + bh * dk, v + bh * dv, a,
-                          beta[bh], out ? out + bh * dv : NULL);
-            orc_damp_pack_head(S, key_perm, h, K_hi, dk, dv, hi + sh * K_hi * dv,
-                               lo + sh * nlo * dv, scale + sh * nlo);
+                                 scale + sh * nlo * ng, key_perm, h, K_hi, group, dk, dv,
+                                 T);
+            orc_sr_step_head(T, dk, dv, h, q + bh * dk, k + bh * dk, v + bh * dv, a,
+                             beta[bh], val_perm, val_scale, out ? out + bh * dv : NULL);
+            orc_damp_pack_head(T, key_perm, h, K_hi, group, dk, dv, hi + sh * K_hi * dv,
+                               lo + sh * nlo * dv, scale + sh * nlo * ng);
         }
     }
     free(a);
-    free(S);
+    free(T);
 }
 
 /* ------------------------------------------------------------------------ */
