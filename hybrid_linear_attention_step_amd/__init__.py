@@ -26,10 +26,10 @@ SIGNATURES = {
     "hla_version": ([], _I),
     "gdn_step": ([_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _I, _P, _P], _I),
     "kda_step": ([_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _I, _P, _P], _I),
-    "damp_step": ([_P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P,
-                   _I, _P, _P], _I),
-    "damp_quantize": ([_P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P], _I),
-    "damp_dequantize": ([_P, _P, _P, _I, _I, _I, _I, _P, _I, _P, _P], _I),
+    "damp_step": ([_P, _P, _P, _I, _P, _I, _I, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _P,
+                   _I, _P, _P, _I, _P, _P], _I),
+    "damp_quantize": ([_P, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P], _I),
+    "damp_dequantize": ([_P, _P, _P, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P], _I),
     "dasc_plan": ([_P, _I, _I, _P, _P, _I, _P, _P], _I),
     "dasc_pack": ([_P, _L, _I, _I, _I, _L, _P, _P, _I, _P, _P, _I, _P, _I, _P, _P], _I),
     "dasc_restore": ([_P, _I, _I, _P, _I, _I, _L, _P, _P, _I, _P, _L, _I, _P, _P], _I),
@@ -188,14 +188,35 @@ def replay_accepted(state, q, k, v, alpha, beta, n_accept, decay_kind, out=None,
     return out
 
 
+def _damp_group(lo_scale, dv):
+    """Scale granularity from the scale tensor's shape: [S,H,rows] per row,
+    [S,H,rows,dv/group] per group."""
+    if lo_scale.dim() == 3:
+        return dv
+    if lo_scale.dim() == 4 and lo_scale.shape[3] > 0 and dv % lo_scale.shape[3] == 0:
+        return dv // lo_scale.shape[3]
+    raise ValueError(f"lo_scale shape {tuple(lo_scale.shape)} fits no scale group of dv={dv}")
+
+
+def _sr_tables(val_perm, val_scale):
+    if val_perm is not None:
+        _dev(val_perm, "val_perm", _i32(), 2)
+    if val_scale is not None:
+        _dev(val_scale, "val_scale", _f32(), 2)
+
+
 def damp_step(hi, lo, lo_scale, key_perm, K_hi, q, k, v, alpha, decay_kind, beta, out=None,
-              slot=None, err_flag=None, stream=None, want_out=True):
-    """One fused dequantise -> update -> requantise step on the packed state (in place)."""
+              slot=None, err_flag=None, stream=None, want_out=True, val_perm=None,
+              val_scale=None):
+    """One fused dequantise -> update -> requantise step on the packed state (in place).
+    The scale group (per row or per 32 values) is read off lo_scale's shape; val_perm /
+    val_scale [H, dv] select the value transform (None: untransformed)."""
     torch = _torch()
     _dev(hi, "hi", (torch.int16, torch.uint16, torch.float16), 4)
     _dev(lo, "lo", (torch.int8,), 4)
-    _dev(lo_scale, "lo_scale", _f32(), 3)
+    _dev(lo_scale, "lo_scale", _f32())
     S, H, _, dv = hi.shape
+    group = _damp_group(lo_scale, dv)
     _dev(q, "q", _in_dtypes(), 3)
     B, _, dk = q.shape
     _dev(k, "k", (q.dtype,), 3)
@@ -204,6 +225,7 @@ def damp_step(hi, lo, lo_scale, key_perm, K_hi, q, k, v, alpha, decay_kind, beta
     _dev(beta, "beta", _f32(), 2)
     if key_perm is not None:
         _dev(key_perm, "key_perm", _i32(), 2)
+    _sr_tables(val_perm, val_scale)
     if slot is not None:
         _dev(slot, "slot", _i32(), 1)
     if err_flag is not None:
@@ -211,42 +233,53 @@ def damp_step(hi, lo, lo_scale, key_perm, K_hi, q, k, v, alpha, decay_kind, beta
     if lo.shape[2] != dk - K_hi or hi.shape[2] != K_hi:
         raise ValueError("hi/lo row counts do not match K_hi and dk")
     out = _opt_out(out, (B, H, dv), hi.device, want_out)
-    _call("damp_step", _ptr(hi), _ptr(lo), _ptr(lo_scale), S, _ptr(key_perm), K_hi, _ptr(slot),
-          B, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _code(q.dtype), _ptr(alpha), int(decay_kind),
-          _ptr(beta), _ptr(out), _code(out.dtype) if out is not None else HLA_F32,
-          _ptr(err_flag), _stream(stream))
+    _call("damp_step", _ptr(hi), _ptr(lo), _ptr(lo_scale), S, _ptr(key_perm), K_hi, group,
+          _ptr(val_perm), _ptr(val_scale), _ptr(slot), B, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
+          _code(q.dtype), _ptr(alpha), int(decay_kind), _ptr(beta), _ptr(out),
+          _code(out.dtype) if out is not None else HLA_F32, _ptr(err_flag), _stream(stream))
     return out
 
 
-def damp_alloc(S, H, dk, dv, K_hi, device="cuda"):
+def damp_alloc(S, H, dk, dv, K_hi, device="cuda", group=None):
+    """Empty packed state; group None or dv: one scale per INT8 row, else per `group`."""
     torch = _torch()
+    g = dv if group is None else int(group)
+    sc_shape = (S, H, dk - K_hi) if g == dv else (S, H, dk - K_hi, dv // g)
     return (torch.empty((S, H, K_hi, dv), dtype=torch.int16, device=device),
             torch.empty((S, H, dk - K_hi, dv), dtype=torch.int8, device=device),
-            torch.empty((S, H, dk - K_hi), dtype=torch.float32, device=device))
+            torch.empty(sc_shape, dtype=torch.float32, device=device))
 
 
-def damp_quantize(state, key_perm, K_hi, hi=None, lo=None, lo_scale=None, stream=None):
+def damp_quantize(state, key_perm, K_hi, hi=None, lo=None, lo_scale=None, stream=None,
+                  group=None, val_perm=None, val_scale=None):
     _dev(state, "state", _f32(), 4)
     S, H, dk, dv = state.shape
     if hi is None:
-        hi, lo, lo_scale = damp_alloc(S, H, dk, dv, K_hi, state.device)
+        hi, lo, lo_scale = damp_alloc(S, H, dk, dv, K_hi, state.device, group)
+    g = _damp_group(lo_scale, dv)
+    if group is not None and int(group) != g:
+        raise ValueError("lo_scale shape does not match group")
     if key_perm is not None:
         _dev(key_perm, "key_perm", _i32(), 2)
-    _call("damp_quantize", _ptr(state), S, H, dk, dv, _ptr(key_perm), K_hi, _ptr(hi), _ptr(lo),
-          _ptr(lo_scale), _stream(stream))
+    _sr_tables(val_perm, val_scale)
+    _call("damp_quantize", _ptr(state), S, H, dk, dv, _ptr(key_perm), K_hi, g, _ptr(val_perm),
+          _ptr(val_scale), _ptr(hi), _ptr(lo), _ptr(lo_scale), _stream(stream))
     return hi, lo, lo_scale
 
 
-def damp_dequantize(hi, lo, lo_scale, key_perm, K_hi, dk, out=None, stream=None):
+def damp_dequantize(hi, lo, lo_scale, key_perm, K_hi, dk, out=None, stream=None,
+                    val_perm=None, val_scale=None):
     torch = _torch()
     S, H, _, dv = hi.shape
+    g = _damp_group(lo_scale, dv)
     if out is None:
         out = torch.empty((S, H, dk, dv), dtype=torch.float32, device=hi.device)
     _dev(out, "state", _f32(), 4)
     if key_perm is not None:
         _dev(key_perm, "key_perm", _i32(), 2)
+    _sr_tables(val_perm, val_scale)
     _call("damp_dequantize", _ptr(hi), _ptr(lo), _ptr(lo_scale), S, H, dk, dv, _ptr(key_perm),
-          K_hi, _ptr(out), _stream(stream))
+          K_hi, g, _ptr(val_perm), _ptr(val_scale), _ptr(out), _stream(stream))
     return out
 
 

@@ -15,8 +15,8 @@ LIB = os.path.join(PKG, "libhla.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["hla_host.cpp", "hla_step.hip", "hla_damp.hip", "hla_dasc.hip"]
-HEADERS = ["hla_device.h", "hla_internal.h"]
+SOURCES = ["hla_host.cpp", "hla_step.hip", "hla_damp.hip", "hla_damp_sr.hip", "hla_dasc.hip"]
+HEADERS = ["hla_device.h", "hla_internal.h", "hla_damp_kernels.h"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
@@ -44,7 +44,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = True) -> str:
     """Compile every source for gfx950 and link libhla.so.  Always rebuilds."""
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(5, os.cpu_count() or 1)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]

@@ -1,499 +1,70 @@
-// gfx950 kernels for the mixed-precision recurrent state ("DAMP: Decay-Aware
-// Mixed-Precision Recurrent-State Quantization", §3.2-§3.3 and §5.2 / App. A.4):
-// K_hi key-channel rows per head in FP16, the rest symmetric INT8 with one
-// FP32 scale per row, updated by one fused dequantise -> FP32 update and
-// readout -> requantise pass.
-//
-// Work decomposition.  The requantisation needs the maximum of each row over
-// all dv columns and the update needs column sums over all dk rows, so one
-// workgroup owns a whole head: (dk/8) x (dv/8) threads, each holding 8 rows x
-// 8 adjacent columns.  A row's dv values are spread over dv/8 consecutive lanes
-// (one DPP row for dv = 128), so the row maximum is a 4-step DPP max.  Column
-// sums run in-lane over 8 rows, then over the row groups of the wave (permlane
-// swaps), then over the waves through a 4 KiB LDS table.  Each INT8 load/store
-// instruction covers whole 128-byte rows.
-//
-// Codec arithmetic (FP32 throughout, as the pages state for the quantiser):
-//   dequantise + decay: signed byte -> float (exact) times fl(a * s);
-//   scale s = fl(max(amax, 1e-8) / 127), bit-identical to the IEEE division
-//     (reciprocal multiply + one FMA correction, see div127);
-//   inv = v_rcp_f32(s), within an ulp of 1/s;
-//   code = round-half-even of the exact product x * inv, formed as the low
-//     byte of fma(x, inv, 1.5 * 2^23): the FMA adds 1.5 * 2^23 before its
-//     single rounding, where the FP32 ulp is 1, so the rounding is exactly
-//     rne(x * inv), and the low 8 mantissa bits are the two's-complement code.
-//     |x * inv| <= amax * inv < 127.5 because s >= amax/127 * (1 - 2^-24) and
-//     inv <= (1/s)(1 + 2^-22), so no clamp is needed for finite states.
-//   This differs from rne(fl(x / s)) only when x / s lies within about 2e-5
-//   of a half-integer.
-#include <hip/hip_runtime.h>
-
-#include "hla.h"
-#include "hla_device.h"
-#include "hla_internal.h"
+// Entry points of the mixed-precision state ("DAMP: Decay-Aware Mixed-Precision
+// Recurrent-State Quantization", §3.3 Eq. (7), §5.2 and App. A.1-A.4), the
+// codec launches and the step variants with one scale per INT8 row and no
+// value transform.  The device code is in hla_damp_kernels.h.
+#include "hla_damp_kernels.h"
 
 namespace hla {
 
-constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
+namespace {
 
-
-template <int CG>
-struct Log2;
-template <>
-struct Log2<8> { static constexpr int v = 3; };
-template <>
-struct Log2<16> { static constexpr int v = 4; };
-
-// Correctly rounded fl(a / 127) for normal a: one multiply by fl(1/127) and one
-// FMA correction of the residual.  Checked exhaustively against the IEEE
-// division over all 2^23 FP32 significands (the result only depends on the
-// significand for normal inputs).
-__device__ __forceinline__ float div127(float a)
-{
-    constexpr float y = 1.0f / 127.0f;
-    const float q0 = a * y;
-    const float r = fmaf(-q0, 127.0f, a);
-    return fmaf(r, y, q0);
-}
-
-// Dequantise one packed 8-value row segment, scaled by `a` (decay, or 1).
-__device__ __forceinline__ void decode_fp16(const uint32_t (&w)[4], float a, float (&x)[8])
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        x[2 * i] = half_bits_to_f32(w[i] & 0xffffu) * a;
-        x[2 * i + 1] = half_bits_to_f32(w[i] >> 16) * a;
-    }
-}
-
-// code * (a * s) for the 8 signed bytes of w0 (values 0..3) and w1 (4..7).
-__device__ __forceinline__ void decode_int8(uint32_t w0, uint32_t w1, float as, float (&x)[8])
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        x[i] = (float)(int)(int8_t)(w0 >> (8 * i)) * as;
-        x[4 + i] = (float)(int)(int8_t)(w1 >> (8 * i)) * as;
-    }
-}
-
-__device__ __forceinline__ void encode_fp16(const float (&x)[8], uint32_t (&w)[4])
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        w[i] = f32_to_half_bits(x[2 * i]) | (f32_to_half_bits(x[2 * i + 1]) << 16);
-}
-
-// Quantise the lane's 8 values of a row whose full-row maximum is amax.
-// Returns the FP32 scale s = fl(max(amax, 1e-8) / 127); the codes land in w0
-// (values 0..3) and w1 (4..7).  inv is v_rcp_f32's reciprocal of s (within an
-// ulp): amax * inv stays below 127.5, so every code lies in [-127, 127].
-__device__ __forceinline__ float encode_int8(const float (&x)[8], float amax, uint32_t &w0,
-                                             uint32_t &w1)
-{
-    const float s = div127(fmaxf(amax, 1e-8f));
-    const float inv = __builtin_amdgcn_rcpf(s);
-    uint32_t c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = __float_as_uint(fmaf(x[i], inv, kRoundMagic));
-    // gather the low bytes: perm(hi, lo, sel) picks bytes of {hi:lo}
-    const uint32_t a01 = __builtin_amdgcn_perm(c[1], c[0], 0x0c0c0400u);
-    const uint32_t a23 = __builtin_amdgcn_perm(c[3], c[2], 0x0c0c0400u);
-    const uint32_t a45 = __builtin_amdgcn_perm(c[5], c[4], 0x0c0c0400u);
-    const uint32_t a67 = __builtin_amdgcn_perm(c[7], c[6], 0x0c0c0400u);
-    w0 = __builtin_amdgcn_perm(a23, a01, 0x05040100u);
-    w1 = __builtin_amdgcn_perm(a67, a45, 0x05040100u);
-    return s;
-}
-
-#ifndef HLA_ASM_ABSMAX
-#define HLA_ASM_ABSMAX 1
-#endif
-
-// max |x_i| of 8 finite floats.  v_max3_f32 takes |.| source modifiers, so the
-// whole row segment is 3 max3 + 1 max (the compiler's maxnum lowering would
-// first canonicalise every |x_i| in IEEE mode).  max is exact and the inputs
-// are finite FMA results, so the result equals the plain definition.
-__device__ __forceinline__ float row_absmax8(const float (&x)[8])
-{
-#if HLA_ASM_ABSMAX
-    float m;
-    asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(m) : "v"(x[0]), "v"(x[1]), "v"(x[2]));
-    asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(m) : "v"(m), "v"(x[3]), "v"(x[4]));
-    asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(m) : "v"(m), "v"(x[5]), "v"(x[6]));
-    asm("v_max_f32 %0, %1, |%2|" : "=v"(m) : "v"(m), "v"(x[7]));
-    return m;
-#else
-    float hi = fmaxf(x[0], fmaxf(x[1], x[2]));
-    float lo = fminf(x[0], fminf(x[1], x[2]));
-    hi = fmaxf(hi, fmaxf(x[3], x[4]));
-    lo = fminf(lo, fminf(x[3], x[4]));
-    hi = fmaxf(hi, fmaxf(x[5], x[6]));
-    lo = fminf(lo, fminf(x[5], x[6]));
-    hi = fmaxf(hi, x[7]);
-    lo = fminf(lo, x[7]);
-    return fmaxf(hi, -lo);
-#endif
-}
-
-// Sum the lane's column partials (8 columns of S'^T k and of S'^T q) and q.k
-// over the row groups of this wave and write the wave's totals to LDS rows
-// red_r / red_p (dv floats each) and red_qk.  LCG = log2 of lanes per row
-// group: 4 (dv = 128, row groups on lane bits 4-5) or 3 (dv = 64, lane bits
-// 3-5; bit 3 is folded first with a DPP butterfly).
-template <int LCG>
-__device__ __forceinline__ void wave_column_sums(float (&pr)[8], float (&pp)[8], float qk,
-                                                 int lane, int col0, float *red_r,
-                                                 float *red_p, float *red_qk)
-{
-    if constexpr (LCG == 3) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            pr[c] = sum_xor8(pr[c]);
-            pp[c] = sum_xor8(pp[c]);
-        }
-    }
-    float r2[2], p2[2];
-    reduce_scatter_rows4(pr, r2);
-    reduce_scatter_rows4(pp, p2);
-    qk = sum_lane_bits<LCG>(qk);
-    // with dv = 64 the lanes with bit 3 set hold duplicates of their partner's sums
-    if (LCG == 4 || ((lane >> 3) & 1) == 0) {
-        const int c = col0 + reduce_scatter_rows4_col(lane);
-        red_r[c] = r2[0];
-        red_r[c + 1] = r2[1];
-        red_p[c] = p2[0];
-        red_p[c + 1] = p2[1];
-    }
-    if (lane == 0) *red_qk = qk;
-}
-
-// ------------------------------------------------------------------ step
-//
-// Thread t of the (dk/8) x (dv/8) block: cg = t % (dv/8) picks 8 adjacent
-// columns, g = t / (dv/8) a row group, and the thread owns packed rows
-// g + (dk/8) m, m = 0..7.  Interleaving the rows this way gives every wave
-// the same row index pattern per m, so the FP16 / INT8 choice is uniform
-// across the block whenever K_hi is a multiple of dk/8 (K_hi = 16 at dk = 128).
-// Each wave stages its own copy of k, q, the decay and the plan row into LDS
-// with plain contiguous loads issued together with the state loads (the
-// permutation is applied on the LDS read, so there is no dependent global
-// gather), and no block barrier is needed before the math.  Two block
-// barriers exchange the per-wave column sums and share u.
-
-// MH >= 0: K_hi == MH * (dk/8), so the thread's rows m < MH are the FP16 ones
-// and the choice is known at compile time (no branches, no registers held for
-// the other format); MH < 0: any K_hi, decided per row at run time.
-template <int DK, int DV, typename TIn, typename TOut, bool VEC, int MH>
-__global__ void __launch_bounds__((DK / 8) * (DV / 8))
-k_damp_step(uint16_t *__restrict__ hi, int8_t *__restrict__ lo, float *__restrict__ lo_scale,
-            int n_slots, const int32_t *__restrict__ key_perm, int K_hi,
-            const int32_t *__restrict__ slot, int H, const TIn *__restrict__ q,
-            const TIn *__restrict__ k, const TIn *__restrict__ v,
-            const float *__restrict__ alpha, const float *__restrict__ beta,
-            TOut *__restrict__ out, int32_t *__restrict__ err)
-{
-    constexpr int CG = DV / 8;              // lanes per row group
-    constexpr int LCG = Log2<CG>::v;
-    constexpr int NRG = DK / 8;             // row groups = row stride between a thread's rows
-    constexpr int NW = NRG * CG / 64;       // waves per head
-    __shared__ f32x4 kqa[NW][DK];  // {k, q, decay, 0} per original key channel
-    __shared__ int pm_[NW][DK];
-    __shared__ float red_r[NW][DV], red_p[NW][DV], red_qk[NW];
-    __shared__ float us[DV];
-
-    const int bh = blockIdx.x;
-    const int b = bh / H, h = bh - b * H;
-    const int s = slot ? slot[b] : b;
-    if (s < 0) return;
-    if (s >= n_slots) {
-        if (err && threadIdx.x == 0) atomicOr(err, HLA_DEVERR_SLOT);
-        return;
-    }
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int cg = t & (CG - 1), g = t >> LCG;
-    const int col0 = cg * 8;
-    if constexpr (MH >= 0) K_hi = MH * NRG;
-    const int nlo = DK - K_hi;
-    const size_t sh = (size_t)s * H + h;
-    uint16_t *hrow = hi + (sh * K_hi) * DV + col0;
-    int8_t *lrow = lo + (sh * nlo) * DV + col0;
-    float *srow = lo_scale + sh * nlo;
-    auto is_hi = [&](int m, int r) { return MH >= 0 ? (m < MH) : (r < K_hi); };
-
-    // 1. this wave's copy of k, q, the decay and the plan row, read contiguously
-    //    (no dependent gather; the permutation is applied when reading LDS).  These
-    //    loads are issued first so that their latency hides under the state loads'.
-    constexpr int SJ = DK / 64;  // staged channels per lane
-    int st_p[SJ];
-    float st_k[SJ], st_q[SJ], st_a[SJ];
-#pragma unroll
-    for (int j = 0; j < SJ; ++j) {
-        const int i = lane + 64 * j;
-        st_p[j] = key_perm ? key_perm[h * DK + i] : i;
-        st_k[j] = load_one(k + (size_t)bh * DK + i);
-        st_q[j] = load_one(q + (size_t)bh * DK + i);
-        st_a[j] = VEC ? alpha[(size_t)bh * DK + i] : 0.0f;
-    }
-    // 2. packed rows of this thread, straight from HBM, plus the per-head inputs
-    uint32_t raw[8][4];
-    float sc[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int r = g + NRG * m;
-        if (is_hi(m, r)) {
-            u32x4 w = ld_nt(reinterpret_cast<const u32x4 *>(hrow + (size_t)r * DV));
-            raw[m][0] = w.x; raw[m][1] = w.y; raw[m][2] = w.z; raw[m][3] = w.w;
-            sc[m] = 1.0f;
-        } else {
-            u32x2 w = ld_nt(reinterpret_cast<const u32x2 *>(lrow + (size_t)(r - K_hi) * DV));
-            raw[m][0] = w.x; raw[m][1] = w.y; raw[m][2] = 0u; raw[m][3] = 0u;
-            sc[m] = srow[r - K_hi];
-        }
-    }
-    // every thread loads (threads >= dv re-read a valid element and ignore it): a
-    // conditional load would end in a wait for all outstanding loads
-    const float vt = load_one(v + (size_t)bh * DV + (t & (DV - 1)));
-    const float a_head = VEC ? 0.0f : alpha[bh];
-    const float bt = beta[bh];
-#pragma unroll
-    for (int j = 0; j < SJ; ++j) {
-        pm_[wave][lane + 64 * j] = st_p[j];
-        kqa[wave][lane + 64 * j] = f32x4{st_k[j], st_q[j], st_a[j], 0.0f};
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float kk[8], qq[8], aa[8];  // k, q and decay of each of the thread's packed rows
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        int u = pm_[wave][g + NRG * m];
-        if ((unsigned)u >= (unsigned)DK) {
-            if (err) atomicOr(err, HLA_DEVERR_PLAN);
-            u = g + NRG * m;
-        }
-        const f32x4 e = kqa[wave][u];
-        kk[m] = e.x;
-        qq[m] = e.y;
-        aa[m] = VEC ? e.z : a_head;
-    }
-
-    // 3. dequantise with the decay folded in; partial column sums
-    float x[8][8];
-    float pr[8], pp[8], qk = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) pr[c] = pp[c] = 0.0f;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int r = g + NRG * m;
-        const float a = aa[m];
-        if (is_hi(m, r))
-            decode_fp16(raw[m], a, x[m]);
+// Per-row scales, no value transform: compile-time FP16 row counts for
+// K_hi = 0, dk/8 and dk/4 (K_hi = 16 and 32 at dk = 128); every other K_hi
+// takes the run-time variant.
+struct RowScale {
+    template <int DK, int DV, typename TIn, typename TOut, bool VEC>
+    static void run(const DampArgs &a, int32_t *err, hipStream_t st)
+    {
+        constexpr int NRG = DK / 8, LG = Log2<DV / 8>::v;
+        if (a.K_hi == 0)
+            launch_damp<DK, DV, TIn, TOut, VEC, 0, LG, false>(a, err, st);
+        else if (a.K_hi == NRG)
+            launch_damp<DK, DV, TIn, TOut, VEC, 1, LG, false>(a, err, st);
+        else if (a.K_hi == 2 * NRG)
+            launch_damp<DK, DV, TIn, TOut, VEC, 2, LG, false>(a, err, st);
         else
-            decode_int8(raw[m][0], raw[m][1], a * sc[m], x[m]);
-        const float qr = qq[m];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            pr[c] = fmaf(kk[m], x[m][c], pr[c]);
-            pp[c] = fmaf(qr, x[m][c], pp[c]);
-        }
-        qk = fmaf(qr, kk[m], qk);
+            launch_damp<DK, DV, TIn, TOut, VEC, -1, LG, false>(a, err, st);
     }
-    // 4. column sums: row groups inside the wave, then the waves through LDS;
-    //    thread j < dv finishes column j and shares u_j
-    wave_column_sums<LCG>(pr, pp, qk, lane, col0, red_r[wave], red_p[wave], &red_qk[wave]);
-    __syncthreads();
-    if (t < DV) {
-        float R = red_r[0][t], P = red_p[0][t], QK = red_qk[0];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) {
-            R += red_r[w][t];
-            P += red_p[w][t];
-            QK += red_qk[w];
-        }
-        const float u = bt * (vt - R);   // u = beta (v - S'^T k)
-        us[t] = u;
-        if (out) store_one(out + (size_t)bh * DV + t, fmaf(QK, u, P));  // o = S^T q
-    }
-    __syncthreads();
-    float u8[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) u8[c] = us[col0 + c];
+};
 
-    // 5. rank-1 write, requantise, store
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int r = g + NRG * m;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) x[m][c] = fmaf(kk[m], u8[c], x[m][c]);
-        if (is_hi(m, r)) {
-            uint32_t w[4];
-            encode_fp16(x[m], w);
-            u32x4 t4 = {w[0], w[1], w[2], w[3]};
-            st_nt(reinterpret_cast<u32x4 *>(hrow + (size_t)r * DV), t4);
-        } else {
-            const float amax = max_low_lane_bits<LCG>(row_absmax8(x[m]));
-            uint32_t w0, w1;
-            const float scale = encode_int8(x[m], amax, w0, w1);
-            u32x2 t2 = {w0, w1};
-            st_nt(reinterpret_cast<u32x2 *>(lrow + (size_t)(r - K_hi) * DV), t2);
-            if (cg == 0) srow[r - K_hi] = scale;
-        }
-    }
-}
-
-// ------------------------------------------------------------------ codec
-
-template <int DK, int DV>
-__global__ void __launch_bounds__((DK / 8) * (DV / 8))
-k_damp_quantize(const float *__restrict__ state, int H, const int32_t *__restrict__ key_perm,
-                int K_hi, uint16_t *__restrict__ hi, int8_t *__restrict__ lo,
-                float *__restrict__ lo_scale)
+template <int DK, int DV, int LG>
+void launch_codec(bool quantize, const CodecArgs &c, hipStream_t st)
 {
-    constexpr int CG = DV / 8;
-    constexpr int LCG = Log2<CG>::v;
-    const size_t sh = blockIdx.x;
-    const int h = (int)(sh % H);
-    const int t = threadIdx.x, cg = t & (CG - 1), rg = t >> LCG;
-    const int nlo = DK - K_hi;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int r = rg * 8 + m;
-        int u = key_perm ? key_perm[h * DK + r] : r;
-        if ((unsigned)u >= (unsigned)DK) u = r;  // host-built plans are permutations
-        const float *src = state + (sh * DK + u) * DV + cg * 8;
-        f32x4 a = reinterpret_cast<const f32x4 *>(src)[0];
-        f32x4 c = reinterpret_cast<const f32x4 *>(src)[1];
-        float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-        if (r < K_hi) {
-            uint32_t w[4];
-            encode_fp16(x, w);
-            u32x4 t4 = {w[0], w[1], w[2], w[3]};
-            *reinterpret_cast<u32x4 *>(hi + (sh * K_hi + r) * DV + cg * 8) = t4;
-        } else {
-            const float amax = max_low_lane_bits<LCG>(row_absmax8(x));
-            uint32_t w0, w1;
-            const float scale = encode_int8(x, amax, w0, w1);
-            u32x2 t2 = {w0, w1};
-            *reinterpret_cast<u32x2 *>(lo + (sh * nlo + (r - K_hi)) * DV + cg * 8) = t2;
-            if (cg == 0) lo_scale[sh * nlo + (r - K_hi)] = scale;
-        }
-    }
-}
-
-template <int DK, int DV>
-__global__ void __launch_bounds__((DK / 8) * (DV / 8))
-k_damp_dequantize(const uint16_t *__restrict__ hi, const int8_t *__restrict__ lo,
-                  const float *__restrict__ lo_scale, int H, const int32_t *__restrict__ key_perm,
-                  int K_hi, float *__restrict__ state)
-{
-    constexpr int CG = DV / 8;
-    constexpr int LCG = Log2<CG>::v;
-    const size_t sh = blockIdx.x;
-    const int h = (int)(sh % H);
-    const int t = threadIdx.x, cg = t & (CG - 1), rg = t >> LCG;
-    const int nlo = DK - K_hi;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int r = rg * 8 + m;
-        int u = key_perm ? key_perm[h * DK + r] : r;
-        if ((unsigned)u >= (unsigned)DK) u = r;
-        float x[8];
-        if (r < K_hi) {
-            u32x4 w = *reinterpret_cast<const u32x4 *>(hi + (sh * K_hi + r) * DV + cg * 8);
-            uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-            decode_fp16(ww, 1.0f, x);
-        } else {
-            u32x2 w = *reinterpret_cast<const u32x2 *>(lo + (sh * nlo + (r - K_hi)) * DV + cg * 8);
-            decode_int8(w.x, w.y, lo_scale[sh * nlo + (r - K_hi)], x);
-        }
-        float *dst = state + (sh * DK + u) * DV + cg * 8;
-        f32x4 a = {x[0], x[1], x[2], x[3]}, c = {x[4], x[5], x[6], x[7]};
-        reinterpret_cast<f32x4 *>(dst)[0] = a;
-        reinterpret_cast<f32x4 *>(dst)[1] = c;
-    }
-}
-
-// ------------------------------------------------------------------ dispatch
-
-template <int DK, int DV, typename TIn, typename TOut, bool VEC, int MH>
-static void launch_damp_mh(const DampArgs &a, int32_t *err, hipStream_t st)
-{
-    const dim3 grid((unsigned)((size_t)a.B * a.H)), block((DK / 8) * (DV / 8));
-    hipLaunchKernelGGL((k_damp_step<DK, DV, TIn, TOut, VEC, MH>), grid, block, 0, st, a.hi, a.lo,
-                       a.lo_scale, a.n_slots, a.key_perm, a.K_hi, a.slot, a.H, (const TIn *)a.q,
-                       (const TIn *)a.k, (const TIn *)a.v, a.alpha, a.beta, (TOut *)a.out, err);
-}
-
-// Compile-time FP16 row counts for K_hi = 0, dk/8 and dk/4 (K_hi = 16 and 32
-// at dk = 128); every other K_hi takes the run-time variant.
-template <int DK, int DV, typename TIn, typename TOut, bool VEC>
-static void launch_damp_khi(const DampArgs &a, int32_t *err, hipStream_t st)
-{
-    constexpr int NRG = DK / 8;
-    if (a.K_hi == 0)
-        launch_damp_mh<DK, DV, TIn, TOut, VEC, 0>(a, err, st);
-    else if (a.K_hi == NRG)
-        launch_damp_mh<DK, DV, TIn, TOut, VEC, 1>(a, err, st);
-    else if (a.K_hi == 2 * NRG)
-        launch_damp_mh<DK, DV, TIn, TOut, VEC, 2>(a, err, st);
-    else
-        launch_damp_mh<DK, DV, TIn, TOut, VEC, -1>(a, err, st);
-}
-
-template <int DK, int DV, typename TIn, typename TOut>
-static int launch_damp_typed(const DampArgs &a, int32_t *err, hipStream_t st)
-{
-    if (a.decay == HLA_DECAY_VECTOR)
-        launch_damp_khi<DK, DV, TIn, TOut, true>(a, err, st);
-    else
-        launch_damp_khi<DK, DV, TIn, TOut, false>(a, err, st);
-    return hipGetLastError() == hipSuccess ? HLA_OK : HLA_ERR_LAUNCH;
-}
-
-template <int DK, int DV>
-static int launch_damp_dtypes(const DampArgs &a, int32_t *err, hipStream_t st)
-{
-    const bool in16 = a.in_dtype == HLA_BF16, out16 = a.out_dtype == HLA_BF16;
-    if (in16)
-        return out16 ? launch_damp_typed<DK, DV, uint16_t, uint16_t>(a, err, st)
-                     : launch_damp_typed<DK, DV, uint16_t, float>(a, err, st);
-    return out16 ? launch_damp_typed<DK, DV, float, uint16_t>(a, err, st)
-                 : launch_damp_typed<DK, DV, float, float>(a, err, st);
-}
-
-template <int DK, int DV>
-static int launch_codec(bool quantize, const float *state_in, float *state_out, int n_slots, int H,
-                        const int32_t *key_perm, int K_hi, uint16_t *hi, int8_t *lo,
-                        float *lo_scale, hipStream_t st)
-{
-    const dim3 grid((unsigned)((size_t)n_slots * H)), block((DK / 8) * (DV / 8));
+    const dim3 grid((unsigned)((size_t)c.n_slots * c.H)), block((DK / 8) * (DV / 8));
     if (quantize)
-        hipLaunchKernelGGL((k_damp_quantize<DK, DV>), grid, block, 0, st, state_in, H, key_perm,
-                           K_hi, hi, lo, lo_scale);
+        hipLaunchKernelGGL((k_damp_quantize<DK, DV, LG>), grid, block, 0, st, c.state_in, c.H,
+                           c.key_perm, c.K_hi, c.val_perm, c.val_scale, c.hi, c.lo, c.lo_scale);
     else
-        hipLaunchKernelGGL((k_damp_dequantize<DK, DV>), grid, block, 0, st, hi, lo, lo_scale, H,
-                           key_perm, K_hi, state_out);
-    return hipGetLastError() == hipSuccess ? HLA_OK : HLA_ERR_LAUNCH;
+        hipLaunchKernelGGL((k_damp_dequantize<DK, DV, LG>), grid, block, 0, st, c.hi, c.lo,
+                           c.lo_scale, c.H, c.key_perm, c.K_hi, c.val_perm, c.val_scale,
+                           c.state_out);
 }
 
-static int run_codec(bool quantize, const float *state_in, float *state_out, int n_slots, int H,
-                     int dk, int dv, const int32_t *key_perm, int K_hi, uint16_t *hi, int8_t *lo,
-                     float *lo_scale, void *stream)
+int run_codec(bool quantize, const CodecArgs &c, void *stream)
 {
-    const void *st_ptr = quantize ? (const void *)state_in : (const void *)state_out;
-    int rc = check_damp_codec(st_ptr, n_slots, H, dk, dv, K_hi, hi, lo, lo_scale);
-    if (rc != HLA_OK || n_slots == 0) return rc;
+    int rc = check_damp_codec(c);
+    if (rc != HLA_OK || c.n_slots == 0) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool row = c.group == c.dv;
 #define HLA_CODEC(DK_, DV_)                                                                   \
-    if (dk == DK_ && dv == DV_)                                                               \
-        return launch_codec<DK_, DV_>(quantize, state_in, state_out, n_slots, H, key_perm, K_hi, \
-                                      hi, lo, lo_scale, st);
+    if (c.dk == DK_ && c.dv == DV_) {                                                         \
+        if (row) launch_codec<DK_, DV_, Log2<DV_ / 8>::v>(quantize, c, st);                    \
+        else launch_codec<DK_, DV_, 2>(quantize, c, st);                                      \
+    }
     HLA_CODEC(128, 128)
     HLA_CODEC(128, 64)
     HLA_CODEC(64, 128)
     HLA_CODEC(64, 64)
 #undef HLA_CODEC
-    return HLA_ERR_UNSUPPORTED;
+    return hipGetLastError() == hipSuccess ? HLA_OK : HLA_ERR_LAUNCH;
+}
+
+} // namespace
+
+int launch_damp_rowscale(const DampArgs &a, int32_t *err, hipStream_t st)
+{
+    damp_dispatch<RowScale>(a, err, st);
+    return hipGetLastError() == hipSuccess ? HLA_OK : HLA_ERR_LAUNCH;
 }
 
 } // namespace hla
@@ -501,35 +72,39 @@ static int run_codec(bool quantize, const float *state_in, float *state_out, int
 extern "C" {
 
 int damp_step(uint16_t *hi, int8_t *lo, float *lo_scale, int n_slots, const int32_t *key_perm,
-              int K_hi, const int32_t *slot, int B, int H, int dk, int dv, const void *q,
-              const void *k, const void *v, int in_dtype, const float *alpha, int decay_kind,
-              const float *beta, void *out, int out_dtype, int32_t *err_flag, void *stream)
+              int K_hi, int group, const int32_t *val_perm, const float *val_scale,
+              const int32_t *slot, int B, int H, int dk, int dv, const void *q, const void *k,
+              const void *v, int in_dtype, const float *alpha, int decay_kind, const float *beta,
+              void *out, int out_dtype, int32_t *err_flag, void *stream)
 {
-    hla::DampArgs a{hi, lo, lo_scale, n_slots, key_perm, K_hi, slot, B, H, dk, dv, q, k, v,
-                    in_dtype, alpha, decay_kind, beta, out, out_dtype};
+    hla::DampArgs a{hi,    lo,        lo_scale, n_slots, key_perm, K_hi,      group,
+                    val_perm, val_scale, slot,  B,       H,        dk,        dv,
+                    q,     k,         v,        in_dtype, alpha,   decay_kind, beta,
+                    out,   out_dtype};
     int rc = hla::check_damp(a);
     if (rc != HLA_OK || B == 0) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (dk == 128 && dv == 128) return hla::launch_damp_dtypes<128, 128>(a, err_flag, st);
-    if (dk == 128 && dv == 64) return hla::launch_damp_dtypes<128, 64>(a, err_flag, st);
-    if (dk == 64 && dv == 128) return hla::launch_damp_dtypes<64, 128>(a, err_flag, st);
-    return hla::launch_damp_dtypes<64, 64>(a, err_flag, st);
+    if (group == dv && !val_perm && !val_scale) return hla::launch_damp_rowscale(a, err_flag, st);
+    return hla::launch_damp_grouped_or_sr(a, err_flag, st);
 }
 
 int damp_quantize(const float *state, int n_slots, int H, int dk, int dv, const int32_t *key_perm,
-                  int K_hi, uint16_t *hi, int8_t *lo, float *lo_scale, void *stream)
+                  int K_hi, int group, const int32_t *val_perm, const float *val_scale,
+                  uint16_t *hi, int8_t *lo, float *lo_scale, void *stream)
 {
-    return hla::run_codec(true, state, nullptr, n_slots, H, dk, dv, key_perm, K_hi, hi, lo,
-                          lo_scale, stream);
+    hla::CodecArgs c{state, nullptr, n_slots, H, dk, dv, key_perm, K_hi, group, val_perm,
+                     val_scale, hi, lo, lo_scale};
+    return hla::run_codec(true, c, stream);
 }
 
 int damp_dequantize(const uint16_t *hi, const int8_t *lo, const float *lo_scale, int n_slots,
-                    int H, int dk, int dv, const int32_t *key_perm, int K_hi, float *state,
-                    void *stream)
+                    int H, int dk, int dv, const int32_t *key_perm, int K_hi, int group,
+                    const int32_t *val_perm, const float *val_scale, float *state, void *stream)
 {
-    return hla::run_codec(false, nullptr, state, n_slots, H, dk, dv, key_perm, K_hi,
-                          const_cast<uint16_t *>(hi), const_cast<int8_t *>(lo),
-                          const_cast<float *>(lo_scale), stream);
+    hla::CodecArgs c{nullptr, state, n_slots, H, dk, dv, key_perm, K_hi, group, val_perm,
+                     val_scale, const_cast<uint16_t *>(hi), const_cast<int8_t *>(lo),
+                     const_cast<float *>(lo_scale)};
+    return hla::run_codec(false, c, stream);
 }
 
 } // extern "C"

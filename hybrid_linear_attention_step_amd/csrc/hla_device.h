@@ -180,19 +180,19 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t x)
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
 }
 
-// Maximum of non-negative finite floats over the low NB lane bits (NB = 3:
-// groups of 8 lanes, 4: groups of 16).  Non-negative IEEE floats order like
+// Maximum of non-negative finite floats over the low NB lane bits (NB = 2:
+// groups of 4 lanes, 3: groups of 8, 4: groups of 16).  Non-negative IEEE floats order like
 // their bit patterns as unsigned integers, so the reduction runs on v_max_u32
 // with the DPP lane exchange fused into it (no NaN canonicalisation).  max is
 // exact, so any pairing pattern gives the same result.
 template <int NB>
 __device__ __forceinline__ float max_low_lane_bits(float x)
 {
-    static_assert(NB == 3 || NB == 4, "row groups of 8 or 16 lanes");
+    static_assert(NB >= 2 && NB <= 4, "groups of 4, 8 or 16 lanes");
     uint32_t u = __float_as_uint(x);
     u = max(u, dpp_u32<DPP_QUAD_XOR1>(u));
     u = max(u, dpp_u32<DPP_QUAD_XOR2>(u));
-    u = max(u, dpp_u32<DPP_ROW_HALF_MIRROR>(u));
+    if constexpr (NB >= 3) u = max(u, dpp_u32<DPP_ROW_HALF_MIRROR>(u));
     if constexpr (NB == 4) u = max(u, dpp_u32<DPP_ROW_MIRROR>(u));
     return __uint_as_float(u);
 }

@@ -52,6 +52,7 @@ int check_damp(const DampArgs &a)
     if (a.decay != HLA_DECAY_SCALAR && a.decay != HLA_DECAY_VECTOR) return HLA_ERR_DTYPE;
     if (a.B == 0) return HLA_OK;
     if (!head_dim_ok(a.dk) || !head_dim_ok(a.dv)) return HLA_ERR_UNSUPPORTED;
+    if (!damp_group_ok(a.group, a.dv)) return HLA_ERR_UNSUPPORTED;
     if (a.K_hi < 0 || a.K_hi > a.dk) return HLA_ERR_SHAPE;
     const int nlo = a.dk - a.K_hi;
     if ((a.K_hi > 0 && !a.hi) || (nlo > 0 && (!a.lo || !a.lo_scale)) || !a.q || !a.k || !a.v ||
@@ -65,10 +66,11 @@ int check_damp(const DampArgs &a)
     const size_t sh = (size_t)a.n_slots * a.H;
     const size_t bh = (size_t)a.B * a.H;
     const size_t es = dtype_bytes(a.in_dtype);
+    const size_t ng = (size_t)(a.dv / a.group);
     Range outs[] = {
         {a.hi, sh * a.K_hi * a.dv * 2},
         {a.lo, sh * nlo * a.dv},
-        {a.lo_scale, sh * nlo * sizeof(float)},
+        {a.lo_scale, sh * nlo * ng * sizeof(float)},
         {a.out, bh * a.dv * dtype_bytes(a.out_dtype)},
     };
     Range ins[] = {
@@ -79,6 +81,8 @@ int check_damp(const DampArgs &a)
         {a.beta, bh * sizeof(float)},
         {a.slot, (size_t)a.B * sizeof(int32_t)},
         {a.key_perm, (size_t)a.H * a.dk * sizeof(int32_t)},
+        {a.val_perm, (size_t)a.H * a.dv * sizeof(int32_t)},
+        {a.val_scale, (size_t)a.H * a.dv * sizeof(float)},
     };
     for (int i = 0; i < 4; ++i) {
         for (const Range &r : ins)
@@ -89,25 +93,40 @@ int check_damp(const DampArgs &a)
     return HLA_OK;
 }
 
-int check_damp_codec(const void *state, int n_slots, int H, int dk, int dv, int K_hi,
-                     const void *hi, const void *lo, const void *lo_scale)
+int check_damp_codec(const CodecArgs &c)
 {
-    if (n_slots < 0 || H <= 0) return HLA_ERR_SHAPE;
-    if (n_slots == 0) return HLA_OK;
-    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return HLA_ERR_UNSUPPORTED;
-    if (K_hi < 0 || K_hi > dk) return HLA_ERR_SHAPE;
-    const int nlo = dk - K_hi;
-    if (!state || (K_hi > 0 && !hi) || (nlo > 0 && (!lo || !lo_scale))) return HLA_ERR_NULL;
-    if ((size_t)n_slots * H > kMaxIndex) return HLA_ERR_SHAPE;
-    if (!aligned16(state) || (hi && !aligned16(hi)) || (lo && !aligned16(lo)))
+    if (c.n_slots < 0 || c.H <= 0) return HLA_ERR_SHAPE;
+    if (c.n_slots == 0) return HLA_OK;
+    if (!head_dim_ok(c.dk) || !head_dim_ok(c.dv)) return HLA_ERR_UNSUPPORTED;
+    if (!damp_group_ok(c.group, c.dv)) return HLA_ERR_UNSUPPORTED;
+    if (c.K_hi < 0 || c.K_hi > c.dk) return HLA_ERR_SHAPE;
+    const int nlo = c.dk - c.K_hi;
+    const void *state = c.state_in ? (const void *)c.state_in : (const void *)c.state_out;
+    if (!state || (c.K_hi > 0 && !c.hi) || (nlo > 0 && (!c.lo || !c.lo_scale)))
+        return HLA_ERR_NULL;
+    if ((size_t)c.n_slots * c.H > kMaxIndex) return HLA_ERR_SHAPE;
+    if (!aligned16(state) || (c.hi && !aligned16(c.hi)) || (c.lo && !aligned16(c.lo)))
         return HLA_ERR_ALIGN;
-    const size_t sh = (size_t)n_slots * H;
-    Range st{state, sh * dk * dv * sizeof(float)};
-    Range packed[] = {{hi, sh * K_hi * dv * 2}, {lo, sh * nlo * dv}, {lo_scale, sh * nlo * 4}};
+    const size_t sh = (size_t)c.n_slots * c.H;
+    const size_t ng = (size_t)(c.dv / c.group);
+    Range st{state, sh * c.dk * c.dv * sizeof(float)};
+    Range packed[] = {{c.hi, sh * c.K_hi * c.dv * 2},
+                      {c.lo, sh * nlo * c.dv},
+                      {c.lo_scale, sh * nlo * ng * 4}};
+    Range tables[] = {{c.key_perm, (size_t)c.H * c.dk * 4},
+                      {c.val_perm, (size_t)c.H * c.dv * 4},
+                      {c.val_scale, (size_t)c.H * c.dv * 4}};
     for (int i = 0; i < 3; ++i) {
         if (overlaps(st, packed[i])) return HLA_ERR_ALIAS;
         for (int j = i + 1; j < 3; ++j)
             if (overlaps(packed[i], packed[j])) return HLA_ERR_ALIAS;
+    }
+    // the codec's output must not overwrite its plan tables
+    for (const Range &t : tables) {
+        if (c.state_out && overlaps(st, t)) return HLA_ERR_ALIAS;
+        if (c.state_in)
+            for (const Range &p : packed)
+                if (overlaps(p, t)) return HLA_ERR_ALIAS;
     }
     return HLA_OK;
 }

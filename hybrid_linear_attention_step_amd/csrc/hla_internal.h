@@ -55,6 +55,9 @@ struct DampArgs {
     int n_slots;
     const int32_t *key_perm;
     int K_hi;
+    int group;                 // INT8 values per FP32 scale: dv (per row) or 32
+    const int32_t *val_perm;   // [H, dv] stored column -> original value index, or NULL
+    const float *val_scale;    // [H, dv] value scale of each stored column, or NULL
     const int32_t *slot;
     int B, H, dk, dv;
     const void *q, *k, *v;
@@ -67,8 +70,26 @@ struct DampArgs {
 };
 
 int check_damp(const DampArgs &a);
-int check_damp_codec(const void *state, int n_slots, int H, int dk, int dv, int K_hi,
-                     const void *hi, const void *lo, const void *lo_scale);
+
+// damp_quantize (state_in set) / damp_dequantize (state_out set).
+struct CodecArgs {
+    const float *state_in;
+    float *state_out;
+    int n_slots, H, dk, dv;
+    const int32_t *key_perm;
+    int K_hi;
+    int group;
+    const int32_t *val_perm;
+    const float *val_scale;
+    uint16_t *hi;
+    int8_t *lo;
+    float *lo_scale;
+};
+
+int check_damp_codec(const CodecArgs &c);
+
+// Scale groups the kernels are built for: one scale per row, or per 32 values.
+inline bool damp_group_ok(int group, int dv) { return group == dv || group == 32; }
 
 int check_dasc(const void *active, int64_t layer_stride_bytes, int S_act, int L, int n_units,
                int64_t unit_bytes, const void *table_a, const void *table_b, int R_total,

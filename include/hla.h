@@ -125,54 +125,75 @@ HLA_API int kda_step(float *state, int n_slots, const int32_t *slot, int B, int 
              int32_t *err_flag, void *stream);
 
 /* -------------------------------------------------------------------------
- * Mixed-precision packed state ([DAMP] §5.2 and App. A.4).  For each slot and
- * head the dk key-channel rows are reordered by a static plan so that packed
- * row r holds key channel key_perm[h*dk + r]; rows r < K_hi are stored in
- * FP16, rows r >= K_hi as symmetric INT8 codes with one FP32 scale per row:
+ * Mixed-precision packed state ([DAMP] §5.2 and App. A.1-A.4).  For each slot
+ * and head the dk key-channel rows are reordered by a static plan so that
+ * packed row r holds key channel key_perm[h*dk + r]; rows r < K_hi are stored
+ * in FP16, rows r >= K_hi as symmetric INT8 codes with one FP32 scale per
+ * `group` consecutive values of the row:
  *     hi        device uint16 (IEEE binary16 bits) [n_slots, H, K_hi, dv]
  *     lo        device int8                        [n_slots, H, dk-K_hi, dv]
- *     lo_scale  device float32                     [n_slots, H, dk-K_hi]
- * The INT8 row quantiser is [DAMP] §3.2 Eq. (5)-(6) with b = 8 as made
- * concrete in [dasc] App. E.1 Eq. (8): a = max_j |x_j|,
- * s = max(a, 1e-8) / 127, c = clip(round(x / s), -127, 127), computed in
- * FP32, s stored in FP32, round = nearest-even.  FP16 rows are rounded to
- * nearest-even.  key_perm is device int32 [H, dk], a permutation of 0..dk-1
- * per head, or NULL for the identity (the pages fold the order into the
- * projection weights, [DAMP] §5.2).  0 <= K_hi <= dk.
+ *     lo_scale  device float32                     [n_slots, H, dk-K_hi, dv/group]
+ * group is dv (one scale per row: [DAMP] §3.2, [dasc] App. E.1 Eq. (8)) or 32
+ * (the deployed layout of [DAMP] App. A.1 / A.4, 9.875 bits per value at
+ * 16 of 128 rows in FP16); other values return HLA_ERR_UNSUPPORTED.
+ * The INT8 quantiser is [DAMP] §3.2 Eq. (5)-(6) with b = 8 as made concrete in
+ * [dasc] App. E.1 Eq. (8), applied to each group on its own: a = max |x| over
+ * the group, s = max(a, 1e-8) / 127, c = clip(round(x / s), -127, 127),
+ * computed in FP32, s stored in FP32, round = nearest-even.  FP16 rows are
+ * rounded to nearest-even.  key_perm is device int32 [H, dk], a permutation of
+ * 0..dk-1 per head, or NULL for the identity (the pages fold the order into
+ * the projection weights, [DAMP] §5.2).  0 <= K_hi <= dk.
+ *
+ * Value scaling and reordering ([DAMP] App. A.3 Eq. (17)-(18)).  The stored
+ * values are those of T = S D^-1 P_V^T: stored column j of every row holds
+ * original value index pi(j) = val_perm[h*dv + j] divided by c'_j =
+ * val_scale[h*dv + j] (c'_j > 0, given in stored order).  val_perm is device
+ * int32 [H, dv], a permutation per head, or NULL when the value order is
+ * already folded into the projection weights (then v is read and o written in
+ * stored order); val_scale is device float32 [H, dv], or NULL for c' = 1.
+ * Both NULL is the untransformed state.
  * ---------------------------------------------------------------------- */
 
 /* damp_step -- one decode step on the packed state, in place ([DAMP] §3.3
  * Eq. (7), S^q_t = Q(A_t S^q_{t-1} + beta k v^T), fused as in App. A.4):
- * reconstruct each row (FP16 value, or code * scale), run the gdn_step /
- * kda_step update and readout in FP32, then requantise every INT8 row with a
- * freshly computed scale and round every FP16 row, and write all three
- * regions back.  The readout o is taken from the FP32 updated state before
- * it is requantised.
+ * reconstruct each row (FP16 value, or code * group scale), run the
+ * gdn_step / kda_step update and readout in FP32 on T (App. A.3 Eq. (18):
+ * v'_j = v_{pi(j)} / c'_j, o_{pi(j)} = c'_j (T^T q)_j), then requantise every
+ * INT8 group with a freshly computed scale and round every FP16 row, and
+ * write all three regions back.  The readout o is taken from the FP32
+ * updated state before it is requantised.
  *
  * q, k, alpha (when decay_kind == HLA_DECAY_VECTOR) are indexed by ORIGINAL
  * key channel, [B, H, dk]; the kernel gathers them through key_perm.
- * alpha is [B, H] for HLA_DECAY_SCALAR.  slot, v, beta, out, err_flag as
- * gdn_step.
- * Errors: as gdn_step, plus SHAPE for K_hi outside [0, dk].
+ * alpha is [B, H] for HLA_DECAY_SCALAR.  v and out are indexed by original
+ * value index when val_perm is given, else by stored column.  slot, beta,
+ * err_flag as gdn_step; a val_perm entry outside [0, dv) sets
+ * HLA_DEVERR_PLAN and is read as the identity.
+ * Errors: as gdn_step, plus SHAPE for K_hi outside [0, dk] and UNSUPPORTED
+ * for another group.
  */
 HLA_API int damp_step(uint16_t *hi, int8_t *lo, float *lo_scale, int n_slots,
-              const int32_t *key_perm, int K_hi, const int32_t *slot, int B, int H,
-              int dk, int dv, const void *q, const void *k, const void *v, int in_dtype,
+              const int32_t *key_perm, int K_hi, int group, const int32_t *val_perm,
+              const float *val_scale, const int32_t *slot, int B, int H, int dk, int dv,
+              const void *q, const void *k, const void *v, int in_dtype,
               const float *alpha, int decay_kind, const float *beta, void *out,
               int out_dtype, int32_t *err_flag, void *stream);
 
-/* damp_quantize -- pack an FP32 state [n_slots, H, dk, dv] (device) into the
- * three regions above with the same quantiser.  The FP32 input is only read.
- */
+/* damp_quantize -- pack an FP32 state S [n_slots, H, dk, dv] (device, original
+ * coordinates) into the three regions above: T = S D^-1 P_V^T (FP32 division),
+ * then the same quantiser.  The FP32 input is only read. */
 HLA_API int damp_quantize(const float *state, int n_slots, int H, int dk, int dv,
-                  const int32_t *key_perm, int K_hi, uint16_t *hi, int8_t *lo,
-                  float *lo_scale, void *stream);
+                  const int32_t *key_perm, int K_hi, int group, const int32_t *val_perm,
+                  const float *val_scale, uint16_t *hi, int8_t *lo, float *lo_scale,
+                  void *stream);
 
-/* damp_dequantize -- reconstruct the FP32 state (original channel order) from
- * the packed regions: FP16 values exactly, INT8 rows as code * scale. */
+/* damp_dequantize -- reconstruct the FP32 state in original coordinates from
+ * the packed regions: FP16 values exactly, INT8 values as code * group scale,
+ * then S[i][pi(j)] = T[i][j] * c'_j. */
 HLA_API int damp_dequantize(const uint16_t *hi, const int8_t *lo, const float *lo_scale,
                     int n_slots, int H, int dk, int dv, const int32_t *key_perm,
-                    int K_hi, float *state, void *stream);
+                    int K_hi, int group, const int32_t *val_perm, const float *val_scale,
+                    float *state, void *stream);
 
 /* -------------------------------------------------------------------------
  * Ragged state checkpoints ([dasc] §4.1, §4.2 and App. B "Ragged (Scheme 2)").

@@ -81,6 +81,8 @@ class Config:
     seed: int = 0
     K_hi: int = 0  # DAMP: rows kept in FP16
     plan_seed: int = 0
+    group: int = 0  # DAMP: INT8 values per FP32 scale (0: one scale per row)
+    sr: bool = False  # DAMP: value scaling and reordering plan
     # dasc + replay
     L: int = 0
     slots: int = 0
@@ -101,6 +103,10 @@ CONFIGS = {
     "damp_kda": Config("damp_kda", B=256, H=32, dk=128, dv=128, steps=100, in_dtype="bf16",
                        decay="vector", state_sigma=0.05, seed=1004, K_hi=16,
                        plan_seed=2004),
+    # the DAMP paper's deployed layout: group-32 scales and value scaling/reordering
+    "damp_kda_g32sr": Config("damp_kda_g32sr", B=256, H=32, dk=128, dv=128, steps=100,
+                             in_dtype="bf16", decay="vector", state_sigma=0.05, seed=1006,
+                             K_hi=16, plan_seed=2006, group=32, sr=True),
     "dasc_gdn": Config("dasc_gdn", B=512, H=32, dk=128, dv=128, steps=1, in_dtype="f32",
                        decay="scalar", alpha_lo=0.90, alpha_hi=0.9999, state_sigma=0.05,
                        seed=1005, plan_seed=2005, L=4, slots=512, retention=0.5, K=8),
@@ -119,6 +125,7 @@ def rng(seed: int, *stream: int) -> np.random.Generator:
 
 
 _STREAM_STEP, _STREAM_STATE, _STREAM_PLAN, _STREAM_MASK, _STREAM_REPLAY = 1, 2, 3, 4, 5
+_STREAM_VPLAN = 6
 
 
 def _l2n(x: np.ndarray) -> np.ndarray:
@@ -195,6 +202,31 @@ def damp_key_perm(cfg: Config, n_cal: int = 256) -> np.ndarray:
         lo = np.setdiff1d(np.arange(dk), hi)
         perm[h] = np.concatenate([hi, lo]).astype(np.int32)
     return perm
+
+
+def damp_value_plan(cfg: Config, sigma: float = 0.5) -> tuple[np.ndarray, np.ndarray]:
+    """Static per-head value scaling and order for the mixed-precision state.
+
+    Per head, value dimension v gets a scale c_v = exp(N(0, sigma)) (seeded); the
+    stored order sorts the dimensions by the RMS they have after scaling, largest
+    first.  The synthetic state has the same RMS in every dimension, so that order is
+    ascending c_v (ties by index).  Returns (val_perm int32 [H, dv]: stored column ->
+    original dimension, val_scale float32 [H, dv]: c of the dimension stored in each
+    column)."""
+    g = rng(cfg.plan_seed, _STREAM_VPLAN)
+    H, dv = cfg.H, cfg.dv
+    perm = np.zeros((H, dv), np.int32)
+    scale = np.zeros((H, dv), np.float32)
+    for h in range(H):
+        c = np.exp(g.normal(0.0, sigma, size=dv)).astype(np.float32)
+        order = np.argsort(c, kind="stable")  # RMS after scaling is proportional to 1 / c
+        perm[h] = order.astype(np.int32)
+        scale[h] = c[order]
+    return perm, scale
+
+
+def damp_group(cfg: Config) -> int:
+    return cfg.dv if cfg.group == 0 else cfg.group
 
 
 # ----------------------------------------------------------------- dasc

@@ -111,9 +111,10 @@ def test_kda_and_replay_validation(L):
 
 def test_damp_validation(L):
     f = Fake()
-    base = dict(hi=f(), lo=f(), sc=f(), n_slots=4, perm=None, K_hi=16, slot=None, B=4, H=2,
-                dk=128, dv=128, q=f(), k=f(), v=f(), in_dtype=1, alpha=f(), decay=1, beta=f(),
-                out=f(), out_dtype=0, err=None, stream=None)
+    base = dict(hi=f(), lo=f(), sc=f(), n_slots=4, perm=None, K_hi=16, group=128,
+                val_perm=None, val_scale=None, slot=None, B=4, H=2, dk=128, dv=128, q=f(),
+                k=f(), v=f(), in_dtype=1, alpha=f(), decay=1, beta=f(), out=f(), out_dtype=0,
+                err=None, stream=None)
 
     def dm(**kw):
         a = dict(base)
@@ -126,10 +127,25 @@ def test_damp_validation(L):
     assert dm(hi=None, K_hi=0, q=ctypes.c_void_p(f().value + 2)) == ALIGN
     assert dm(lo=None) == NULL
     assert dm(dk=32) == UNSUP
+    # scale groups: one per row (group = dv) or per 32 values; nothing else is built
+    assert dm(group=64) == UNSUP and dm(group=0) == UNSUP and dm(group=16) == UNSUP
+    assert dm(group=32, q=ctypes.c_void_p(f().value + 2)) == ALIGN
     hi = f()
     assert dm(hi=hi, lo=hi) == ALIAS
-    assert L.damp_quantize(f(), 2, 2, 128, 128, None, 200, f(), f(), f(), None) == SHAPE
-    assert L.damp_dequantize(f(), f(), f(), 2, 2, 100, 128, None, 16, f(), None) == UNSUP
+    # the value-transform tables are inputs: an output written over one is an alias
+    vs = f()
+    assert dm(val_scale=vs, out=vs) == ALIAS
+    assert dm(val_perm=hi, hi=hi) == ALIAS
+    assert L.damp_quantize(f(), 2, 2, 128, 128, None, 200, 128, None, None, f(), f(), f(),
+                           None) == SHAPE
+    assert L.damp_quantize(f(), 2, 2, 128, 128, None, 16, 48, None, None, f(), f(), f(),
+                           None) == UNSUP
+    assert L.damp_dequantize(f(), f(), f(), 2, 2, 100, 128, None, 16, 128, None, None, f(),
+                             None) == UNSUP
+    # dequantise must not write its state over a plan table
+    st = f()
+    assert L.damp_dequantize(f(), f(), f(), 2, 2, 128, 128, None, 16, 32, st, None, st,
+                             None) == ALIAS
 
 
 def test_dasc_validation(L):

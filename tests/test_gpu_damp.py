@@ -17,66 +17,12 @@ import pytest
 
 import oracle
 import synth
+from damp_util import (CODE_FRAC, STATE_TOL, _assert_bars, _code_stats, _packed_dev,
+                       _packed_host, _perm, _state_bars)
 from gpu_util import (dev, dev_inputs, f64_inputs, gather_heads, host, need_gpu, rel_err_tiles,
                       sample_heads, torch)
 
 pytestmark = pytest.mark.gpu
-STATE_TOL = 1e-3
-CODE_FRAC = 1e-3
-
-
-def _packed_dev(hi, lo, sc):
-    return dev(hi.view(np.int16)), dev(lo), dev(sc)
-
-
-def _packed_host(hi_d, lo_d, sc_d):
-    return (hi_d.cpu().numpy().view(np.uint16).copy(), lo_d.cpu().numpy().copy(),
-            sc_d.cpu().numpy().copy())
-
-
-def _code_stats(lo_g, lo_o):
-    d = np.abs(lo_g.astype(np.int32) - lo_o.astype(np.int32))
-    return (float((d > 0).mean()) if d.size else 0.0), (int(d.max()) if d.size else 0)
-
-
-def _state_bars(g, o, perm, K_hi, dk):
-    """Compare two packed states (hi, lo, scale) and return the worst statistics."""
-    hi_g, lo_g, sc_g = g
-    hi_o, lo_o, sc_o = o
-    frac, dmax = _code_stats(lo_g, lo_o)
-    scale_rel = float((np.abs(sc_g.astype(np.float64) - sc_o) / sc_o).max()) if sc_o.size else 0.0
-    if hi_o.size:
-        a = hi_g.view(np.float16).astype(np.float64)
-        b = hi_o.view(np.float16).astype(np.float64)
-        ulp = np.spacing(np.maximum(np.abs(a), np.abs(b)).astype(np.float16)).astype(np.float64)
-        fp16_ulps = float((np.abs(a - b) / ulp).max())
-    else:
-        fp16_ulps = 0.0
-    if lo_o.size:
-        dq_g = lo_g.astype(np.float64) * sc_g[..., None]
-        dq_o = lo_o.astype(np.float64) * sc_o[..., None]
-        step = np.maximum(sc_g, sc_o)[..., None].astype(np.float64)
-        steps = float((np.abs(dq_g - dq_o) / step).max())
-    else:
-        steps = 0.0
-    s_g = oracle.damp_dequantize(hi_g, lo_g, sc_g, perm, K_hi, dk)
-    s_o = oracle.damp_dequantize(hi_o, lo_o, sc_o, perm, K_hi, dk)
-    d = (s_g - s_o).reshape(s_o.shape[0] * s_o.shape[1], -1)
-    r = s_o.reshape(d.shape)
-    frob = float((np.linalg.norm(d, axis=1) / np.maximum(np.linalg.norm(r, axis=1), 1e-30)).max())
-    return dict(frac=frac, dmax=dmax, scale_rel=scale_rel, fp16_ulps=fp16_ulps,
-                code_steps=steps, state=frob)
-
-
-def _assert_bars(w):
-    assert w["dmax"] <= 1 and w["frac"] <= CODE_FRAC
-    assert w["scale_rel"] <= 1e-5 and w["fp16_ulps"] <= 1.0
-    assert w["code_steps"] <= 1.001
-    assert w["state"] <= STATE_TOL and w["out"] <= STATE_TOL
-
-
-def _perm(rng, H, dk):
-    return np.stack([rng.permutation(dk) for _ in range(H)]).astype(np.int32)
 
 
 @pytest.mark.parametrize("dk,dv,K_hi", [(128, 128, 16), (64, 64, 5), (128, 64, 0), (64, 128, 64)])
@@ -155,8 +101,8 @@ def test_workload_plan_teacher_forced():
 
 
 def test_many_heads_per_block_teacher_forced():
-    """More heads than resident workgroups (1,280 heads with padding requests), so the
-    persistent kernel walks several heads per workgroup through its double-buffered LDS."""
+    """More heads than the GPU holds resident at once (1,280 heads with padding requests):
+    workgroups are scheduled in several waves over the chip."""
     hla = need_gpu()
     cfg = synth.shrink(synth.CONFIGS["damp_kda"], B=40)
     slot = np.arange(cfg.B, dtype=np.int32)

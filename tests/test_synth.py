@@ -75,3 +75,18 @@ def test_replay_inputs():
     d = synth.replay_inputs(cfg, 0, B=64)
     assert d["q"].shape == (64, 8, 32, 128) and d["alpha"].shape == (64, 8, 32)
     assert d["n_accept"].min() >= 0 and d["n_accept"].max() <= 8
+
+
+def test_damp_value_plan():
+    cfg = synth.CONFIGS["damp_kda_g32sr"]
+    perm, scale = synth.damp_value_plan(cfg)
+    assert perm.shape == (cfg.H, cfg.dv) and scale.shape == (cfg.H, cfg.dv)
+    assert perm.dtype == np.int32 and scale.dtype == np.float32
+    for h in range(cfg.H):
+        assert sorted(perm[h].tolist()) == list(range(cfg.dv))
+    assert (scale > 0).all()
+    # stored order: largest RMS after scaling first, i.e. ascending scale
+    assert (np.diff(scale, axis=1) >= 0).all()
+    p2, s2 = synth.damp_value_plan(cfg)
+    assert np.array_equal(perm, p2) and np.array_equal(scale, s2)
+    assert synth.damp_group(cfg) == 32 and synth.damp_group(synth.CONFIGS["damp_kda"]) == 128
