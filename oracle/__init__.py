@@ -53,6 +53,9 @@ def _declare(L):
     L.orc_gdn_step.argtypes = [_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
     L.orc_kda_step.argtypes = L.orc_gdn_step.argtypes
     L.orc_replay.argtypes = [_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P]
+    L.orc_verify.argtypes = [_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P]
+    L.orc_replay_bonus.argtypes = [_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P,
+                                   _P, _P, _P, _P, _P, _P, _P]
     L.orc_half_to_double.argtypes = [ctypes.c_uint16]
     L.orc_half_to_double.restype = ctypes.c_double
     L.orc_double_to_half.argtypes = [ctypes.c_double]
@@ -131,6 +134,41 @@ def replay(state, q, k, v, alpha, beta, n_accept, *, per_channel, slot=None, wan
     lib().orc_replay(_ptr(state), S, _ptr(slot), B, H, dk, dv, K, _ptr(q), _ptr(k), _ptr(v),
                      _ptr(alpha), int(bool(per_channel)), _ptr(beta), _ptr(n_accept), _ptr(out))
     return out
+
+
+def verify(state, q, k, v, alpha, beta, *, per_channel, slot=None):
+    """Readout at every one of the K draft positions from the committed state advanced
+    through the drafts in order; `state` is not changed.  Returns out [B, K, H, dv]
+    (NaN for skipped requests)."""
+    state = np.ascontiguousarray(state, np.float64)
+    S, H, dk, dv = state.shape
+    q, k, v, alpha, beta = map(_f64, (q, k, v, alpha, beta))
+    B, K = q.shape[:2]
+    slot = _i32(slot)
+    out = np.full((B, K, H, dv), np.nan)
+    lib().orc_verify(_ptr(state), S, _ptr(slot), B, H, dk, dv, K, _ptr(q), _ptr(k), _ptr(v),
+                     _ptr(alpha), int(bool(per_channel)), _ptr(beta), _ptr(out))
+    return out
+
+
+def replay_bonus(state, q, k, v, alpha, beta, n_accept, qb, kb, vb, alpha_b, beta_b, *,
+                 per_channel, slot=None, want_out=False):
+    """Replay the first n_accept[b] drafts, then apply the bonus token (inputs [B, H, .])
+    in place.  Returns (out [B, K, H, dv] or None, out_bonus [B, H, dv])."""
+    _need_f64_inplace(state, "state")
+    S, H, dk, dv = state.shape
+    q, k, v, alpha, beta, qb, kb, vb, alpha_b, beta_b = map(
+        _f64, (q, k, v, alpha, beta, qb, kb, vb, alpha_b, beta_b))
+    B, K = q.shape[:2]
+    slot = _i32(slot)
+    n_accept = _i32(n_accept)
+    out = np.full((B, K, H, dv), np.nan) if want_out else None
+    out_b = np.full((B, H, dv), np.nan)
+    lib().orc_replay_bonus(_ptr(state), S, _ptr(slot), B, H, dk, dv, K, _ptr(q), _ptr(k),
+                           _ptr(v), _ptr(alpha), int(bool(per_channel)), _ptr(beta),
+                           _ptr(n_accept), _ptr(out), _ptr(qb), _ptr(kb), _ptr(vb),
+                           _ptr(alpha_b), _ptr(beta_b), _ptr(out_b))
+    return out, out_b
 
 
 # --------------------------------------------------------------------- FP16

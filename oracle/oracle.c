@@ -166,6 +166,71 @@ ORC_API void orc_replay(double *state, int n_slots, const int32_t *slot, int B,
     free(a);
 }
 
+
+/* Verify pass over K draft tokens ([K3], same section): the target model
+   needs the readout at every draft position, computed from the committed
+   state advanced through the drafts in order, while the committed state
+   itself is not changed (a rejected draft must leave no trace).  The state
+   of each (request, head) is copied, advanced through all K tokens with the
+   ordinary step, and the copy is dropped.
+   out [B, K, H, dv] (every t < K is written); layouts as orc_replay. */
+ORC_API void orc_verify(const double *state, int n_slots, const int32_t *slot, int B,
+                        int H, int dk, int dv, int K, const double *q,
+                        const double *k, const double *v, const double *alpha,
+                        int per_channel, const double *beta, double *out)
+{
+    double *a = (double *)malloc(sizeof(double) * dk);
+    double *S = (double *)malloc(sizeof(double) * dk * dv);
+    for (int b = 0; b < B; ++b) {
+        long s = orc_slot(slot, b, n_slots);
+        if (s < 0) continue;
+        for (int h = 0; h < H; ++h) {
+            memcpy(S, state + (s * H + h) * (long)dk * dv, sizeof(double) * dk * dv);
+            for (int t = 0; t < K; ++t) {
+                long bth = ((long)b * K + t) * H + h;
+                for (int i = 0; i < dk; ++i)
+                    a[i] = per_channel ? alpha[bth * dk + i] : alpha[bth];
+                orc_step_head(S, dk, dv, q + bth * dk, k + bth * dk, v + bth * dv, a,
+                              beta[bth], out + bth * dv);
+            }
+        }
+    }
+    free(S);
+    free(a);
+}
+
+/* After verification ([K3], same section): replay the n_b accepted draft
+   projections, then apply the target model's bonus token (its own
+   projections, [B, H, .] like an ordinary step) and read it out.  The
+   bonus token is applied for every live request, also when n_b = 0.
+   out [B, K, H, dv] or NULL for the replayed tokens (rows t >= n_b
+   untouched); out_bonus [B, H, dv] or NULL. */
+ORC_API void orc_replay_bonus(double *state, int n_slots, const int32_t *slot, int B,
+                              int H, int dk, int dv, int K, const double *q,
+                              const double *k, const double *v, const double *alpha,
+                              int per_channel, const double *beta,
+                              const int32_t *n_accept, double *out, const double *qb,
+                              const double *kb, const double *vb, const double *alpha_b,
+                              const double *beta_b, double *out_b)
+{
+    double *a = (double *)malloc(sizeof(double) * dk);
+    orc_replay(state, n_slots, slot, B, H, dk, dv, K, q, k, v, alpha, per_channel, beta,
+               n_accept, out);
+    for (int b = 0; b < B; ++b) {
+        long s = orc_slot(slot, b, n_slots);
+        if (s < 0) continue;
+        for (int h = 0; h < H; ++h) {
+            long bh = (long)b * H + h;
+            for (int i = 0; i < dk; ++i)
+                a[i] = per_channel ? alpha_b[bh * dk + i] : alpha_b[bh];
+            orc_step_head(state + (s * H + h) * (long)dk * dv, dk, dv, qb + bh * dk,
+                          kb + bh * dk, vb + bh * dv, a, beta_b[bh],
+                          out_b ? out_b + bh * dv : NULL);
+        }
+    }
+    free(a);
+}
+
 /* ------------------------------------------------------------------------ */
 /* IEEE-754 binary16, written from the format's definition (1 sign bit,      */
 /* 5 exponent bits with bias 15, 10 fraction bits, subnormals, round to      */
