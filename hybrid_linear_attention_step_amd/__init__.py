@@ -35,6 +35,10 @@ SIGNATURES = {
     "dasc_restore": ([_P, _I, _I, _P, _I, _I, _L, _P, _P, _I, _P, _L, _I, _P, _P], _I),
     "replay_accepted": ([_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, _P, _I,
                          _P, _P], _I),
+    "replay_accepted_bonus": ([_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P,
+                               _P, _P, _P, _P, _P, _P, _P, _I, _P, _P], _I),
+    "verify_drafts": ([_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, _I, _P,
+                       _P], _I),
 }
 
 
@@ -185,6 +189,61 @@ def replay_accepted(state, q, k, v, alpha, beta, n_accept, decay_kind, out=None,
           _ptr(v), _code(q.dtype), _ptr(alpha), int(decay_kind), _ptr(beta), _ptr(n_accept),
           _ptr(out), _code(out.dtype) if out is not None else HLA_F32, _ptr(err_flag),
           _stream(stream))
+    return out
+
+
+def _drafts(state, q, k, v, alpha, beta, slot, err_flag):
+    """Shared checks of the multi-token entry points; returns (S, H, dk, dv, B, K)."""
+    _dev(state, "state", _f32(), 4)
+    S, H, dk, dv = state.shape
+    _dev(q, "q", _in_dtypes(), 4)
+    B, K = q.shape[:2]
+    _dev(k, "k", (q.dtype,), 4)
+    _dev(v, "v", (q.dtype,), 4)
+    _dev(alpha, "alpha", _f32())
+    _dev(beta, "beta", _f32(), 3)
+    if slot is not None:
+        _dev(slot, "slot", _i32(), 1)
+    if err_flag is not None:
+        _dev(err_flag, "err_flag", _i32())
+    return S, H, dk, dv, B, K
+
+
+def replay_accepted_bonus(state, q, k, v, alpha, beta, n_accept, decay_kind, q_bonus, k_bonus,
+                          v_bonus, alpha_bonus, beta_bonus, out=None, out_bonus=None, slot=None,
+                          err_flag=None, stream=None, want_out_bonus=True):
+    """Replay the first n_accept[b] drafts, then the bonus token ([B, H, .] inputs), in one
+    pass over the state.  Returns the bonus token's readout [B, H, dv] (or None)."""
+    S, H, dk, dv, B, K = _drafts(state, q, k, v, alpha, beta, slot, err_flag)
+    _dev(n_accept, "n_accept", _i32(), 1)
+    _dev(q_bonus, "q_bonus", (q.dtype,), 3)
+    _dev(k_bonus, "k_bonus", (q.dtype,), 3)
+    _dev(v_bonus, "v_bonus", (q.dtype,), 3)
+    _dev(alpha_bonus, "alpha_bonus", _f32())
+    _dev(beta_bonus, "beta_bonus", _f32(), 2)
+    if out is not None:
+        _dev(out, "out", _in_dtypes(), 4)
+    out_bonus = _opt_out(out_bonus, (B, H, dv), state.device, want_out_bonus)
+    if out is not None and out_bonus is not None and out.dtype != out_bonus.dtype:
+        raise TypeError("out and out_bonus must have the same dtype")
+    od = out_bonus if out_bonus is not None else out
+    _call("replay_accepted_bonus", _ptr(state), S, _ptr(slot), B, H, dk, dv, K, _ptr(q),
+          _ptr(k), _ptr(v), _code(q.dtype), _ptr(alpha), int(decay_kind), _ptr(beta),
+          _ptr(n_accept), _ptr(out), _ptr(q_bonus), _ptr(k_bonus), _ptr(v_bonus),
+          _ptr(alpha_bonus), _ptr(beta_bonus), _ptr(out_bonus),
+          _code(od.dtype) if od is not None else HLA_F32, _ptr(err_flag), _stream(stream))
+    return out_bonus
+
+
+def verify_drafts(state, q, k, v, alpha, beta, decay_kind, out=None, slot=None, err_flag=None,
+                  stream=None):
+    """Readouts at all K draft positions from the committed state (which is only read).
+    Returns out [B, K, H, dv]."""
+    S, H, dk, dv, B, K = _drafts(state, q, k, v, alpha, beta, slot, err_flag)
+    out = _opt_out(out, (B, K, H, dv), state.device, True)
+    _call("verify_drafts", _ptr(state), S, _ptr(slot), B, H, dk, dv, K, _ptr(q), _ptr(k),
+          _ptr(v), _code(q.dtype), _ptr(alpha), int(decay_kind), _ptr(beta), _ptr(out),
+          _code(out.dtype), _ptr(err_flag), _stream(stream))
     return out
 
 

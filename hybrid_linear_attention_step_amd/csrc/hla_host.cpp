@@ -10,38 +10,56 @@ namespace hla {
 
 static const size_t kMaxIndex = (size_t)INT_MAX;
 
-int check_step(const StepArgs &a, bool replay)
+int check_step(const StepArgs &a)
 {
+    const bool multi = a.mode != MODE_STEP;
+    const bool replay = a.mode == MODE_REPLAY || a.mode == MODE_BONUS;
+    const bool bonus = a.mode == MODE_BONUS;
     if (a.B < 0 || a.H <= 0 || a.n_slots < 0) return HLA_ERR_SHAPE;
-    if (replay && (a.K < 1 || a.K > 16)) return HLA_ERR_SHAPE;
+    if (multi && (a.K < 1 || a.K > 16)) return HLA_ERR_SHAPE;
     if (!dtype_ok(a.in_dtype) || !dtype_ok(a.out_dtype)) return HLA_ERR_DTYPE;
     if (a.decay != HLA_DECAY_SCALAR && a.decay != HLA_DECAY_VECTOR) return HLA_ERR_DTYPE;
     if (a.B == 0) return HLA_OK;
     if (!a.state || !a.q || !a.k || !a.v || !a.alpha || !a.beta) return HLA_ERR_NULL;
     if (replay && !a.n_accept) return HLA_ERR_NULL;
+    if (a.mode == MODE_VERIFY && !a.out) return HLA_ERR_NULL;  // readouts are the result
+    if (bonus && (!a.qb || !a.kb || !a.vb || !a.alpha_b || !a.beta_b)) return HLA_ERR_NULL;
     if (!a.slot && a.n_slots < a.B) return HLA_ERR_SHAPE;
     if (!head_dim_ok(a.dk) || !head_dim_ok(a.dv)) return HLA_ERR_UNSUPPORTED;
     if ((size_t)a.B * a.H > kMaxIndex) return HLA_ERR_SHAPE;
+    const bool vec = a.decay == HLA_DECAY_VECTOR;
     if (!aligned16(a.state) || !aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v) ||
-        (a.out && !aligned16(a.out)) || (a.decay == HLA_DECAY_VECTOR && !aligned16(a.alpha)))
+        (a.out && !aligned16(a.out)) || (vec && !aligned16(a.alpha)))
+        return HLA_ERR_ALIGN;
+    if (bonus && (!aligned16(a.qb) || !aligned16(a.kb) || !aligned16(a.vb) ||
+                  (a.out_b && !aligned16(a.out_b)) || (vec && !aligned16(a.alpha_b))))
         return HLA_ERR_ALIGN;
 
-    const size_t tok = (size_t)a.B * a.K * a.H;  // (request, token, head) triples
-    const size_t es = dtype_bytes(a.in_dtype);
+    const size_t bh = (size_t)a.B * a.H;
+    const size_t tok = bh * a.K;  // (request, token, head) triples
+    const size_t es = dtype_bytes(a.in_dtype), os = dtype_bytes(a.out_dtype);
+    const size_t adk = vec ? a.dk : 1;
     Range state{a.state, (size_t)a.n_slots * a.H * a.dk * a.dv * sizeof(float)};
-    Range out{a.out, tok * a.dv * dtype_bytes(a.out_dtype)};
+    Range out{a.out, tok * a.dv * os};
+    Range out_b{bonus ? a.out_b : nullptr, bh * a.dv * os};
     Range ins[] = {
         {a.q, tok * a.dk * es},
         {a.k, tok * a.dk * es},
         {a.v, tok * a.dv * es},
-        {a.alpha, tok * (a.decay == HLA_DECAY_VECTOR ? a.dk : 1) * sizeof(float)},
+        {a.alpha, tok * adk * sizeof(float)},
         {a.beta, tok * sizeof(float)},
         {a.slot, (size_t)a.B * sizeof(int32_t)},
         {a.n_accept, (size_t)a.B * sizeof(int32_t)},
+        {bonus ? a.qb : nullptr, bh * a.dk * es},
+        {bonus ? a.kb : nullptr, bh * a.dk * es},
+        {bonus ? a.vb : nullptr, bh * a.dv * es},
+        {bonus ? a.alpha_b : nullptr, bh * adk * sizeof(float)},
+        {bonus ? a.beta_b : nullptr, bh * sizeof(float)},
     };
     for (const Range &r : ins)
-        if (overlaps(state, r) || overlaps(out, r)) return HLA_ERR_ALIAS;
-    if (overlaps(state, out)) return HLA_ERR_ALIAS;
+        if (overlaps(state, r) || overlaps(out, r) || overlaps(out_b, r)) return HLA_ERR_ALIAS;
+    if (overlaps(state, out) || overlaps(state, out_b) || overlaps(out, out_b))
+        return HLA_ERR_ALIAS;
     return HLA_OK;
 }
 

@@ -27,26 +27,38 @@ inline bool head_dim_ok(int d) { return d == 64 || d == 128; }
 inline bool dtype_ok(int t) { return t == HLA_F32 || t == HLA_BF16; }
 inline size_t dtype_bytes(int t) { return t == HLA_BF16 ? 2 : 4; }
 
-// Everything the step / replay launchers need, in one place.
+// What a step-kernel launch does with its tokens.
+enum StepMode {
+    MODE_STEP = 0,    // one token, state updated (gdn_step / kda_step)
+    MODE_REPLAY = 1,  // first n_b of K tokens, state updated (replay_accepted)
+    MODE_BONUS = 2,   // first n_b of K tokens, then one bonus token (replay_accepted_bonus)
+    MODE_VERIFY = 3,  // all K tokens with readouts, state not written (verify_drafts)
+};
+
+// Everything the step / replay / verify launchers need, in one place.
 struct StepArgs {
     float *state;
     int n_slots;
     const int32_t *slot;
     int B, H, dk, dv;
-    int K;  // tokens per request: 1 for a step, the draft count for replay
+    int K;  // tokens per request: 1 for a step, the draft count otherwise
     const void *q, *k, *v;
     int in_dtype;
     const float *alpha;
     int decay;
     const float *beta;
-    const int32_t *n_accept;  // replay only
+    const int32_t *n_accept;  // replay modes only
     void *out;
     int out_dtype;
+    int mode;
+    // bonus token [B, H, .] (MODE_BONUS only)
+    const void *qb, *kb, *vb;
+    const float *alpha_b, *beta_b;
+    void *out_b;
 };
 
-// Returns HLA_OK or the first error found.  `replay` selects the replay
-// rules (n_accept required, 1 <= K <= 16).
-int check_step(const StepArgs &a, bool replay);
+// Returns HLA_OK or the first error found.
+int check_step(const StepArgs &a);
 
 struct DampArgs {
     uint16_t *hi;

@@ -1,5 +1,7 @@
 // gfx950 kernels for the FP32 gated delta-rule step (GDN scalar decay, KDA
-// per-key-channel decay) and for the replay of accepted draft tokens.
+// per-key-channel decay) and for several tokens per launch: the replay of
+// accepted draft tokens (optionally followed by the bonus token) and the
+// verify pass over all drafts.
 //
 // Operation ("DAMP: Decay-Aware Mixed-Precision Recurrent-State
 // Quantization", §3.1 Eq. (1)-(2)), per (request, head), state S in dk x dv:
@@ -212,12 +214,24 @@ k_delta_step(float *__restrict__ state, int n_slots, const int32_t *__restrict__
     if (out && rg == 0) store_out4(out + (size_t)bh * DV + col0, o);
 }
 
-template <int DK, int DV, typename TIn, typename TOut, bool VEC>
+// Several tokens per (request, head) with the tile held in registers
+// throughout ("Serving recurrent attention", part "Speculative decoding
+// without state snapshots"):
+//   MODE_REPLAY  the first n_b of K cached draft projections; the state is
+//                read once and written once, and not touched when n_b = 0;
+//   MODE_BONUS   the same, then the target model's bonus token ([B, H, .]
+//                inputs, applied also when n_b = 0), then one write;
+//   MODE_VERIFY  all K drafts with their readouts from the committed state;
+//                the state is read and never written.
+template <int DK, int DV, typename TIn, typename TOut, bool VEC, int MODE>
 __global__ void __launch_bounds__(2 * DV)
-k_replay(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slot, int H, int K,
+k_tokens(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slot, int H, int K,
          const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
          const float *__restrict__ alpha, const float *__restrict__ beta,
-         const int32_t *__restrict__ n_accept, TOut *__restrict__ out, int32_t *__restrict__ err)
+         const int32_t *__restrict__ n_accept, TOut *__restrict__ out,
+         const TIn *__restrict__ qb, const TIn *__restrict__ kb, const TIn *__restrict__ vb,
+         const float *__restrict__ alpha_b, const float *__restrict__ beta_b,
+         TOut *__restrict__ out_b, int32_t *__restrict__ err)
 {
     constexpr int RPL = DK / 8;
     const int bh = blockIdx.x;
@@ -228,12 +242,15 @@ k_replay(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
         if (err && threadIdx.x == 0) atomicOr(err, HLA_DEVERR_SLOT);
         return;
     }
-    int n = n_accept[b];
-    if (n < 0 || n > K) {
-        if (err && threadIdx.x == 0 && h == 0) atomicOr(err, HLA_DEVERR_ACCEPT);
-        n = n < 0 ? 0 : K;
+    int n = K;
+    if constexpr (MODE != MODE_VERIFY) {
+        n = n_accept[b];
+        if (n < 0 || n > K) {
+            if (err && threadIdx.x == 0 && h == 0) atomicOr(err, HLA_DEVERR_ACCEPT);
+            n = n < 0 ? 0 : K;
+        }
     }
-    if (n == 0) return;  // nothing accepted: the state is not touched
+    if (MODE == MODE_REPLAY && n == 0) return;  // nothing accepted: the state is not touched
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int cg = lane & 7, rg = lane >> 3;
     const int col0 = wave * 32 + cg * 4, row0 = rg * RPL;
@@ -251,53 +268,75 @@ k_replay(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
         tile_token<RPL, VEC>(x, kk, qq, aa, bt, vv, o);
         if (out && rg == 0) store_out4(out + tok * DV + col0, o);
     }
-    tile_store<RPL>(S, DV, x);
+    if constexpr (MODE == MODE_BONUS) {
+        TokenRaw<DK, TIn, VEC> raw;
+        token_load<DK, DV, TIn, VEC>(qb, kb, vb, alpha_b, beta_b, (size_t)bh, row0, col0, raw);
+        float kk[RPL], qq[RPL], aa[VEC ? RPL : 1], vv[4], bt;
+        token_convert<DK, TIn, VEC>(raw, qq, kk, aa, vv, bt);
+        float o[4];
+        tile_token<RPL, VEC>(x, kk, qq, aa, bt, vv, o);
+        if (out_b && rg == 0) store_out4(out_b + (size_t)bh * DV + col0, o);
+    }
+    if constexpr (MODE != MODE_VERIFY) tile_store<RPL>(S, DV, x);
 }
 
 // ----------------------------------------------------------------- dispatch
 
-template <int DK, int DV, typename TIn, typename TOut, bool VEC>
-static int launch_typed(const StepArgs &a, bool replay, int32_t *err, hipStream_t st)
+template <int DK, int DV, typename TIn, typename TOut, bool VEC, int MODE>
+static void launch_tokens(const StepArgs &a, int32_t *err, hipStream_t st)
 {
     const dim3 grid((unsigned)((size_t)a.B * a.H)), block(2 * DV);
-    if (replay)
-        hipLaunchKernelGGL((k_replay<DK, DV, TIn, TOut, VEC>), grid, block, 0, st, a.state,
-                           a.n_slots, a.slot, a.H, a.K, (const TIn *)a.q, (const TIn *)a.k,
-                           (const TIn *)a.v, a.alpha, a.beta, a.n_accept, (TOut *)a.out, err);
-    else
+    hipLaunchKernelGGL((k_tokens<DK, DV, TIn, TOut, VEC, MODE>), grid, block, 0, st, a.state,
+                       a.n_slots, a.slot, a.H, a.K, (const TIn *)a.q, (const TIn *)a.k,
+                       (const TIn *)a.v, a.alpha, a.beta, a.n_accept, (TOut *)a.out,
+                       (const TIn *)a.qb, (const TIn *)a.kb, (const TIn *)a.vb, a.alpha_b,
+                       a.beta_b, (TOut *)a.out_b, err);
+}
+
+template <int DK, int DV, typename TIn, typename TOut, bool VEC>
+static int launch_typed(const StepArgs &a, int32_t *err, hipStream_t st)
+{
+    const dim3 grid((unsigned)((size_t)a.B * a.H)), block(2 * DV);
+    switch (a.mode) {
+    case MODE_STEP:
         hipLaunchKernelGGL((k_delta_step<DK, DV, TIn, TOut, VEC>), grid, block, 0, st, a.state,
                            a.n_slots, a.slot, a.H, (const TIn *)a.q, (const TIn *)a.k,
                            (const TIn *)a.v, a.alpha, a.beta, (TOut *)a.out, err);
+        break;
+    case MODE_REPLAY: launch_tokens<DK, DV, TIn, TOut, VEC, MODE_REPLAY>(a, err, st); break;
+    case MODE_BONUS: launch_tokens<DK, DV, TIn, TOut, VEC, MODE_BONUS>(a, err, st); break;
+    default: launch_tokens<DK, DV, TIn, TOut, VEC, MODE_VERIFY>(a, err, st); break;
+    }
     return hipGetLastError() == hipSuccess ? HLA_OK : HLA_ERR_LAUNCH;
 }
 
 template <int DK, int DV, typename TIn, typename TOut>
-static int launch_decay(const StepArgs &a, bool replay, int32_t *err, hipStream_t st)
+static int launch_decay(const StepArgs &a, int32_t *err, hipStream_t st)
 {
-    return a.decay == HLA_DECAY_VECTOR ? launch_typed<DK, DV, TIn, TOut, true>(a, replay, err, st)
-                                       : launch_typed<DK, DV, TIn, TOut, false>(a, replay, err, st);
+    return a.decay == HLA_DECAY_VECTOR ? launch_typed<DK, DV, TIn, TOut, true>(a, err, st)
+                                       : launch_typed<DK, DV, TIn, TOut, false>(a, err, st);
 }
 
 template <int DK, int DV>
-static int launch_dtypes(const StepArgs &a, bool replay, int32_t *err, hipStream_t st)
+static int launch_dtypes(const StepArgs &a, int32_t *err, hipStream_t st)
 {
     const bool in16 = a.in_dtype == HLA_BF16, out16 = a.out_dtype == HLA_BF16;
     if (in16)
-        return out16 ? launch_decay<DK, DV, uint16_t, uint16_t>(a, replay, err, st)
-                     : launch_decay<DK, DV, uint16_t, float>(a, replay, err, st);
-    return out16 ? launch_decay<DK, DV, float, uint16_t>(a, replay, err, st)
-                 : launch_decay<DK, DV, float, float>(a, replay, err, st);
+        return out16 ? launch_decay<DK, DV, uint16_t, uint16_t>(a, err, st)
+                     : launch_decay<DK, DV, uint16_t, float>(a, err, st);
+    return out16 ? launch_decay<DK, DV, float, uint16_t>(a, err, st)
+                 : launch_decay<DK, DV, float, float>(a, err, st);
 }
 
-static int run_step(const StepArgs &a, bool replay, int32_t *err, void *stream)
+static int run_step(const StepArgs &a, int32_t *err, void *stream)
 {
-    int rc = check_step(a, replay);
+    int rc = check_step(a);
     if (rc != HLA_OK || a.B == 0) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (a.dk == 128 && a.dv == 128) return launch_dtypes<128, 128>(a, replay, err, st);
-    if (a.dk == 128 && a.dv == 64) return launch_dtypes<128, 64>(a, replay, err, st);
-    if (a.dk == 64 && a.dv == 128) return launch_dtypes<64, 128>(a, replay, err, st);
-    return launch_dtypes<64, 64>(a, replay, err, st);
+    if (a.dk == 128 && a.dv == 128) return launch_dtypes<128, 128>(a, err, st);
+    if (a.dk == 128 && a.dv == 64) return launch_dtypes<128, 64>(a, err, st);
+    if (a.dk == 64 && a.dv == 128) return launch_dtypes<64, 128>(a, err, st);
+    return launch_dtypes<64, 64>(a, err, st);
 }
 
 } // namespace hla
@@ -309,8 +348,8 @@ int gdn_step(float *state, int n_slots, const int32_t *slot, int B, int H, int d
              const float *beta, void *out, int out_dtype, int32_t *err_flag, void *stream)
 {
     hla::StepArgs a{state, n_slots, slot, B, H, dk, dv, 1, q, k, v, in_dtype, alpha,
-                    HLA_DECAY_SCALAR, beta, nullptr, out, out_dtype};
-    return hla::run_step(a, false, err_flag, stream);
+                    HLA_DECAY_SCALAR, beta, nullptr, out, out_dtype, hla::MODE_STEP};
+    return hla::run_step(a, err_flag, stream);
 }
 
 int kda_step(float *state, int n_slots, const int32_t *slot, int B, int H, int dk, int dv,
@@ -318,8 +357,8 @@ int kda_step(float *state, int n_slots, const int32_t *slot, int B, int H, int d
              const float *beta, void *out, int out_dtype, int32_t *err_flag, void *stream)
 {
     hla::StepArgs a{state, n_slots, slot, B, H, dk, dv, 1, q, k, v, in_dtype, alpha,
-                    HLA_DECAY_VECTOR, beta, nullptr, out, out_dtype};
-    return hla::run_step(a, false, err_flag, stream);
+                    HLA_DECAY_VECTOR, beta, nullptr, out, out_dtype, hla::MODE_STEP};
+    return hla::run_step(a, err_flag, stream);
 }
 
 int replay_accepted(float *state, int n_slots, const int32_t *slot, int B, int H, int dk, int dv,
@@ -329,8 +368,35 @@ int replay_accepted(float *state, int n_slots, const int32_t *slot, int B, int H
                     void *stream)
 {
     hla::StepArgs a{state, n_slots, slot, B, H, dk, dv, K, q, k, v, in_dtype, alpha,
-                    decay_kind, beta, n_accept, out, out_dtype};
-    return hla::run_step(a, true, err_flag, stream);
+                    decay_kind, beta, n_accept, out, out_dtype, hla::MODE_REPLAY};
+    return hla::run_step(a, err_flag, stream);
+}
+
+int replay_accepted_bonus(float *state, int n_slots, const int32_t *slot, int B, int H, int dk,
+                          int dv, int K, const void *q, const void *k, const void *v,
+                          int in_dtype, const float *alpha, int decay_kind, const float *beta,
+                          const int32_t *n_accept, void *out, const void *q_bonus,
+                          const void *k_bonus, const void *v_bonus, const float *alpha_bonus,
+                          const float *beta_bonus, void *out_bonus, int out_dtype,
+                          int32_t *err_flag, void *stream)
+{
+    hla::StepArgs a{state,     n_slots,  slot,    B,       H,          dk,          dv,
+                    K,         q,        k,       v,       in_dtype,   alpha,       decay_kind,
+                    beta,      n_accept, out,     out_dtype, hla::MODE_BONUS, q_bonus, k_bonus,
+                    v_bonus,   alpha_bonus, beta_bonus, out_bonus};
+    return hla::run_step(a, err_flag, stream);
+}
+
+int verify_drafts(const float *state, int n_slots, const int32_t *slot, int B, int H, int dk,
+                  int dv, int K, const void *q, const void *k, const void *v, int in_dtype,
+                  const float *alpha, int decay_kind, const float *beta, void *out,
+                  int out_dtype, int32_t *err_flag, void *stream)
+{
+    // the kernel never writes the state in this mode
+    hla::StepArgs a{const_cast<float *>(state), n_slots, slot, B, H, dk, dv, K, q, k, v,
+                    in_dtype, alpha, decay_kind, beta, nullptr, out, out_dtype,
+                    hla::MODE_VERIFY};
+    return hla::run_step(a, err_flag, stream);
 }
 
 } // extern "C"

@@ -277,6 +277,50 @@ HLA_API int replay_accepted(float *state, int n_slots, const int32_t *slot, int 
                     const int32_t *n_accept, void *out, int out_dtype, int32_t *err_flag,
                     void *stream);
 
+/* -------------------------------------------------------------------------
+ * replay_accepted_bonus -- replay_accepted fused with the next ordinary step
+ * ([K3] "Speculative decoding without state snapshots": after verification
+ * one kernel replays the accepted projections on-chip, adds the target
+ * model's bonus token and continues).  For request b: the first n_b draft
+ * tokens as replay_accepted, then one gdn_step / kda_step update with the
+ * bonus token's own projections, all on one read and one write of the state.
+ * The bonus token is applied for every live request, also when n_b = 0.
+ *
+ * q .. n_accept, out  as replay_accepted (out may be NULL).
+ * q_bonus, k_bonus    device [B, H, dk]; v_bonus [B, H, dv] (in_dtype).
+ * alpha_bonus         device float32 [B, H] or [B, H, dk] (decay_kind).
+ * beta_bonus          device float32 [B, H].
+ * out_bonus           device [B, H, dv] of out_dtype, or NULL: the bonus
+ *                     token's readout from the updated state.
+ * Errors: as replay_accepted, plus NULL for a missing bonus input.
+ * ---------------------------------------------------------------------- */
+HLA_API int replay_accepted_bonus(float *state, int n_slots, const int32_t *slot, int B, int H,
+                          int dk, int dv, int K, const void *q, const void *k, const void *v,
+                          int in_dtype, const float *alpha, int decay_kind, const float *beta,
+                          const int32_t *n_accept, void *out, const void *q_bonus,
+                          const void *k_bonus, const void *v_bonus, const float *alpha_bonus,
+                          const float *beta_bonus, void *out_bonus, int out_dtype,
+                          int32_t *err_flag, void *stream);
+
+/* -------------------------------------------------------------------------
+ * verify_drafts -- the recurrent layer's part of the target model's verify
+ * pass over K draft tokens ([K3] "Speculative decoding without state
+ * snapshots": the committed state must not absorb drafts that may be
+ * rejected).  For every request, the committed state is advanced through all
+ * K draft tokens in order in registers and the readout after each token is
+ * written to out[b, t]; the state in memory is only read.  The same
+ * projections, kept by the caller, are what replay_accepted later replays.
+ *
+ * state    device float32 [n_slots, H, dk, dv], read only.
+ * q .. beta, slot, K  as replay_accepted.
+ * out      device [B, K, H, dv] of out_dtype; required.
+ * Errors: as replay_accepted; NULL if out is NULL.
+ * ---------------------------------------------------------------------- */
+HLA_API int verify_drafts(const float *state, int n_slots, const int32_t *slot, int B, int H,
+                  int dk, int dv, int K, const void *q, const void *k, const void *v,
+                  int in_dtype, const float *alpha, int decay_kind, const float *beta,
+                  void *out, int out_dtype, int32_t *err_flag, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

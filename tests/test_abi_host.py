@@ -108,6 +108,39 @@ def test_kda_and_replay_validation(L):
     assert rp(decay=2) == DTYPE
     assert rp(B=0) == OK
 
+    # replay fused with the bonus token
+    bonus = dict(base)
+    n_out = bonus.pop("out_dtype")
+    tail = dict(err=bonus.pop("err"), stream=bonus.pop("stream"))
+    bonus.update(qb=f(), kb=f(), vb=f(), ab=f(), bb=f(), out_b=f(), out_dtype=n_out, **tail)
+
+    def rb(**kw):
+        a = dict(bonus)
+        a.update(kw)
+        return L.replay_accepted_bonus(*a.values())
+
+    assert rb(qb=None) == NULL and rb(bb=None) == NULL and rb(n_accept=None) == NULL
+    assert rb(kb=ctypes.c_void_p(f().value + 8)) == ALIGN
+    assert rb(out_b=ctypes.c_void_p(f().value + 4)) == ALIGN
+    st = f()
+    assert rb(state=st, out_b=st) == ALIAS
+    assert rb(qb=st, state=st) == ALIAS
+    assert rb(K=0) == SHAPE and rb(B=0) == OK
+    # the verify pass: readouts are required, the state is only read
+    ver = {k: base[k] for k in ("state", "n_slots", "slot", "B", "H", "dk", "dv", "K", "q",
+                                "k", "v", "in_dtype", "alpha", "decay", "beta")}
+    ver.update(out=f(), out_dtype=0, err=None, stream=None)
+
+    def vd(**kw):
+        a = dict(ver)
+        a.update(kw)
+        return L.verify_drafts(*a.values())
+
+    assert vd(out=None) == NULL
+    assert vd(K=17) == SHAPE and vd(decay=5) == DTYPE
+    assert vd(out=st, state=st) == ALIAS
+    assert vd(B=0) == OK
+
 
 def test_damp_validation(L):
     f = Fake()
