@@ -56,6 +56,14 @@ def _declare(L):
     L.orc_verify.argtypes = [_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P]
     L.orc_replay_bonus.argtypes = [_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P,
                                    _P, _P, _P, _P, _P, _P, _P]
+    _D = ctypes.c_double
+    L.orc_static_horizon.argtypes = [_P, _P, _I, _I, _D, _D, _P]
+    L.orc_static_mask.argtypes = [_P, _I, _D, _P]
+    L.orc_replay_window.argtypes = [_P, _P, _I, _I, _I, _P]
+    L.orc_replay_window.restype = _I
+    L.orc_dasc_pack_int8.argtypes = [_P, _L, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P]
+    L.orc_dasc_restore_int8.argtypes = [_P, _P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P,
+                                        _L]
     L.orc_half_to_double.argtypes = [ctypes.c_uint16]
     L.orc_half_to_double.restype = ctypes.c_double
     L.orc_double_to_half.argtypes = [ctypes.c_double]
@@ -333,3 +341,73 @@ def dasc_restore(packed, offsets, unit_index, L, n_units, src_slot, dst_slot, ac
                            n_units, ub, _ptr(src), _ptr(dst), len(src), _ptr(active_out),
                            S_dst * n_units * ub, S_dst)
     return active_out
+
+
+# --------------------------------------------------------------------- horizons
+
+GATE_SOFTPLUS, GATE_BOUNDED = 0, 1
+
+
+def static_horizon(A_log, d, gate, a_s, eps=1e-3):
+    """Static retention horizon H per unit (dasc Eq. (2)-(3)); arrays of any shape."""
+    A_log, d = _f64(A_log), _f64(d)
+    H = np.zeros(A_log.shape, np.float64)
+    lib().orc_static_horizon(_ptr(A_log), _ptr(d), A_log.size, int(gate), float(a_s),
+                             float(eps), _ptr(H))
+    return H
+
+
+def static_mask(H, W_max):
+    """uint8 mask, 1 where the unit is global (H > W_max)."""
+    H = _f64(H)
+    m = np.zeros(H.shape, np.uint8)
+    lib().orc_static_mask(_ptr(H), H.size, float(W_max), _ptr(m))
+    return m
+
+
+def replay_window(H, mask, n_prefix, W_max):
+    """(W_replay, W_u int32 per unit) of dasc Eq. (7)."""
+    H = _f64(H)
+    mask = np.ascontiguousarray(mask, np.uint8)
+    W_u = np.zeros(H.shape, np.int32)
+    w = lib().orc_replay_window(_ptr(H), _ptr(mask), H.size, int(n_prefix), int(W_max),
+                                _ptr(W_u))
+    return int(w), W_u
+
+
+# --------------------------------------------------------------------- INT8 checkpoints
+
+def dasc_pack_int8(active, offsets, unit_index, src_slot, dst_slot, S_ckpt):
+    """active float32 [L, S_act, n_units, unit_rows, dv] -> (codes int8
+    [S_ckpt, R, unit_rows, dv], scales float32 [S_ckpt, R, unit_rows]); rows of
+    checkpoint slots no pair names are zero."""
+    active = np.ascontiguousarray(active, np.float32)
+    L, S_act, n_units, unit_rows, dv = active.shape
+    R = int(offsets[-1])
+    codes = np.zeros((S_ckpt, R, unit_rows, dv), np.int8)
+    scales = np.zeros((S_ckpt, R, unit_rows), np.float32)
+    offsets, unit_index = _i32(offsets), _i32(unit_index)
+    src_slot, dst_slot = _i32(src_slot), _i32(dst_slot)
+    lib().orc_dasc_pack_int8(_ptr(active), S_act * n_units * unit_rows * dv * 4, L, n_units,
+                             unit_rows, dv, _ptr(offsets), _ptr(unit_index), R, _ptr(src_slot),
+                             _ptr(dst_slot), len(src_slot), _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def dasc_restore_int8(codes, scales, offsets, unit_index, L, n_units, src_slot, dst_slot,
+                      active_out):
+    """Dequantise into active_out float32 [L, S_dst, n_units, unit_rows, dv] (in place)."""
+    if not (active_out.dtype == np.float32 and active_out.flags.c_contiguous):
+        raise TypeError("active_out must be C-contiguous float32")
+    _, S_dst, _, unit_rows, dv = active_out.shape
+    codes = np.ascontiguousarray(codes, np.int8)
+    scales = np.ascontiguousarray(scales, np.float32)
+    R = codes.shape[1]
+    offsets, unit_index = _i32(offsets), _i32(unit_index)
+    src_slot, dst_slot = _i32(src_slot), _i32(dst_slot)
+    lib().orc_dasc_restore_int8(_ptr(codes), _ptr(scales), R, _ptr(offsets), _ptr(unit_index),
+                                L, n_units, unit_rows, dv, _ptr(src_slot), _ptr(dst_slot),
+                                len(src_slot), _ptr(active_out),
+                                S_dst * n_units * unit_rows * dv * 4)
+    return active_out
+

@@ -584,3 +584,125 @@ ORC_API void orc_dasc_restore(const uint8_t *packed, int S_ckpt, int R_total,
         }
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Static retention horizons ([dasc] §3.3 Eq. (2)-(3)) and the selection    */
+/* mask of §4.1.  For unit u (a GDN head or a KDA (head, key) channel) with   */
+/* learned log-scale A_log[u] and decay bias d[u], and the model-level        */
+/* representative gate input a_s:                                            */
+/*   gate 0 (softplus gate):  g = -exp(A_log) * softplus(a_s + d),           */
+/*                            softplus(z) = ln(1 + e^z);                      */
+/*   gate 1 (bounded gate):   g = l * sigmoid(exp(A_log) * (a_s + d)),       */
+/*                            l = -5, sigmoid(z) = 1 / (1 + e^-z);           */
+/*   H = ln(eps) / g  (eps = 1e-3 on the page).                               */
+/* A unit is global (retained in the checkpoint) when H > W_max.             */
+/* ------------------------------------------------------------------------ */
+static double orc_softplus(double z)
+{
+    /* ln(1 + e^z), written so that e^z cannot overflow */
+    return z > 0.0 ? z + log1p(exp(-z)) : log1p(exp(z));
+}
+
+ORC_API void orc_static_horizon(const double *A_log, const double *d, int n, int gate,
+                                double a_s, double eps, double *H)
+{
+    for (int u = 0; u < n; ++u) {
+        double z = a_s + d[u];
+        double g;
+        if (gate == 0)
+            g = -exp(A_log[u]) * orc_softplus(z);
+        else
+            g = -5.0 / (1.0 + exp(-exp(A_log[u]) * z));
+        H[u] = log(eps) / g;
+    }
+}
+
+ORC_API void orc_static_mask(const double *H, int n, double W_max, uint8_t *mask)
+{
+    for (int u = 0; u < n; ++u) mask[u] = H[u] > W_max ? 1 : 0;
+}
+
+/* Refresh window of dasc-wr ([dasc] §4.2 Eq. (7)), for W_max >= 4:
+     next_pow2(x) = 2^ceil(log2 x) for x > 0, next_pow2(0) = 4;
+     W_u = clamp(next_pow2(H_u), 4, W_max);
+     W_replay = min(n_prefix, max of W_u over the omitted (local) units),
+   and W_replay = 0 when no unit is omitted.  W_u is written for every unit. */
+ORC_API int orc_replay_window(const double *H, const uint8_t *mask, int n, int n_prefix,
+                              int W_max, int32_t *W_u)
+{
+    int any_local = 0;
+    double w_max_local = 0.0;
+    for (int u = 0; u < n; ++u) {
+        double w = H[u] > 0.0 ? pow(2.0, ceil(log2(H[u]))) : 4.0;
+        if (w < 4.0) w = 4.0;
+        if (w > (double)W_max) w = (double)W_max;
+        W_u[u] = (int32_t)w;
+        if (!mask[u]) {
+            any_local = 1;
+            if (w > w_max_local) w_max_local = w;
+        }
+    }
+    if (!any_local) return 0;
+    return (double)n_prefix < w_max_local ? n_prefix : (int)w_max_local;
+}
+
+/* ------------------------------------------------------------------------ */
+/* INT8-composed checkpoints ([dasc] App. E.1 and E.2): the retained units   */
+/* of the FP32 temporal state are quantised once when the checkpoint is      */
+/* stored, one scale per key-channel row over its dv values (Eq. (8), the    */
+/* row quantiser above), and dequantised once, q * s in FP32, into a fresh   */
+/* active slot on a hit; omitted units read as zero (dasc-nr).               */
+/* A unit is unit_rows rows of dv FP32 values: dk rows for a GDN head, one   */
+/* row for a KDA key channel.  Layer l's active state is                     */
+/* [S, n_units, unit_rows, dv] starting layer_stride_bytes * l into `active`;*/
+/* codes are [S_ckpt, R_total, unit_rows, dv] int8 and scales               */
+/* [S_ckpt, R_total, unit_rows] float32.                                     */
+/* ------------------------------------------------------------------------ */
+ORC_API void orc_dasc_pack_int8(const uint8_t *active, long layer_stride_bytes, int L,
+                                int n_units, int unit_rows, int dv, const int32_t *offsets,
+                                const int32_t *unit_index, int R_total,
+                                const int32_t *src_slot, const int32_t *dst_slot, int N,
+                                int8_t *codes, float *scales)
+{
+    double *row = (double *)malloc(sizeof(double) * dv);
+    for (int n = 0; n < N; ++n) {
+        for (int l = 0; l < L; ++l) {
+            for (int p = offsets[l]; p < offsets[l + 1]; ++p) {
+                const float *unit = (const float *)(active + (long)l * layer_stride_bytes) +
+                                    ((long)src_slot[n] * n_units + unit_index[p]) *
+                                        unit_rows * dv;
+                for (int r = 0; r < unit_rows; ++r) {
+                    for (int j = 0; j < dv; ++j) row[j] = (double)unit[(long)r * dv + j];
+                    long dst_row = ((long)dst_slot[n] * R_total + p) * unit_rows + r;
+                    orc_quantize_row_int8(row, dv, codes + dst_row * dv, scales + dst_row);
+                }
+            }
+        }
+    }
+    free(row);
+}
+
+ORC_API void orc_dasc_restore_int8(const int8_t *codes, const float *scales, int R_total,
+                                   const int32_t *offsets, const int32_t *unit_index, int L,
+                                   int n_units, int unit_rows, int dv,
+                                   const int32_t *src_slot, const int32_t *dst_slot, int N,
+                                   uint8_t *active_out, long layer_stride_bytes)
+{
+    long unit_vals = (long)unit_rows * dv;
+    for (int n = 0; n < N; ++n) {
+        for (int l = 0; l < L; ++l) {
+            float *layer = (float *)(active_out + (long)l * layer_stride_bytes) +
+                           (long)dst_slot[n] * n_units * unit_vals;
+            memset(layer, 0, sizeof(float) * (size_t)(n_units * unit_vals));
+            for (int p = offsets[l]; p < offsets[l + 1]; ++p) {
+                float *unit = layer + (long)unit_index[p] * unit_vals;
+                for (int r = 0; r < unit_rows; ++r) {
+                    long src_row = ((long)src_slot[n] * R_total + p) * unit_rows + r;
+                    double s = (double)scales[src_row];
+                    for (int j = 0; j < dv; ++j)  /* exact product, rounded once to FP32 */
+                        unit[(long)r * dv + j] = (float)((double)codes[src_row * dv + j] * s);
+                }
+            }
+        }
+    }
+}

@@ -83,6 +83,10 @@ class Config:
     plan_seed: int = 0
     group: int = 0  # DAMP: INT8 values per FP32 scale (0: one scale per row)
     sr: bool = False  # DAMP: value scaling and reordering plan
+    # dasc static-horizon selection: gate kind (0 softplus, 1 bounded), a_s, cutoff
+    gate: int = 0
+    a_s: float = 0.0
+    W_max: int = 0
     # dasc + replay
     L: int = 0
     slots: int = 0
@@ -107,6 +111,10 @@ CONFIGS = {
     "damp_kda_g32sr": Config("damp_kda_g32sr", B=256, H=32, dk=128, dv=128, steps=100,
                              in_dtype="bf16", decay="vector", state_sigma=0.05, seed=1006,
                              K_hi=16, plan_seed=2006, group=32, sr=True),
+    # KDA checkpoints: one unit per (head, key channel) row, selected by static horizons
+    "dasc_kda": Config("dasc_kda", B=512, H=32, dk=128, dv=128, steps=1, in_dtype="f32",
+                       decay="vector", state_sigma=0.05, seed=1007, plan_seed=2007, L=4,
+                       slots=512, K=8, gate=0, a_s=-0.3, W_max=16),
     "dasc_gdn": Config("dasc_gdn", B=512, H=32, dk=128, dv=128, steps=1, in_dtype="f32",
                        decay="scalar", alpha_lo=0.90, alpha_hi=0.9999, state_sigma=0.05,
                        seed=1005, plan_seed=2005, L=4, slots=512, retention=0.5, K=8),
@@ -126,6 +134,7 @@ def rng(seed: int, *stream: int) -> np.random.Generator:
 
 _STREAM_STEP, _STREAM_STATE, _STREAM_PLAN, _STREAM_MASK, _STREAM_REPLAY = 1, 2, 3, 4, 5
 _STREAM_VPLAN = 6
+_STREAM_GATE = 7
 
 
 def _l2n(x: np.ndarray) -> np.ndarray:
@@ -230,6 +239,22 @@ def damp_group(cfg: Config) -> int:
 
 
 # ----------------------------------------------------------------- dasc
+
+
+def gate_params(cfg: Config) -> tuple[np.ndarray, np.ndarray]:
+    """Synthetic learned gate parameters (A_log, d), float32 [L, H, dk] (one per KDA
+    (head, key) channel).  Layers differ in their typical decay and heads within a layer
+    around it, so the static-horizon selection is ragged across layers and mixed within
+    heads: per layer mu_l ~ U(-0.5, 1.5), per head an offset ~ N(0, 0.5), per channel
+    d = mu_l + offset + N(0, 1) and A_log ~ N(0, 0.5)."""
+    g = rng(cfg.plan_seed, _STREAM_GATE)
+    L, H, dk = cfg.L, cfg.H, cfg.dk
+    mu = g.uniform(-0.5, 1.5, L)
+    head = g.normal(0.0, 0.5, (L, H))
+    A_log = g.normal(0.0, 0.5, (L, H, dk))
+    d = mu[:, None, None] + head[:, :, None] + g.normal(0.0, 1.0, (L, H, dk))
+    return A_log.astype(np.float32), d.astype(np.float32)
+
 
 
 def dasc_masks(cfg: Config, lo: int | None = None, hi: int | None = None) -> np.ndarray:

@@ -90,3 +90,13 @@ def test_damp_value_plan():
     p2, s2 = synth.damp_value_plan(cfg)
     assert np.array_equal(perm, p2) and np.array_equal(scale, s2)
     assert synth.damp_group(cfg) == 32 and synth.damp_group(synth.CONFIGS["damp_kda"]) == 128
+
+
+def test_gate_params():
+    cfg = synth.CONFIGS["dasc_kda"]
+    A, d = synth.gate_params(cfg)
+    assert A.shape == d.shape == (cfg.L, cfg.H, cfg.dk) and A.dtype == np.float32
+    A2, d2 = synth.gate_params(cfg)
+    assert np.array_equal(A, A2) and np.array_equal(d, d2)
+    # layers differ in their typical bias
+    assert np.ptp(d.mean(axis=(1, 2))) > 0.3
