@@ -64,6 +64,7 @@ def _declare(L):
     L.orc_dasc_pack_int8.argtypes = [_P, _L, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P]
     L.orc_dasc_restore_int8.argtypes = [_P, _P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P,
                                         _L]
+    L.orc_dasc_refresh_local.argtypes = [_P, _L, _P, _L, _I, _I, _L, _P, _P, _P, _I]
     L.orc_half_to_double.argtypes = [ctypes.c_uint16]
     L.orc_half_to_double.restype = ctypes.c_double
     L.orc_double_to_half.argtypes = [ctypes.c_double]
@@ -410,4 +411,20 @@ def dasc_restore_int8(codes, scales, offsets, unit_index, L, n_units, src_slot, 
                                 len(src_slot), _ptr(active_out),
                                 S_dst * n_units * unit_rows * dv * 4)
     return active_out
+
+
+def dasc_refresh_local(scratch, active, local, src_slot, dst_slot):
+    """Copy the local units (local uint8 [L, n_units] == 1) of scratch slots into active
+    slots, in place; both uint8 [L, S, n_units, unit_bytes]."""
+    scratch = np.ascontiguousarray(scratch, np.uint8)
+    if not (active.dtype == np.uint8 and active.flags.c_contiguous):
+        raise TypeError("active must be C-contiguous uint8")
+    L, S_s, n_units, ub = scratch.shape
+    S_a = active.shape[1]
+    local = np.ascontiguousarray(local, np.uint8)
+    src_slot, dst_slot = _i32(src_slot), _i32(dst_slot)
+    lib().orc_dasc_refresh_local(_ptr(scratch), S_s * n_units * ub, _ptr(active),
+                                 S_a * n_units * ub, L, n_units, ub, _ptr(local),
+                                 _ptr(src_slot), _ptr(dst_slot), len(src_slot))
+    return active
 

@@ -706,3 +706,25 @@ ORC_API void orc_dasc_restore_int8(const int8_t *codes, const float *scales, int
         }
     }
 }
+
+/* dasc-wr copy-back ([dasc] §4.2): after the refresh window has been
+   replayed from a zero-initialised scratch state, only the refreshed local
+   units are copied into the active state; the retained global units keep
+   their exact checkpoint values.  `local` is uint8 [L, n_units], 1 for a
+   local (omitted) unit.  Both states are [S, n_units, unit_bytes] per layer
+   with their own layer strides. */
+ORC_API void orc_dasc_refresh_local(const uint8_t *scratch, long scratch_layer_stride,
+                                    uint8_t *active, long layer_stride, int L, int n_units,
+                                    long unit_bytes, const uint8_t *local,
+                                    const int32_t *src_slot, const int32_t *dst_slot, int N)
+{
+    for (int n = 0; n < N; ++n)
+        for (int l = 0; l < L; ++l)
+            for (int u = 0; u < n_units; ++u) {
+                if (!local[(long)l * n_units + u]) continue;
+                memcpy(active + l * layer_stride + ((long)dst_slot[n] * n_units + u) * unit_bytes,
+                       scratch + l * scratch_layer_stride +
+                           ((long)src_slot[n] * n_units + u) * unit_bytes,
+                       (size_t)unit_bytes);
+            }
+}

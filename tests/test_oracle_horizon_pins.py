@@ -155,3 +155,26 @@ def test_int8_checkpoint_bytes_closed_form(orc):
     ratio = act.nbytes / (codes.nbytes + scales.nbytes)
     assert ratio == 4 * dv / (dv + 4)
     assert round(ratio, 2) == 3.88
+
+
+def test_refresh_local_copies_local_units_only(orc):
+    """dasc-wr copy-back: local units take the scratch values, global units keep theirs,
+    and an all-global mask copies nothing."""
+    g = rng(75)
+    L, S_, n_units, ub = 3, 4, 6, 32
+    scratch = g.integers(0, 256, size=(L, S_, n_units, ub), dtype=np.uint8)
+    active = g.integers(0, 256, size=(L, S_ + 1, n_units, ub), dtype=np.uint8)
+    mask = (g.random((L, n_units)) < 0.5).astype(np.uint8)  # 1 = global (retained)
+    local = 1 - mask
+    src = np.array([3, 1], np.int32)
+    dst = np.array([0, 4], np.int32)
+    out = orc.dasc_refresh_local(scratch, active.copy(), local, src, dst)
+    for n in range(2):
+        for l in range(L):
+            for u in range(n_units):
+                want = scratch[l, src[n], u] if local[l, u] else active[l, dst[n], u]
+                assert np.array_equal(out[l, dst[n], u], want)
+    untouched = [s for s in range(S_ + 1) if s not in dst]
+    assert np.array_equal(out[:, untouched], active[:, untouched])
+    out2 = orc.dasc_refresh_local(scratch, active.copy(), np.zeros_like(local), src, dst)
+    assert np.array_equal(out2, active)
