@@ -33,6 +33,15 @@ SIGNATURES = {
     "dasc_plan": ([_P, _I, _I, _P, _P, _I, _P, _P], _I),
     "dasc_pack": ([_P, _L, _I, _I, _I, _L, _P, _P, _I, _P, _P, _I, _P, _I, _P, _P], _I),
     "dasc_restore": ([_P, _I, _I, _P, _I, _I, _L, _P, _P, _I, _P, _L, _I, _P, _P], _I),
+    "dasc_pack_int8": ([_P, _L, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P],
+                       _I),
+    "dasc_restore_int8": ([_P, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P, _I, _P, _L, _I, _P, _P],
+                          _I),
+    "dasc_static_horizon": ([_P, _P, _I, _I, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                             _P, _P], _I),
+    "dasc_replay_window": ([_P, _P, _I, _I, _I, _P, _P], _I),
+    "dasc_refresh_local": ([_P, _L, _I, _P, _L, _I, _I, _I, _L, _P, _P, _I, _P, _P, _I, _P, _P],
+                           _I),
     "replay_accepted": ([_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P, _P, _I,
                          _P, _P], _I),
     "replay_accepted_bonus": ([_P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P, _I, _P, _P,
@@ -377,3 +386,79 @@ def dasc_restore(packed, S_ckpt, R_total, unit_pos, L, n_units, unit_bytes, src_
     _call("dasc_restore", _ptr(packed), S_ckpt, R_total, _ptr(unit_pos), L, n_units,
           int(unit_bytes), _ptr(src_slot), _ptr(dst_slot), src_slot.numel(), _ptr(active_out),
           int(layer_stride_bytes), S_dst, _ptr(err_flag), _stream(stream))
+
+
+def dasc_pack_int8(active, layer_stride_bytes, S_act, L, n_units, unit_rows, dv, offsets,
+                   unit_index, R_total, src_slot, dst_slot, codes, scales, S_ckpt, err_flag=None,
+                   stream=None):
+    """Quantise-once pack of the retained units of an FP32 state into (codes, scales)."""
+    for t, nm in ((offsets, "offsets"), (src_slot, "src_slot"), (dst_slot, "dst_slot")):
+        _dev(t, nm, _i32(), 1)
+    torch = _torch()
+    _dev(codes, "codes", (torch.int8,))
+    _dev(scales, "scales", _f32())
+    _call("dasc_pack_int8", _ptr(active), int(layer_stride_bytes), S_act, L, n_units, unit_rows,
+          dv, _ptr(offsets), _ptr(unit_index) if unit_index.numel() else None, R_total,
+          _ptr(src_slot), _ptr(dst_slot), src_slot.numel(), _ptr(codes), _ptr(scales), S_ckpt,
+          _ptr(err_flag), _stream(stream))
+
+
+def dasc_restore_int8(codes, scales, S_ckpt, R_total, unit_pos, L, n_units, unit_rows, dv,
+                      src_slot, dst_slot, active_out, layer_stride_bytes, S_dst, err_flag=None,
+                      stream=None):
+    """Dequantise-once restore into FP32 active slots, omitted units zero."""
+    for t, nm in ((src_slot, "src_slot"), (dst_slot, "dst_slot")):
+        _dev(t, nm, _i32(), 1)
+    _dev(unit_pos, "unit_pos", _i32())
+    _dev(active_out, "active_out", _f32())
+    _call("dasc_restore_int8", _ptr(codes), _ptr(scales), S_ckpt, R_total, _ptr(unit_pos), L,
+          n_units, unit_rows, dv, _ptr(src_slot), _ptr(dst_slot), src_slot.numel(),
+          _ptr(active_out), int(layer_stride_bytes), S_dst, _ptr(err_flag), _stream(stream))
+
+
+GATE_SOFTPLUS, GATE_BOUNDED = 0, 1
+
+
+def dasc_static_horizon(A_log, d, gate, a_s, W_max, eps=1e-3):
+    """Host: static horizons (float64) and the selection mask (uint8) of numpy float32
+    gate parameters of any shape."""
+    import numpy as np
+
+    A_log = np.ascontiguousarray(A_log, np.float32)
+    d = np.ascontiguousarray(d, np.float32)
+    if A_log.shape != d.shape:
+        raise ValueError("A_log and d must have the same shape")
+    H = np.zeros(A_log.shape, np.float64)
+    mask = np.zeros(A_log.shape, np.uint8)
+    _call("dasc_static_horizon", A_log.ctypes.data, d.ctypes.data, A_log.size, int(gate),
+          float(a_s), float(eps), float(W_max), H.ctypes.data, mask.ctypes.data)
+    return H, mask
+
+
+def dasc_replay_window(H, mask, n_prefix, W_max):
+    """Host: (W_replay, W_u int32) of the dasc-wr refresh window."""
+    import numpy as np
+
+    H = np.ascontiguousarray(H, np.float64)
+    mask = np.ascontiguousarray(mask, np.uint8)
+    W_u = np.zeros(H.shape, np.int32)
+    W = ctypes.c_int32(0)
+    _call("dasc_replay_window", H.ctypes.data, mask.ctypes.data, H.size, int(n_prefix),
+          int(W_max), W_u.ctypes.data, ctypes.byref(W))
+    return W.value, W_u
+
+
+def dasc_refresh_local(scratch, scratch_layer_stride_bytes, S_scratch, active,
+                       layer_stride_bytes, S_act, L, n_units, unit_bytes, offsets_local,
+                       unit_index_local, R_local, src_slot, dst_slot, err_flag=None,
+                       stream=None):
+    """Copy the local units (plan of the inverted mask) from scratch slots into active
+    slots; everything else in the active slots is left alone."""
+    for t, nm in ((offsets_local, "offsets"), (src_slot, "src_slot"), (dst_slot, "dst_slot")):
+        _dev(t, nm, _i32(), 1)
+    _call("dasc_refresh_local", _ptr(scratch), int(scratch_layer_stride_bytes), S_scratch,
+          _ptr(active), int(layer_stride_bytes), S_act, L, n_units, int(unit_bytes),
+          _ptr(offsets_local), _ptr(unit_index_local) if unit_index_local.numel() else None,
+          R_local, _ptr(src_slot), _ptr(dst_slot), src_slot.numel(), _ptr(err_flag),
+          _stream(stream))
+

@@ -8,11 +8,16 @@
 // loads and stores (each byte is touched once).  The ragged index arithmetic
 // (vector -> unit, unit -> layer) uses precomputed magic-number division and
 // a binary search over the L+1 layer offsets held in LDS.
+//
+// The same file holds the INT8-composed checkpoint (App. E.1-E.2: each
+// retained key-channel row quantised once at store, dequantised once on a
+// hit) and the dasc-wr copy-back of refreshed local units (§4.2).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 
 #include "hla.h"
+#include "hla_codec.h"
 #include "hla_device.h"
 #include "hla_internal.h"
 
@@ -137,6 +142,201 @@ k_dasc_restore(const uint8_t *__restrict__ packed, int S_ckpt, int R_total,
         if (dptr[i]) st_nt(reinterpret_cast<u32x4 *>(dptr[i]), buf[i]);
 }
 
+// Layer of flat position p: offs[lo] <= p < offs[lo + 1] (offsets in LDS).
+__device__ __forceinline__ int layer_of(const int32_t *offs, int L, uint32_t p)
+{
+    int lo = 0, hi = L;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((uint32_t)offs[mid] <= p) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// ------------------------------------------------------------------ dasc-wr copy-back
+//
+// Copy the listed units of scratch slot src into active slot dst, layer by
+// layer; units not listed are not touched.  The list is a ragged plan of the
+// LOCAL units (dasc_plan of the inverted selection mask).
+__global__ void __launch_bounds__(kCopyThreads)
+k_dasc_copy_units(const uint8_t *__restrict__ scratch, int64_t scratch_stride, int S_scratch,
+                  uint8_t *__restrict__ active, int64_t layer_stride, int S_act, int L,
+                  int n_units, int64_t unit_bytes, FastDiv unit_vecs,
+                  const int32_t *__restrict__ offsets, const int32_t *__restrict__ unit_index,
+                  int R_local, const int32_t *__restrict__ src_slot,
+                  const int32_t *__restrict__ dst_slot, int pair0, int32_t *__restrict__ err)
+{
+    __shared__ int32_t offs[kMaxLayers + 1];
+    for (int i = threadIdx.x; i <= L; i += kCopyThreads) offs[i] = offsets[i];
+    __syncthreads();
+    const int n = pair0 + blockIdx.y;
+    const int src = src_slot[n], dst = dst_slot[n];
+    if (src < 0 || src >= S_scratch || dst < 0 || dst >= S_act) {
+        if (err && threadIdx.x == 0 && blockIdx.x == 0) atomicOr(err, HLA_DEVERR_SLOT);
+        return;
+    }
+    const uint32_t total = (uint32_t)R_local * unit_vecs.d;
+    const uint32_t base = blockIdx.x * (kCopyThreads * kCopyVecs) + threadIdx.x;
+    const uint8_t *src_base = scratch + (int64_t)src * n_units * unit_bytes;
+    uint8_t *dst_base = active + (int64_t)dst * n_units * unit_bytes;
+
+    u32x4 buf[kCopyVecs];
+    uint8_t *dptr[kCopyVecs];
+#pragma unroll
+    for (int i = 0; i < kCopyVecs; ++i) {
+        const uint32_t e = base + i * kCopyThreads;
+        dptr[i] = nullptr;
+        if (e >= total) continue;
+        const uint32_t p = fdiv(e, unit_vecs);
+        const uint32_t off = e - p * unit_vecs.d;
+        const int l = layer_of(offs, L, p);
+        const int u = unit_index[p];
+        if (u < 0 || u >= n_units) {
+            if (err) atomicOr(err, HLA_DEVERR_PLAN);
+            continue;
+        }
+        const int64_t unit_off = (int64_t)u * unit_bytes + (int64_t)off * 16;
+        buf[i] = ld_nt(reinterpret_cast<const u32x4 *>(src_base + l * scratch_stride + unit_off));
+        dptr[i] = dst_base + l * layer_stride + unit_off;
+    }
+#pragma unroll
+    for (int i = 0; i < kCopyVecs; ++i)
+        if (dptr[i]) st_nt(reinterpret_cast<u32x4 *>(dptr[i]), buf[i]);
+}
+
+// ------------------------------------------------------------------ INT8 checkpoints
+//
+// One FP32 row of dv values is handled by CG = dv/8 adjacent lanes, 8 values
+// per lane: values 4*cg .. 4*cg+3 of each half of the row, so that every
+// 16-byte FP32 access and every 4-byte code access of a wave is contiguous
+// across the row's lanes (whole 64-byte segments per instruction).  A block
+// of 256 threads covers 256/CG rows per pass and a few passes, with
+// every pass's loads issued before the first conversion.  The row maximum is a DPP max over the
+// CG lanes; codes and scale come from the shared codec (hla_codec.h).
+// passes per block, measured on the checkpoint workloads (restore: more,
+// smaller blocks beat more rows in flight per lane)
+constexpr int kInt8PassesPack = 4;
+constexpr int kInt8PassesRestore = 1;
+
+template <int DV>
+__global__ void __launch_bounds__(kCopyThreads)
+k_dasc_pack_int8(const uint8_t *__restrict__ active, int64_t layer_stride, int S_act, int L,
+                 int n_units, int log2_rows, const int32_t *__restrict__ offsets,
+                 const int32_t *__restrict__ unit_index, int R_total,
+                 const int32_t *__restrict__ src_slot, const int32_t *__restrict__ dst_slot,
+                 int pair0, int8_t *__restrict__ codes, float *__restrict__ scales, int S_ckpt,
+                 int32_t *__restrict__ err)
+{
+    constexpr int CG = DV / 8, LCG = Log2<CG>::v, RPP = kCopyThreads / CG;
+    __shared__ int32_t offs[kMaxLayers + 1];
+    for (int i = threadIdx.x; i <= L; i += kCopyThreads) offs[i] = offsets[i];
+    __syncthreads();
+    const int n = pair0 + blockIdx.y;
+    const int src = src_slot[n], dst = dst_slot[n];
+    if (src < 0 || src >= S_act || dst < 0 || dst >= S_ckpt) {
+        if (err && threadIdx.x == 0 && blockIdx.x == 0) atomicOr(err, HLA_DEVERR_SLOT);
+        return;
+    }
+    const int cg = threadIdx.x & (CG - 1);
+    const uint32_t rows = (uint32_t)R_total << log2_rows;
+    const uint32_t row_mask = (1u << log2_rows) - 1u;
+    const uint8_t *src_base = active + (int64_t)src * n_units * ((int64_t)DV * 4 << log2_rows);
+    float x[kInt8PassesPack][8];
+    uint32_t out_row[kInt8PassesPack];
+    bool live[kInt8PassesPack];
+#pragma unroll
+    for (int i = 0; i < kInt8PassesPack; ++i) {
+        const uint32_t rr = (blockIdx.x * kInt8PassesPack + i) * RPP + (threadIdx.x >> LCG);
+        live[i] = rr < rows;  // uniform over a row's CG lanes
+        out_row[i] = 0;
+        if (!live[i]) continue;
+        const uint32_t p = rr >> log2_rows, r = rr & row_mask;
+        const int l = layer_of(offs, L, p);
+        int u = unit_index[p];
+        if (u < 0 || u >= n_units) {
+            if (err) atomicOr(err, HLA_DEVERR_PLAN);
+            u = 0;  // keep the lanes of the row together; the flag reports the plan
+        }
+        const float *row = reinterpret_cast<const float *>(
+            src_base + l * layer_stride + ((((int64_t)u << log2_rows) + r) * DV) * 4);
+        const f32x4 a = ld_nt(reinterpret_cast<const f32x4 *>(row + cg * 4));
+        const f32x4 b = ld_nt(reinterpret_cast<const f32x4 *>(row + DV / 2 + cg * 4));
+        x[i][0] = a.x; x[i][1] = a.y; x[i][2] = a.z; x[i][3] = a.w;
+        x[i][4] = b.x; x[i][5] = b.y; x[i][6] = b.z; x[i][7] = b.w;
+        out_row[i] = ((uint32_t)dst * (uint32_t)R_total << log2_rows) + rr;
+    }
+#pragma unroll
+    for (int i = 0; i < kInt8PassesPack; ++i) {
+        if (!live[i]) continue;
+        const float amax = max_low_lane_bits<LCG>(row_absmax8(x[i]));
+        uint32_t w0, w1;
+        const float s = encode_int8(x[i], amax, w0, w1);
+        int8_t *crow = codes + (int64_t)out_row[i] * DV;
+        st_nt(reinterpret_cast<uint32_t *>(crow + cg * 4), w0);
+        st_nt(reinterpret_cast<uint32_t *>(crow + DV / 2 + cg * 4), w1);
+        if (cg == 0) scales[out_row[i]] = s;
+    }
+}
+
+template <int DV>
+__global__ void __launch_bounds__(kCopyThreads)
+k_dasc_restore_int8(const int8_t *__restrict__ codes, const float *__restrict__ scales,
+                    int S_ckpt, int R_total, const int32_t *__restrict__ unit_pos, int L,
+                    int n_units, FastDiv units, int log2_rows,
+                    const int32_t *__restrict__ src_slot, const int32_t *__restrict__ dst_slot,
+                    int pair0, uint8_t *__restrict__ active_out, int64_t layer_stride,
+                    int S_dst, int32_t *__restrict__ err)
+{
+    constexpr int CG = DV / 8, LCG = Log2<CG>::v, RPP = kCopyThreads / CG;
+    const int n = pair0 + blockIdx.y;
+    const int src = src_slot[n], dst = dst_slot[n];
+    if (src < 0 || src >= S_ckpt || dst < 0 || dst >= S_dst) {
+        if (err && threadIdx.x == 0 && blockIdx.x == 0) atomicOr(err, HLA_DEVERR_SLOT);
+        return;
+    }
+    const int cg = threadIdx.x & (CG - 1);
+    const uint32_t rows = ((uint32_t)L * (uint32_t)n_units) << log2_rows;
+    const uint32_t row_mask = (1u << log2_rows) - 1u;
+    uint8_t *dst_base = active_out + (int64_t)dst * n_units * ((int64_t)DV * 4 << log2_rows);
+    uint32_t w0[kInt8PassesRestore], w1[kInt8PassesRestore];
+    float sc[kInt8PassesRestore];
+    float *dptr[kInt8PassesRestore];
+#pragma unroll
+    for (int i = 0; i < kInt8PassesRestore; ++i) {
+        const uint32_t rr = (blockIdx.x * kInt8PassesRestore + i) * RPP + (threadIdx.x >> LCG);
+        dptr[i] = nullptr;
+        w0[i] = w1[i] = 0u;
+        sc[i] = 0.0f;
+        if (rr >= rows) continue;
+        const uint32_t g = rr >> log2_rows, r = rr & row_mask;  // g = l * n_units + u
+        const uint32_t l = fdiv(g, units);
+        const uint32_t u = g - l * units.d;
+        const int pos = unit_pos[g];
+        if (pos >= 0) {
+            if (pos < R_total) {
+                const int64_t in_row = (((int64_t)src * R_total + pos) << log2_rows) + r;
+                const int8_t *crow = codes + in_row * DV;
+                w0[i] = ld_nt(reinterpret_cast<const uint32_t *>(crow + cg * 4));
+                w1[i] = ld_nt(reinterpret_cast<const uint32_t *>(crow + DV / 2 + cg * 4));
+                sc[i] = scales[in_row];
+            } else if (err) {
+                atomicOr(err, HLA_DEVERR_PLAN);
+            }
+        }
+        dptr[i] = reinterpret_cast<float *>(dst_base + l * layer_stride +
+                                            ((((int64_t)u << log2_rows) + r) * DV) * 4) +
+                  cg * 4;
+    }
+#pragma unroll
+    for (int i = 0; i < kInt8PassesRestore; ++i) {
+        if (!dptr[i]) continue;
+        float y[8];
+        decode_int8(w0[i], w1[i], sc[i], y);  // q * s, one FP32 rounding (0 when omitted)
+        st_nt(reinterpret_cast<f32x4 *>(dptr[i]), f32x4{y[0], y[1], y[2], y[3]});
+        st_nt(reinterpret_cast<f32x4 *>(dptr[i] + DV / 2), f32x4{y[4], y[5], y[6], y[7]});
+    }
+}
+
 } // namespace hla
 
 extern "C" {
@@ -187,6 +387,111 @@ int dasc_restore(const void *packed, int S_ckpt, int R_total, const int32_t *uni
                            (const uint8_t *)packed, S_ckpt, R_total, unit_pos, L, n_units,
                            unit_bytes, uv, un, src_slot, dst_slot, p0, (uint8_t *)active_out,
                            layer_stride_bytes, S_dst, err_flag);
+        if (hipGetLastError() != hipSuccess) return HLA_ERR_LAUNCH;
+    }
+    return HLA_OK;
+}
+
+int dasc_refresh_local(const void *scratch, int64_t scratch_layer_stride_bytes, int S_scratch,
+                       void *active, int64_t layer_stride_bytes, int S_act, int L, int n_units,
+                       int64_t unit_bytes, const int32_t *offsets, const int32_t *unit_index,
+                       int R_local, const int32_t *src_slot, const int32_t *dst_slot, int N,
+                       int32_t *err_flag, void *stream)
+{
+    // the scratch side as the "packed" operand only for the alias test; its own
+    // geometry is checked as a second active-style layout
+    int rc = hla::check_dasc(active, layer_stride_bytes, S_act, L, n_units, unit_bytes, offsets,
+                             unit_index, R_local, src_slot, dst_slot, N, scratch, 0);
+    if (rc == HLA_OK)
+        rc = hla::check_dasc(scratch, scratch_layer_stride_bytes, S_scratch, L, n_units,
+                             unit_bytes, offsets, unit_index, R_local, src_slot, dst_slot, N,
+                             active, 0);
+    if (rc == HLA_OK && N > 0 && scratch && active) {
+        const int64_t span_a = (L - 1) * layer_stride_bytes + (int64_t)S_act * n_units * unit_bytes;
+        const int64_t span_s =
+            (L - 1) * scratch_layer_stride_bytes + (int64_t)S_scratch * n_units * unit_bytes;
+        if (hla::overlaps(hla::Range{active, (size_t)span_a}, hla::Range{scratch, (size_t)span_s}))
+            rc = HLA_ERR_ALIAS;
+    }
+    if (rc != HLA_OK) return rc;
+    if (L > hla::kMaxLayers) return HLA_ERR_UNSUPPORTED;
+    if (N == 0 || R_local == 0) return HLA_OK;
+    const hla::FastDiv uv = hla::make_fastdiv((uint32_t)(unit_bytes / 16));
+    const uint64_t total = (uint64_t)R_local * uv.d;
+    const unsigned bx = (unsigned)((total + hla::kCopyThreads * hla::kCopyVecs - 1) /
+                                   (hla::kCopyThreads * hla::kCopyVecs));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int p0 = 0; p0 < N; p0 += (int)hla::kMaxGridY) {
+        const unsigned by = (unsigned)std::min<int>(N - p0, (int)hla::kMaxGridY);
+        hipLaunchKernelGGL(hla::k_dasc_copy_units, dim3(bx, by), dim3(hla::kCopyThreads), 0, st,
+                           (const uint8_t *)scratch, scratch_layer_stride_bytes, S_scratch,
+                           (uint8_t *)active, layer_stride_bytes, S_act, L, n_units, unit_bytes,
+                           uv, offsets, unit_index, R_local, src_slot, dst_slot, p0, err_flag);
+        if (hipGetLastError() != hipSuccess) return HLA_ERR_LAUNCH;
+    }
+    return HLA_OK;
+}
+
+int dasc_pack_int8(const float *active, int64_t layer_stride_bytes, int S_act, int L, int n_units,
+                   int unit_rows, int dv, const int32_t *offsets, const int32_t *unit_index,
+                   int R_total, const int32_t *src_slot, const int32_t *dst_slot, int N,
+                   int8_t *codes, float *scales, int S_ckpt, int32_t *err_flag, void *stream)
+{
+    int rc = hla::check_dasc_int8(active, layer_stride_bytes, S_act, L, n_units, unit_rows, dv,
+                                  offsets, unit_index, R_total, src_slot, dst_slot, N, codes,
+                                  scales, S_ckpt);
+    if (rc != HLA_OK) return rc;
+    if (L > hla::kMaxLayers) return HLA_ERR_UNSUPPORTED;
+    if (N == 0 || R_total == 0) return HLA_OK;
+    const int lr = hla::log2_exact(unit_rows);
+    const uint64_t rows = (uint64_t)R_total << lr;
+    const uint64_t per_block = (uint64_t)(hla::kCopyThreads / (dv / 8)) * hla::kInt8PassesPack;
+    const unsigned bx = (unsigned)((rows + per_block - 1) / per_block);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int p0 = 0; p0 < N; p0 += (int)hla::kMaxGridY) {
+        const unsigned by = (unsigned)std::min<int>(N - p0, (int)hla::kMaxGridY);
+        const dim3 grid(bx, by), block(hla::kCopyThreads);
+        if (dv == 128)
+            hipLaunchKernelGGL(hla::k_dasc_pack_int8<128>, grid, block, 0, st,
+                               (const uint8_t *)active, layer_stride_bytes, S_act, L, n_units, lr,
+                               offsets, unit_index, R_total, src_slot, dst_slot, p0, codes,
+                               scales, S_ckpt, err_flag);
+        else
+            hipLaunchKernelGGL(hla::k_dasc_pack_int8<64>, grid, block, 0, st,
+                               (const uint8_t *)active, layer_stride_bytes, S_act, L, n_units, lr,
+                               offsets, unit_index, R_total, src_slot, dst_slot, p0, codes,
+                               scales, S_ckpt, err_flag);
+        if (hipGetLastError() != hipSuccess) return HLA_ERR_LAUNCH;
+    }
+    return HLA_OK;
+}
+
+int dasc_restore_int8(const int8_t *codes, const float *scales, int S_ckpt, int R_total,
+                      const int32_t *unit_pos, int L, int n_units, int unit_rows, int dv,
+                      const int32_t *src_slot, const int32_t *dst_slot, int N, float *active_out,
+                      int64_t layer_stride_bytes, int S_dst, int32_t *err_flag, void *stream)
+{
+    int rc = hla::check_dasc_int8(active_out, layer_stride_bytes, S_dst, L, n_units, unit_rows,
+                                  dv, unit_pos, unit_pos, R_total, src_slot, dst_slot, N, codes,
+                                  scales, S_ckpt);
+    if (rc != HLA_OK || N == 0) return rc;
+    const int lr = hla::log2_exact(unit_rows);
+    const hla::FastDiv un = hla::make_fastdiv((uint32_t)n_units);
+    const uint64_t rows = ((uint64_t)L * n_units) << lr;
+    const uint64_t per_block = (uint64_t)(hla::kCopyThreads / (dv / 8)) * hla::kInt8PassesRestore;
+    const unsigned bx = (unsigned)((rows + per_block - 1) / per_block);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int p0 = 0; p0 < N; p0 += (int)hla::kMaxGridY) {
+        const unsigned by = (unsigned)std::min<int>(N - p0, (int)hla::kMaxGridY);
+        const dim3 grid(bx, by), block(hla::kCopyThreads);
+        if (dv == 128)
+            hipLaunchKernelGGL(hla::k_dasc_restore_int8<128>, grid, block, 0, st, codes, scales,
+                               S_ckpt, R_total, unit_pos, L, n_units, un, lr, src_slot, dst_slot,
+                               p0, (uint8_t *)active_out, layer_stride_bytes, S_dst, err_flag);
+        else
+            hipLaunchKernelGGL(hla::k_dasc_restore_int8<64>, grid, block, 0, st, codes, scales,
+                               S_ckpt, R_total, unit_pos, L, n_units, un, lr, src_slot, dst_slot,
+                               p0, (uint8_t *)active_out, layer_stride_bytes, S_dst, err_flag);
         if (hipGetLastError() != hipSuccess) return HLA_ERR_LAUNCH;
     }
     return HLA_OK;

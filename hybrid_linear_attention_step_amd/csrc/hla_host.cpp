@@ -1,6 +1,7 @@
 // Host-only parts of the C ABI: status strings, argument validation and the
 // ragged checkpoint plan.  Nothing here calls the HIP runtime.
 #include <limits.h>
+#include <math.h>
 #include <string.h>
 
 #include "hla.h"
@@ -175,6 +176,32 @@ int check_dasc(const void *active, int64_t layer_stride_bytes, int S_act, int L,
     return HLA_OK;
 }
 
+int check_dasc_int8(const void *active, int64_t layer_stride_bytes, int S_act, int L,
+                    int n_units, int unit_rows, int dv, const void *table_a,
+                    const void *table_b, int R_total, const int32_t *src_slot,
+                    const int32_t *dst_slot, int N, const void *codes, const void *scales,
+                    int S_ckpt)
+{
+    if (unit_rows <= 0 || unit_rows > 256 || (unit_rows & (unit_rows - 1)) != 0)
+        return HLA_ERR_SHAPE;
+    if (dv != 64 && dv != 128) return HLA_ERR_UNSUPPORTED;
+    const int64_t unit_bytes = (int64_t)unit_rows * dv * 4;
+    // the FP32 side, with the codes standing in for the packed operand (sized below)
+    int rc = check_dasc(active, layer_stride_bytes, S_act, L, n_units, unit_bytes, table_a,
+                        table_b, R_total, src_slot, dst_slot, N, codes, 0);
+    if (rc != HLA_OK || N == 0) return rc;
+    if (!scales) return HLA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(scales) & 3u) != 0) return HLA_ERR_ALIGN;
+    // checkpoint rows must fit the kernels' 32-bit row indexing
+    if ((int64_t)S_ckpt * R_total * unit_rows > (int64_t)INT_MAX) return HLA_ERR_SHAPE;
+    const int64_t layer_bytes = (int64_t)S_act * n_units * unit_bytes;
+    Range act{active, (size_t)((L - 1) * layer_stride_bytes + layer_bytes)};
+    Range cd{codes, (size_t)S_ckpt * R_total * unit_rows * dv};
+    Range sc{scales, (size_t)S_ckpt * R_total * unit_rows * sizeof(float)};
+    if (overlaps(act, cd) || overlaps(act, sc) || overlaps(cd, sc)) return HLA_ERR_ALIAS;
+    return HLA_OK;
+}
+
 } // namespace hla
 
 extern "C" {
@@ -225,6 +252,54 @@ int dasc_plan(const uint8_t *mask, int L, int n_units, int32_t *offsets, int32_t
         offsets[l + 1] = pos;
     }
     *R_total = pos;
+    return HLA_OK;
+}
+
+int dasc_static_horizon(const float *A_log, const float *d, int n, int gate, double a_s,
+                        double eps, double W_max, double *H_out, uint8_t *mask_out)
+{
+    if (n < 0) return HLA_ERR_SHAPE;
+    if (gate != HLA_GATE_SOFTPLUS && gate != HLA_GATE_BOUNDED) return HLA_ERR_UNSUPPORTED;
+    if (!(eps > 0.0 && eps < 1.0)) return HLA_ERR_SHAPE;
+    if (n == 0) return HLA_OK;
+    if (!A_log || !d || (!H_out && !mask_out)) return HLA_ERR_NULL;
+    const double log_eps = log(eps);
+    for (int u = 0; u < n; ++u) {
+        const double x = (double)a_s + (double)d[u];
+        const double scale = exp((double)A_log[u]);
+        double g;  // static one-step log-decay, < 0
+        if (gate == HLA_GATE_SOFTPLUS) {
+            const double sp = x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));
+            g = -scale * sp;
+        } else {
+            g = -5.0 / (1.0 + exp(-scale * x));
+        }
+        const double H = log_eps / g;
+        if (H_out) H_out[u] = H;
+        if (mask_out) mask_out[u] = H > W_max ? 1 : 0;
+    }
+    return HLA_OK;
+}
+
+int dasc_replay_window(const double *H, const uint8_t *mask, int n, int n_prefix, int W_max,
+                       int32_t *W_u_out, int32_t *W_replay_out)
+{
+    if (n < 0 || n_prefix < 0 || W_max < 4) return HLA_ERR_SHAPE;
+    if (!W_replay_out || (n > 0 && (!H || !mask))) return HLA_ERR_NULL;
+    int32_t longest_local = -1;
+    for (int u = 0; u < n; ++u) {
+        // next power of two at or above H (H <= 0 maps to 4), clamped to [4, W_max]
+        int64_t w = 4;
+        if (H[u] > 0.0) {
+            const double e = ceil(log2(H[u]));
+            w = e >= 62.0 ? ((int64_t)1 << 62) : e <= 0.0 ? 1 : ((int64_t)1 << (int)e);
+        }
+        if (w < 4) w = 4;
+        if (w > W_max) w = W_max;
+        if (W_u_out) W_u_out[u] = (int32_t)w;
+        if (!mask[u] && w > longest_local) longest_local = (int32_t)w;
+    }
+    *W_replay_out = longest_local < 0 ? 0 : (n_prefix < longest_local ? n_prefix : longest_local);
     return HLA_OK;
 }
 

@@ -108,4 +108,21 @@ int check_dasc(const void *active, int64_t layer_stride_bytes, int S_act, int L,
                const int32_t *src_slot, const int32_t *dst_slot, int N, const void *packed,
                int S_ckpt);
 
+// INT8 checkpoints: a unit is unit_rows (a power of two, <= 256) rows of dv
+// (64 or 128) FP32 values; codes [S_ckpt, R_total, unit_rows, dv] int8 and
+// scales [S_ckpt, R_total, unit_rows] float32.
+int check_dasc_int8(const void *active, int64_t layer_stride_bytes, int S_act, int L,
+                    int n_units, int unit_rows, int dv, const void *table_a,
+                    const void *table_b, int R_total, const int32_t *src_slot,
+                    const int32_t *dst_slot, int N, const void *codes, const void *scales,
+                    int S_ckpt);
+
+// log2 of a power of two (checked by the caller).
+inline int log2_exact(int x)
+{
+    int l = 0;
+    while ((1 << l) < x) ++l;
+    return l;
+}
+
 } // namespace hla

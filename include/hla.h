@@ -321,6 +321,79 @@ HLA_API int verify_drafts(const float *state, int n_slots, const int32_t *slot, 
                   int in_dtype, const float *alpha, int decay_kind, const float *beta,
                   void *out, int out_dtype, int32_t *err_flag, void *stream);
 
+/* -------------------------------------------------------------------------
+ * INT8-composed checkpoints ([dasc] App. E.1 Eq. (8) and App. E.2): the
+ * retained units of an FP32 temporal state are quantised once when the
+ * checkpoint is stored, one FP32 scale per key-channel row over its dv values
+ * (the row quantiser of the mixed-precision state: a = max |x|, s = max(a,
+ * 1e-8) / 127, codes clip(round(x / s), -127, 127), FP32), and dequantised
+ * once on a hit, q * s rounded once to FP32, into a fresh active slot; the
+ * omitted units of that slot read as zero (dasc-nr).
+ *
+ * A unit is unit_rows consecutive rows of dv FP32 values: unit_rows = dk for
+ * a GDN head, 1 for a KDA (head, key) channel.  unit_rows is a power of two
+ * <= 256; dv is 64 or 128.  Layer l's active state is
+ * [S, n_units, unit_rows, dv] starting layer_stride_bytes * l into active
+ * (16-byte aligned, stride a multiple of 16).
+ *   codes   device int8    [S_ckpt, R_total, unit_rows, dv] (16-byte aligned)
+ *   scales  device float32 [S_ckpt, R_total, unit_rows]
+ * Plans, slots, N, err_flag and errors as dasc_pack / dasc_restore.
+ * ---------------------------------------------------------------------- */
+HLA_API int dasc_pack_int8(const float *active, int64_t layer_stride_bytes, int S_act, int L,
+                   int n_units, int unit_rows, int dv, const int32_t *offsets,
+                   const int32_t *unit_index, int R_total, const int32_t *src_slot,
+                   const int32_t *dst_slot, int N, int8_t *codes, float *scales, int S_ckpt,
+                   int32_t *err_flag, void *stream);
+
+HLA_API int dasc_restore_int8(const int8_t *codes, const float *scales, int S_ckpt,
+                      int R_total, const int32_t *unit_pos, int L, int n_units, int unit_rows,
+                      int dv, const int32_t *src_slot, const int32_t *dst_slot, int N,
+                      float *active_out, int64_t layer_stride_bytes, int S_dst,
+                      int32_t *err_flag, void *stream);
+
+/* -------------------------------------------------------------------------
+ * Static selection ([dasc] §3.3 Eq. (2)-(3), §4.1).  Host-only, float64.
+ * For each of n units (a GDN head or a KDA (head, key) channel) with learned
+ * log-scale A_log[u] and decay bias d[u], and the model-level representative
+ * gate input a_s:
+ *   HLA_GATE_SOFTPLUS  g = -exp(A_log) * ln(1 + exp(a_s + d))
+ *   HLA_GATE_BOUNDED   g = -5 / (1 + exp(-exp(A_log) * (a_s + d)))
+ *   H = ln(eps) / g  (the pages use eps = 1e-3),
+ * and the unit is global (retained, mask 1) when H > W_max.  H_out (double
+ * [n]) and mask_out (uint8 [n]) may each be NULL, not both.  The mask feeds
+ * dasc_plan.  Errors: SHAPE for n < 0 or eps outside (0, 1), UNSUPPORTED for
+ * another gate, NULL.
+ * ---------------------------------------------------------------------- */
+enum hla_gate { HLA_GATE_SOFTPLUS = 0, HLA_GATE_BOUNDED = 1 };
+
+HLA_API int dasc_static_horizon(const float *A_log, const float *d, int n, int gate,
+                        double a_s, double eps, double W_max, double *H_out,
+                        uint8_t *mask_out);
+
+/* dasc_replay_window -- the dasc-wr refresh window ([dasc] §4.2 Eq. (7)).
+ * Host-only.  W_u = clamp(next_pow2(H_u), 4, W_max) with next_pow2(x) =
+ * 2^ceil(log2 x) for x > 0 and 4 for x <= 0; W_replay = min(n_prefix, max of
+ * W_u over the local units (mask 0)), and 0 when no unit is local.  W_u_out
+ * (int32 [n]) may be NULL.  Errors: SHAPE for W_max < 4 or negative sizes,
+ * NULL. */
+HLA_API int dasc_replay_window(const double *H, const uint8_t *mask, int n, int n_prefix,
+                       int W_max, int32_t *W_u_out, int32_t *W_replay_out);
+
+/* dasc_refresh_local -- the copy-back of dasc-wr ([dasc] §4.2): after the
+ * refresh window has been replayed from a zero-initialised scratch state,
+ * copy only the local (omitted) units of scratch slot src_slot[n] into
+ * active slot dst_slot[n]; every other unit of the active slot, the global
+ * ones included, is left as it is.  offsets / unit_index / R_local are the
+ * ragged plan of the LOCAL units, i.e. dasc_plan of the inverted selection
+ * mask.  The scratch state has the active state's unit geometry with its own
+ * layer stride and slot count.  Units, alignment, err_flag and errors as
+ * dasc_pack; ALIAS when the two states overlap. */
+HLA_API int dasc_refresh_local(const void *scratch, int64_t scratch_layer_stride_bytes,
+                       int S_scratch, void *active, int64_t layer_stride_bytes, int S_act,
+                       int L, int n_units, int64_t unit_bytes, const int32_t *offsets,
+                       const int32_t *unit_index, int R_local, const int32_t *src_slot,
+                       const int32_t *dst_slot, int N, int32_t *err_flag, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

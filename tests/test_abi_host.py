@@ -232,3 +232,86 @@ def test_dasc_plan_errors(L):
                        ctypes.byref(R)) == NULL
     assert L.dasc_plan(mask.ctypes.data, 0, 5, off.ctypes.data, idx.ctypes.data, 4, None,
                        ctypes.byref(R)) == SHAPE
+
+
+# ---------------------------------------------------------------- static selection (host)
+
+def test_static_horizon_and_mask_match_oracle(orc):
+    """The library's host horizons (float64) equal the oracle's, and the masks are
+    bit-exact, on the KDA checkpoint workload's synthetic gate parameters and on the
+    bounded gate."""
+    import synth
+
+    import hybrid_linear_attention_step_amd as hla
+
+    cfg = synth.CONFIGS["dasc_kda"]
+    A, d = synth.gate_params(cfg)
+    for gate, a_s in ((hla.GATE_SOFTPLUS, cfg.a_s), (hla.GATE_BOUNDED, 0.8)):
+        H, m = hla.dasc_static_horizon(A, d, gate, a_s, cfg.W_max)
+        Ho = orc.static_horizon(A.astype(np.float64), d.astype(np.float64), gate, a_s)
+        np.testing.assert_allclose(H, Ho, rtol=1e-15)
+        assert np.array_equal(m, orc.static_mask(Ho, cfg.W_max))
+        if gate == hla.GATE_SOFTPLUS:
+            assert 0.05 < m.mean() < 0.95  # a mixed selection, not all or nothing
+
+
+@pytest.mark.parametrize("H,mask,n_p,W_max", [
+    ([3.0, 4.0, 4.5, 9.0, 0.5], [0, 0, 0, 0, 0], 100, 16),
+    ([3.0, 9.0, 40.0], [0, 0, 1], 7, 16),
+    ([30.0, 40.0], [1, 1], 100, 16),
+    ([0.0, -1.0, 1e300], [0, 0, 0], 10 ** 6, 64),
+    ([32.0, 64.0, 33.0], [0, 0, 1], 1000, 64),
+])
+def test_replay_window_matches_oracle(orc, H, mask, n_p, W_max):
+    import hybrid_linear_attention_step_amd as hla
+
+    H, mask = np.array(H), np.array(mask, np.uint8)
+    assert hla.dasc_replay_window(H, mask, n_p, W_max)[0] == orc.replay_window(H, mask, n_p,
+                                                                                W_max)[0]
+    assert np.array_equal(hla.dasc_replay_window(H, mask, n_p, W_max)[1],
+                          orc.replay_window(H, mask, n_p, W_max)[1])
+
+
+def test_selection_and_int8_validation(L):
+    f = Fake()
+    A = (ctypes.c_float * 4)()
+    H = (ctypes.c_double * 4)()
+    m = (ctypes.c_uint8 * 4)()
+    W = ctypes.c_int32(0)
+    assert L.dasc_static_horizon(A, A, 4, 2, -0.3, 1e-3, 16.0, H, m) == UNSUP
+    assert L.dasc_static_horizon(A, A, 4, 0, -0.3, 0.0, 16.0, H, m) == SHAPE
+    assert L.dasc_static_horizon(A, A, 4, 0, -0.3, 1e-3, 16.0, None, None) == NULL
+    assert L.dasc_static_horizon(None, A, 0, 0, -0.3, 1e-3, 16.0, None, None) == OK
+    assert L.dasc_replay_window(H, m, 4, 10, 3, None, ctypes.byref(W)) == SHAPE
+    assert L.dasc_replay_window(H, m, 4, 10, 16, None, None) == NULL
+    base = dict(active=f(), stride=512 * 4096 * 512, S_act=512, L=4, n_units=4096,
+                unit_rows=1, dv=128, offsets=f(), unit_index=f(), R=4096, src=f(), dst=f(),
+                N=8, codes=f(), scales=f(), S_ckpt=8, err=None, stream=None)
+
+    def pk(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.dasc_pack_int8(*a.values())
+
+    assert pk(unit_rows=3) == SHAPE and pk(unit_rows=512) == SHAPE
+    assert pk(dv=96) == UNSUP
+    assert pk(scales=None) == NULL
+    assert pk(scales=ctypes.c_void_p(f().value + 2)) == ALIGN
+    assert pk(codes=ctypes.c_void_p(f().value + 8)) == ALIGN
+    act = f()
+    assert pk(active=act, codes=ctypes.c_void_p(act.value + 4096)) == ALIAS
+    assert pk(N=0) == OK
+    rs = dict(codes=f(), scales=f(), S_ckpt=8, R=4096, unit_pos=f(), L=4, n_units=4096,
+              unit_rows=1, dv=128, src=f(), dst=f(), N=8, out=f(), stride=512 * 4096 * 512,
+              S_dst=512, err=None, stream=None)
+    assert L.dasc_restore_int8(*dict(rs, dv=32).values()) == UNSUP
+    assert L.dasc_restore_int8(*dict(rs, unit_pos=None).values()) == NULL
+    # copy-back: the scratch and active states must not overlap
+    st = f()
+    cb = dict(scratch=st, s_stride=64 * 32 * 65536, S_s=64, active=f(), stride=512 * 32 * 65536,
+              S_act=512, L=4, n_units=32, unit_bytes=65536, offsets=f(), unit_index=f(), R=64,
+              src=f(), dst=f(), N=8, err=None, stream=None)
+    assert L.dasc_refresh_local(*dict(cb, active=ctypes.c_void_p(st.value + 65536)).values()) \
+        == ALIAS
+    assert L.dasc_refresh_local(*dict(cb, unit_bytes=65540).values()) == ALIGN
+

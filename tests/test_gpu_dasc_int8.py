@@ -1,0 +1,180 @@
+"""GPU parity of the INT8-composed checkpoints (dasc_pack_int8 / dasc_restore_int8) and
+of the dasc-wr copy-back (dasc_refresh_local) against the float64 oracle.
+
+Bars: restore and copy-back bit-exact (q * s is one FP32 rounding on both sides; copies
+are copies); pack: FP32 scales bit-exact (the same FP32 row maximum divided by 127),
+codes differ by at most 1 on at most 0.1% of values (the quantiser's rounding decision
+is taken on x * rcp(s) on the GPU and on fl(x / s) in the oracle)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import dev, host, need_gpu, torch
+
+pytestmark = pytest.mark.gpu
+CODE_FRAC = 1e-3
+
+
+def _stride(S_, n_units, unit_rows, dv):
+    return S_ * n_units * unit_rows * dv * 4
+
+
+@pytest.mark.parametrize("unit_rows,dv,n_units,p_keep", [
+    (1, 128, 40, 0.3),      # KDA channel rows
+    (1, 64, 33, 0.6),
+    (128, 128, 5, 0.5),     # GDN heads
+    (4, 64, 9, 0.7),
+])
+def test_pack_and_restore_int8(unit_rows, dv, n_units, p_keep):
+    hla = need_gpu()
+    g = np.random.default_rng(unit_rows * 100 + dv + n_units)
+    L, S_ = 3, 5
+    act = (g.standard_normal((L, S_, n_units, unit_rows, dv)) * 0.05).astype(np.float32)
+    act[0, 1, 2, 0] = 0.0                      # a zero row
+    act[2, 3, 1, 0, 7] = 25.0                  # an outlier
+    mask = (g.random((L, n_units)) < p_keep).astype(np.uint8)
+    mask[1] = 0                                # an empty layer
+    offsets, unit_index, unit_pos, R = hla.dasc_plan(mask)
+    S_ckpt = S_ + 1
+    src = g.permutation(S_)[:4].astype(np.int32)
+    dst = g.permutation(S_ckpt)[:4].astype(np.int32)
+    codes = torch.full((S_ckpt, R, unit_rows, dv), 99, dtype=torch.int8, device="cuda")
+    scales = torch.full((S_ckpt, R, unit_rows), -1.0, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hla.dasc_pack_int8(dev(act), _stride(S_, n_units, unit_rows, dv), S_, L, n_units, unit_rows,
+                       dv, dev(offsets), dev(unit_index), R, dev(src), dev(dst), codes, scales,
+                       S_ckpt, err_flag=err)
+    c_o, s_o = oracle.dasc_pack_int8(act, offsets, unit_index, src, dst, S_ckpt)
+    c_g, s_g = host(codes), host(scales)
+    for d_ in dst:
+        assert np.array_equal(s_g[d_], s_o[d_])
+        diff = np.abs(c_g[d_].astype(int) - c_o[d_].astype(int))
+        assert diff.max(initial=0) <= 1 and (diff > 0).mean() <= CODE_FRAC
+    others = [s for s in range(S_ckpt) if s not in dst]
+    assert (c_g[others] == 99).all() and (s_g[others] == -1.0).all()
+    # restore the oracle's checkpoint into sentinel-filled private slots: bit-exact
+    S_dst = S_ + 2
+    dst2 = g.permutation(S_dst)[:4].astype(np.int32)
+    out0 = np.full((L, S_dst, n_units, unit_rows, dv), 3.5, np.float32)
+    out = dev(out0)
+    hla.dasc_restore_int8(dev(c_o), dev(s_o), S_ckpt, R, dev(unit_pos.reshape(-1)), L, n_units,
+                          unit_rows, dv, dev(dst), dev(dst2), out,
+                          _stride(S_dst, n_units, unit_rows, dv), S_dst, err_flag=err)
+    ref = oracle.dasc_restore_int8(c_o, s_o, offsets, unit_index, L, n_units, dst, dst2,
+                                   out0.copy())
+    assert np.array_equal(host(out), ref)
+    assert int(err.item()) == 0
+
+
+def test_kda_checkpoint_workload_static_horizon_selection():
+    """4 layers x 512 request states x 32 heads x 128 key channels, one unit per channel
+    row (512 B), selected by static horizons (softplus gate, a_s = -0.3, W_max = 16) from
+    the synthetic gate parameters: INT8 pack of all 512 states, restore into 512 private
+    slots.  Over the whole 4 GiB state: every retained value within half a quantisation
+    step of the original (plus the rounding slack of the GPU quantiser), every omitted
+    value zero; 4 sampled pairs against the oracle."""
+    hla = need_gpu()
+    cfg = synth.CONFIGS["dasc_kda"]
+    A, d = synth.gate_params(cfg)
+    _, mask3 = hla.dasc_static_horizon(A, d, hla.GATE_SOFTPLUS, cfg.a_s, cfg.W_max)
+    mask = mask3.reshape(cfg.L, cfg.H * cfg.dk)
+    offsets, unit_index, unit_pos, R = hla.dasc_plan(mask)
+    L, S_, nu, dv = cfg.L, cfg.slots, cfg.H * cfg.dk, cfg.dv
+    gen = torch.Generator(device="cuda").manual_seed(cfg.seed)
+    act = torch.randn((L, S_, nu, dv), device="cuda", generator=gen) * 0.05
+    codes = torch.empty((S_, R, 1, dv), dtype=torch.int8, device="cuda")
+    scales = torch.empty((S_, R, 1), device="cuda")
+    ids = dev(np.arange(S_, dtype=np.int32))
+    stride = S_ * nu * dv * 4
+    hla.dasc_pack_int8(act, stride, S_, L, nu, 1, dv, dev(offsets), dev(unit_index), R, ids, ids,
+                       codes, scales, S_)
+    out = torch.full_like(act, float("nan"))
+    hla.dasc_restore_int8(codes, scales, S_, R, dev(unit_pos.reshape(-1)), L, nu, 1, dv, ids,
+                          ids, out, stride, S_)
+    keep = torch.from_numpy(mask.astype(bool)).cuda()[:, None, :, None]
+    step = act.abs().amax(-1, keepdim=True) / 127
+    # half a step, widened by the rounding decision taken on x * rcp(s) (it can fall on
+    # the other side of a half-integer within ~2e-5 of it) and the FP32 rounding of q * s
+    bound = (0.5 + 5e-5) * step + act.abs() * 2.0 ** -23
+    assert bool(((out - act).abs() <= bound)[keep.expand_as(act)].all())
+    assert bool((out[~keep.expand_as(act)] == 0).all())
+    g = np.random.default_rng(3)
+    for s in g.choice(S_, size=4, replace=False):
+        a_s = act[:, s:s + 1].cpu().numpy().reshape(L, 1, nu, 1, dv)
+        c_o, s_o = oracle.dasc_pack_int8(a_s, offsets, unit_index, np.zeros(1, np.int32),
+                                         np.zeros(1, np.int32), 1)
+        assert np.array_equal(scales[s].cpu().numpy(), s_o[0])
+        diff = np.abs(codes[s].cpu().numpy().astype(int) - c_o[0].astype(int))
+        assert diff.max() <= 1 and (diff > 0).mean() <= CODE_FRAC
+
+
+def test_refresh_local_bit_exact():
+    hla = need_gpu()
+    g = np.random.default_rng(41)
+    L, S_s, S_a, n_units, ub = 3, 4, 6, 37, 512
+    scratch = g.integers(0, 256, size=(L, S_s, n_units, ub), dtype=np.uint8)
+    active = g.integers(0, 256, size=(L, S_a, n_units, ub), dtype=np.uint8)
+    mask = (g.random((L, n_units)) < 0.4).astype(np.uint8)   # 1 = global
+    local = 1 - mask
+    offsets, unit_index, _, R_local = hla.dasc_plan(local)
+    src = np.array([2, 0, 3], np.int32)
+    dst = np.array([5, 1, 2], np.int32)
+    act_d = dev(active.reshape(-1))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hla.dasc_refresh_local(dev(scratch.reshape(-1)), S_s * n_units * ub, S_s, act_d,
+                           S_a * n_units * ub, S_a, L, n_units, ub, dev(offsets),
+                           dev(unit_index), R_local, dev(src), dev(dst), err_flag=err)
+    ref = oracle.dasc_refresh_local(scratch, active.copy(), local, src, dst)
+    assert np.array_equal(host(act_d).reshape(active.shape), ref)
+    assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_dasc_wr_flow(kind):
+    """The whole dasc-wr load path on the GPU: restore the checkpoint with zero-filled
+    local units, replay the refresh window from a zero scratch state with the ordinary
+    step, copy the refreshed local units back.  Global units end exactly at their
+    checkpoint values, local units exactly at the scratch replay's values."""
+    hla = need_gpu()
+    base = synth.CONFIGS["dasc_kda" if kind == "kda" else "dasc_gdn"]
+    cfg = synth.shrink(base, B=3, H=4, dk=64, dv=64, slots=3, L=2)
+    L, S_, H, dk, dv = cfg.L, cfg.slots, cfg.H, cfg.dk, cfg.dv
+    g = np.random.default_rng(7)
+    if kind == "kda":
+        A, d = synth.gate_params(cfg)
+        Hs, m = hla.dasc_static_horizon(A, d, hla.GATE_SOFTPLUS, cfg.a_s, cfg.W_max)
+        mask, unit_rows, n_units = m.reshape(L, H * dk), 1, H * dk
+    else:
+        Hs = g.uniform(2, 64, (L, H))
+        mask, unit_rows, n_units = (Hs > 16).astype(np.uint8), dk, H
+    ub = unit_rows * dv * 4
+    W, _ = hla.dasc_replay_window(Hs.reshape(-1), mask.reshape(-1), 48, 16)
+    assert 4 <= W <= 16
+    offsets, unit_index, unit_pos, R = hla.dasc_plan(mask)
+    lo_off, lo_idx, _, R_loc = hla.dasc_plan(1 - mask)
+    ckpt_state = (g.standard_normal((L, S_, H, dk, dv)) * 0.05).astype(np.float32)
+    ids = dev(np.arange(S_, dtype=np.int32))
+    stride = S_ * H * dk * dv * 4
+    packed = torch.empty((S_, R, ub // 4), device="cuda")
+    hla.dasc_pack(dev(ckpt_state), stride, S_, L, n_units, ub, dev(offsets), dev(unit_index), R,
+                  ids, ids, packed, S_)
+    active = torch.full((L, S_, H, dk, dv), float("nan"), device="cuda")
+    hla.dasc_restore(packed, S_, R, dev(unit_pos.reshape(-1)), L, n_units, ub, ids, ids, active,
+                     stride, S_)
+    scratch = torch.zeros_like(active)
+    step = hla.kda_step if kind == "kda" else hla.gdn_step
+    rep = synth.shrink(cfg, B=S_)
+    for t in range(W):
+        for l in range(L):
+            x = synth.step_inputs(rep, 100 * l + t)
+            xd = {n: dev(a) for n, a in x.items()}
+            step(scratch[l], xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], want_out=False)
+    hla.dasc_refresh_local(scratch, stride, S_, active, stride, S_, L, n_units, ub,
+                           dev(lo_off), dev(lo_idx), R_loc, ids, ids)
+    glob = torch.from_numpy(mask.astype(bool)).cuda()
+    shape = (L, S_, n_units, unit_rows * dv)
+    a2, c2, s2 = (active.reshape(shape), dev(ckpt_state).reshape(shape), scratch.reshape(shape))
+    gm = glob[:, None, :, None].expand(shape)
+    assert torch.equal(a2[gm], c2[gm])
+    assert torch.equal(a2[~gm], s2[~gm])
