@@ -2,8 +2,9 @@
 verify_drafts (readouts at all K draft positions, committed state only read) and
 replay_accepted_bonus (accepted drafts, then the bonus token, in one pass over the state).
 Tolerance as the FP32 step: per head tile, max|gpu - oracle| <= 1e-5 * max|oracle|.
-Bitwise checks: verify leaves the state's bits alone, its readouts equal a full-acceptance
-replay's, and the fused bonus equals replay_accepted followed by one step call."""
+Bitwise checks: verify leaves the state's bits alone and the fused bonus equals
+replay_accepted followed by one step call; verify's readouts match a full-acceptance
+replay's to the FP32 tolerance (verify evaluates the drafts in unrolled form)."""
 import numpy as np
 import pytest
 
@@ -55,7 +56,9 @@ def test_verify_matches_oracle_and_reads_only(kind, in_dtype, dk, dv):
 
 
 @pytest.mark.parametrize("kind", ["gdn", "kda"])
-def test_verify_readouts_equal_full_acceptance_replay(kind):
+def test_verify_readouts_match_full_acceptance_replay(kind):
+    """The verify pass (unrolled form) and a replay accepting every draft (token by token)
+    compute the same readouts from the same state, up to summation order."""
     hla = need_gpu()
     cfg = _cfg(kind, 128, 128, "bf16", B=8, K=8, H=4)
     x = synth.replay_inputs(cfg, 2)
@@ -64,9 +67,10 @@ def test_verify_readouts_equal_full_acceptance_replay(kind):
     xd = dev_inputs({n: x[n] for n in NAMES}, "bf16")
     dk = 1 if kind == "kda" else 0
     o_v = hla.verify_drafts(st, xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], dk)
+    assert np.array_equal(host(st), S0)
     full = dev(np.full(cfg.B, cfg.K, np.int32))
     o_r = hla.replay_accepted(st, xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], full, dk)
-    assert torch.equal(o_v, o_r)
+    assert rel_err_tiles(host(o_v), host(o_r), 1) <= 2 * TOL
 
 
 @pytest.mark.parametrize("kind", ["gdn", "kda"])
