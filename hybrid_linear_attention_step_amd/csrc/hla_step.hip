@@ -31,50 +31,6 @@
 
 namespace hla {
 
-// One token's update of a lane's tile.  x[m][c] is row (rg*RPL + m), column
-// (slice + 4*cg + c).  kk, qq, aa are this lane's rows of k, q and the decay
-// (aa[0] for a scalar decay).  Returns the readout for the lane's 4 columns
-// (valid in every lane).  Shared by the step and the replay kernels so that
-// a replay is bitwise identical to the same number of single steps.
-template <int RPL, bool VEC>
-__device__ __forceinline__ void tile_token(float (&x)[RPL][4], const float (&kk)[RPL],
-                                           const float (&qq)[RPL], const float *aa, float beta,
-                                           const float (&vv)[4], float (&o)[4])
-{
-    float r[4] = {0.f, 0.f, 0.f, 0.f};
-    float p[4] = {0.f, 0.f, 0.f, 0.f};
-    float qk = 0.f;
-#pragma unroll
-    for (int m = 0; m < RPL; ++m) {
-        const float a = VEC ? aa[m] : aa[0];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            x[m][c] = x[m][c] * a;                 // S' = Lambda S
-            r[c] = fmaf(kk[m], x[m][c], r[c]);     // partial (S'^T k)_j
-            p[c] = fmaf(qq[m], x[m][c], p[c]);     // partial (S'^T q)_j
-        }
-        qk = fmaf(qq[m], kk[m], qk);
-    }
-    // Sum the 8 row blocks: lane bits 3..5.
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        r[c] = sum_lane_bits<3>(r[c]);
-        p[c] = sum_lane_bits<3>(p[c]);
-    }
-    qk = sum_lane_bits<3>(qk);
-    float u[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        u[c] = beta * (vv[c] - r[c]);   // u = beta (v - S'^T k)
-        o[c] = fmaf(qk, u[c], p[c]);    // o = S'^T q + (q.k) u = S^T q
-    }
-#pragma unroll
-    for (int m = 0; m < RPL; ++m)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            x[m][c] = fmaf(kk[m], u[c], x[m][c]);  // S = S' + k u^T
-}
-
 template <int RPL>
 __device__ __forceinline__ void tile_load(const float *S, int DV, float (&x)[RPL][4])
 {
@@ -97,8 +53,7 @@ __device__ __forceinline__ void tile_store(float *S, int DV, const float (&x)[RP
 
 // One token's per-lane inputs as loaded (raw 16-byte words): rows
 // [row0, row0+RPL) of q, k and of a vector decay, the lane's 4 columns of v,
-// the scalar decay and beta.  Loading and converting are separate steps so
-// that the bf16 unpacking (which waits for the data) can be scheduled after
+// the scalar decay and beta.  Values are unpacked where they are used, after
 // the state loads have been issued.
 template <int DK, typename TIn, bool VEC>
 struct TokenRaw {
@@ -138,51 +93,96 @@ __device__ __forceinline__ void token_load(const TIn *q, const TIn *k, const TIn
     R.b0 = beta[tok];
 }
 
-template <int DK, typename TIn, bool VEC>
-__device__ __forceinline__ void token_convert(const TokenRaw<DK, TIn, VEC> &R, float (&qq)[DK / 8],
-                                              float (&kk)[DK / 8], float (&aa)[VEC ? DK / 8 : 1],
-                                              float (&vv)[4], float &bt)
+// The lane's 4 columns of v as floats.
+template <typename TIn>
+__device__ __forceinline__ void token_v(const u32x2 &v2, const u32x4 &v4, float (&vv)[4])
 {
-    using TR = TokenRaw<DK, TIn, VEC>;
-#pragma unroll
-    for (int i = 0; i < TR::QW; ++i) {
-        if constexpr (sizeof(TIn) == 2) {
-            const uint32_t kw[4] = {R.k[i].x, R.k[i].y, R.k[i].z, R.k[i].w};
-            const uint32_t qw[4] = {R.q[i].x, R.q[i].y, R.q[i].z, R.q[i].w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                kk[8 * i + 2 * j] = bf16_lo(kw[j]);
-                kk[8 * i + 2 * j + 1] = bf16_hi(kw[j]);
-                qq[8 * i + 2 * j] = bf16_lo(qw[j]);
-                qq[8 * i + 2 * j + 1] = bf16_hi(qw[j]);
-            }
-        } else {
-            kk[4 * i + 0] = __uint_as_float(R.k[i].x); kk[4 * i + 1] = __uint_as_float(R.k[i].y);
-            kk[4 * i + 2] = __uint_as_float(R.k[i].z); kk[4 * i + 3] = __uint_as_float(R.k[i].w);
-            qq[4 * i + 0] = __uint_as_float(R.q[i].x); qq[4 * i + 1] = __uint_as_float(R.q[i].y);
-            qq[4 * i + 2] = __uint_as_float(R.q[i].z); qq[4 * i + 3] = __uint_as_float(R.q[i].w);
-        }
-    }
-    if constexpr (VEC) {
-#pragma unroll
-        for (int i = 0; i < TR::RPL / 4; ++i) {
-            aa[4 * i + 0] = __uint_as_float(R.a[i].x); aa[4 * i + 1] = __uint_as_float(R.a[i].y);
-            aa[4 * i + 2] = __uint_as_float(R.a[i].z); aa[4 * i + 3] = __uint_as_float(R.a[i].w);
-        }
-    } else {
-        aa[0] = R.a0;
-    }
     if constexpr (sizeof(TIn) == 2) {
-        vv[0] = bf16_lo(R.v2.x); vv[1] = bf16_hi(R.v2.x); vv[2] = bf16_lo(R.v2.y); vv[3] = bf16_hi(R.v2.y);
+        vv[0] = bf16_lo(v2.x); vv[1] = bf16_hi(v2.x); vv[2] = bf16_lo(v2.y); vv[3] = bf16_hi(v2.y);
     } else {
-        vv[0] = __uint_as_float(R.v4.x); vv[1] = __uint_as_float(R.v4.y);
-        vv[2] = __uint_as_float(R.v4.z); vv[3] = __uint_as_float(R.v4.w);
+        vv[0] = __uint_as_float(v4.x); vv[1] = __uint_as_float(v4.y);
+        vv[2] = __uint_as_float(v4.z); vv[3] = __uint_as_float(v4.w);
     }
-    bt = R.b0;
 }
+
+// Row m of the lane's k or q block as loaded (the 16-byte words of
+// TokenRaw), converted at the point of use: a bf16 pair shares one register
+// until it is needed, which keeps the step's register count low enough for
+// five waves per SIMD with bf16 inputs.
+template <typename TIn, int QW>
+__device__ __forceinline__ float raw_row(const u32x4 (&w)[QW], int m)
+{
+    if constexpr (sizeof(TIn) == 2) {
+        const u32x4 &t = w[m / 8];
+        const int c = (m % 8) / 2;
+        const uint32_t word = c == 0 ? t.x : c == 1 ? t.y : c == 2 ? t.z : t.w;
+        return (m & 1) ? bf16_hi(word) : bf16_lo(word);
+    } else {
+        const u32x4 &t = w[m / 4];
+        const int c = m % 4;
+        return __uint_as_float(c == 0 ? t.x : c == 1 ? t.y : c == 2 ? t.z : t.w);
+    }
+}
+
+// One token's update of a lane's tile.  x[m][c] is row (rg*RPL + m), column
+// (slice + 4*cg + c); k, q and a per-channel decay are read from the token's
+// raw words row by row.  Returns the readout for the lane's 4 columns (valid
+// in every lane).  Shared by the step and the replay kernels so that a replay
+// is bitwise identical to the same number of single steps.
+template <int DK, typename TIn, bool VEC>
+__device__ __forceinline__ void tile_token_raw(float (&x)[DK / 8][4],
+                                               const TokenRaw<DK, TIn, VEC> &R,
+                                               const float (&vv)[4], float beta, float (&o)[4])
+{
+    constexpr int RPL = DK / 8, QW = TokenRaw<DK, TIn, VEC>::QW;
+    float r[4] = {0.f, 0.f, 0.f, 0.f};
+    float p[4] = {0.f, 0.f, 0.f, 0.f};
+    float qk = 0.f;
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+        float a = R.a0;
+        if constexpr (VEC) a = raw_row<float, RPL / 4>(R.a, m);
+        const float km = raw_row<TIn, QW>(R.k, m), qm = raw_row<TIn, QW>(R.q, m);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            x[m][c] = x[m][c] * a;             // S' = Lambda S
+            r[c] = fmaf(km, x[m][c], r[c]);    // partial (S'^T k)_j
+            p[c] = fmaf(qm, x[m][c], p[c]);    // partial (S'^T q)_j
+        }
+        qk = fmaf(qm, km, qk);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        r[c] = sum_lane_bits<3>(r[c]);
+        p[c] = sum_lane_bits<3>(p[c]);
+    }
+    qk = sum_lane_bits<3>(qk);
+    float u[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        u[c] = beta * (vv[c] - r[c]);   // u = beta (v - S'^T k)
+        o[c] = fmaf(qk, u[c], p[c]);    // o = S'^T q + (q.k) u = S^T q
+    }
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+        const float km = raw_row<TIn, QW>(R.k, m);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[m][c] = fmaf(km, u[c], x[m][c]);  // S = S' + k u^T
+    }
+}
+
+// Waves per SIMD the step is compiled for: with bf16 inputs and a scalar
+// decay the tile, the raw k / q words and the rest fit 96 VGPRs, i.e. five
+// waves per SIMD instead of four (measured faster); otherwise the compiler's
+// default (four at 128 x 128).
+template <int DK, typename TIn, bool VEC>
+struct StepWaves {
+    static constexpr int v = (DK == 128 && sizeof(TIn) == 2 && !VEC) ? 5 : 1;
+};
 
 template <int DK, int DV, typename TIn, typename TOut, bool VEC>
 __global__ void __launch_bounds__(2 * DV)
+__attribute__((amdgpu_waves_per_eu(StepWaves<DK, TIn, VEC>::v)))
 k_delta_step(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slot, int H,
              const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
              const float *__restrict__ alpha, const float *__restrict__ beta,
@@ -206,10 +206,10 @@ k_delta_step(float *__restrict__ state, int n_slots, const int32_t *__restrict__
     token_load<DK, DV, TIn, VEC>(q, k, v, alpha, beta, (size_t)bh, row0, col0, raw);
     float x[RPL][4];
     tile_load<RPL>(S, DV, x);
-    float kk[RPL], qq[RPL], aa[VEC ? RPL : 1], vv[4], bt;
-    token_convert<DK, TIn, VEC>(raw, qq, kk, aa, vv, bt);
+    float vv[4];
+    token_v<TIn>(raw.v2, raw.v4, vv);
     float o[4];
-    tile_token<RPL, VEC>(x, kk, qq, aa, bt, vv, o);
+    tile_token_raw<DK, TIn, VEC>(x, raw, vv, raw.b0, o);
     tile_store<RPL>(S, DV, x);
     if (out && rg == 0) store_out4(out + (size_t)bh * DV + col0, o);
 }
@@ -257,19 +257,19 @@ k_tokens(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
         const size_t tok = ((size_t)b * K + t) * H + h;
         TokenRaw<DK, TIn, VEC> raw;
         token_load<DK, DV, TIn, VEC>(q, k, v, alpha, beta, tok, row0, col0, raw);
-        float kk[RPL], qq[RPL], aa[VEC ? RPL : 1], vv[4], bt;
-        token_convert<DK, TIn, VEC>(raw, qq, kk, aa, vv, bt);
+        float vv[4];
+        token_v<TIn>(raw.v2, raw.v4, vv);
         float o[4];
-        tile_token<RPL, VEC>(x, kk, qq, aa, bt, vv, o);
+        tile_token_raw<DK, TIn, VEC>(x, raw, vv, raw.b0, o);
         if (out && rg == 0) store_out4(out + tok * DV + col0, o);
     }
     if constexpr (MODE == MODE_BONUS) {
         TokenRaw<DK, TIn, VEC> raw;
         token_load<DK, DV, TIn, VEC>(qb, kb, vb, alpha_b, beta_b, (size_t)bh, row0, col0, raw);
-        float kk[RPL], qq[RPL], aa[VEC ? RPL : 1], vv[4], bt;
-        token_convert<DK, TIn, VEC>(raw, qq, kk, aa, vv, bt);
+        float vv[4];
+        token_v<TIn>(raw.v2, raw.v4, vv);
         float o[4];
-        tile_token<RPL, VEC>(x, kk, qq, aa, bt, vv, o);
+        tile_token_raw<DK, TIn, VEC>(x, raw, vv, raw.b0, o);
         if (out_b && rg == 0) store_out4(out_b + (size_t)bh * DV + col0, o);
     }
     tile_store<RPL>(S, DV, x);

@@ -83,3 +83,54 @@ def test_replay_accepted_graph_replays():
                             x["n_accept"], 0, out=o)
 
     _check_replays(launch, [st_e, out_e], [st_g, out_g])
+
+
+def test_verify_and_bonus_graph_replays():
+    hla = need_gpu()
+    cfg = synth.shrink(synth.CONFIGS["dasc_gdn"], B=5, H=3, decay="vector")
+    x = {k: dev(v) for k, v in synth.replay_inputs(cfg, 1).items()}
+    xb = {k: dev(v) for k, v in synth.step_inputs(cfg, 30_000).items()}
+    S0 = synth.initial_state(cfg)
+    st_e, st_g = dev(S0), dev(S0)
+    ov_e = torch.zeros((cfg.B, cfg.K, cfg.H, cfg.dv), device="cuda")
+    ov_g = torch.zeros_like(ov_e)
+    ob_e = torch.zeros((cfg.B, cfg.H, cfg.dv), device="cuda")
+    ob_g = torch.zeros_like(ob_e)
+
+    def launch(state, i):
+        eager = state[0] is st_e
+        st = state[0]
+        hla.verify_drafts(st, x["q"], x["k"], x["v"], x["alpha"], x["beta"], 1,
+                          out=ov_e if eager else ov_g)
+        hla.replay_accepted_bonus(st, x["q"], x["k"], x["v"], x["alpha"], x["beta"],
+                                  x["n_accept"], 1, xb["q"], xb["k"], xb["v"], xb["alpha"],
+                                  xb["beta"], out_bonus=ob_e if eager else ob_g)
+
+    _check_replays(launch, [st_e, ov_e, ob_e], [st_g, ov_g, ob_g])
+
+
+def test_dasc_int8_graph_replays():
+    hla = need_gpu()
+    import numpy as np
+
+    g = np.random.default_rng(5)
+    L, S_, n_units, dv = 2, 3, 24, 128
+    act = dev((g.standard_normal((L, S_, n_units, 1, dv)) * 0.05).astype(np.float32))
+    mask = (g.random((L, n_units)) < 0.5).astype(np.uint8)
+    offsets, unit_index, unit_pos, R = hla.dasc_plan(mask)
+    ids = dev(np.arange(S_, dtype=np.int32))
+    stride = S_ * n_units * dv * 4
+    tabs = [dev(offsets), dev(unit_index), dev(unit_pos.reshape(-1))]
+    bufs = {}
+    for side in ("e", "g"):
+        bufs[side] = [torch.zeros((S_, R, 1, dv), dtype=torch.int8, device="cuda"),
+                      torch.zeros((S_, R, 1), device="cuda"), torch.zeros_like(act)]
+
+    def launch(state, i):
+        codes, scales, out = state
+        hla.dasc_pack_int8(act, stride, S_, L, n_units, 1, dv, tabs[0], tabs[1], R, ids, ids,
+                           codes, scales, S_)
+        hla.dasc_restore_int8(codes, scales, S_, R, tabs[2], L, n_units, 1, dv, ids, ids, out,
+                              stride, S_)
+
+    _check_replays(launch, bufs["e"], bufs["g"])
