@@ -31,23 +31,44 @@
 
 namespace hla {
 
+// The tile is read through a buffer resource over the head (scalar registers:
+// base, size) with one 32-bit per-lane byte offset and the row offset in the
+// scalar offset operand, so no 64-bit per-lane pointer is kept live across
+// the token (registers are what limits waves per SIMD here), and any read
+// outside the head's dk*dv*4 bytes would be dropped by the hardware range
+// check.  Word 3 of the descriptor is the raw-buffer format used on
+// gfx9-family GPUs; cache policy: nontemporal.  The tile is written back with
+// ordinary global nontemporal stores, whose addresses are formed only after
+// the token's arithmetic (the buffer form of the store gave wrong values in
+// part of the tile and is not used).
+constexpr int kBufNt = 2;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const float *head, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(head), (short)0, bytes,
+                                             0x00020000);
+}
+
 template <int RPL>
-__device__ __forceinline__ void tile_load(const float *S, int DV, float (&x)[RPL][4])
+__device__ __forceinline__ void tile_load(__amdgpu_buffer_rsrc_t rsrc, uint32_t off_bytes, int DV,
+                                          float (&x)[RPL][4])
 {
 #pragma unroll
     for (int m = 0; m < RPL; ++m) {
-        f32x4 t = ld_nt(reinterpret_cast<const f32x4 *>(S + (size_t)m * DV));
-        x[m][0] = t.x; x[m][1] = t.y; x[m][2] = t.z; x[m][3] = t.w;
+        const auto t = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off_bytes, m * DV * 4, kBufNt);
+        x[m][0] = __uint_as_float(t[0]); x[m][1] = __uint_as_float(t[1]);
+        x[m][2] = __uint_as_float(t[2]); x[m][3] = __uint_as_float(t[3]);
     }
 }
 
 template <int RPL>
-__device__ __forceinline__ void tile_store(float *S, int DV, const float (&x)[RPL][4])
+__device__ __forceinline__ void tile_store(float *head, uint32_t off_bytes, int DV,
+                                           const float (&x)[RPL][4])
 {
 #pragma unroll
     for (int m = 0; m < RPL; ++m) {
         f32x4 t = {x[m][0], x[m][1], x[m][2], x[m][3]};
-        st_nt(reinterpret_cast<f32x4 *>(S + (size_t)m * DV), t);
+        st_nt(reinterpret_cast<f32x4 *>(head + (size_t)m * DV + off_bytes / 4), t);
     }
 }
 
@@ -177,7 +198,7 @@ __device__ __forceinline__ void tile_token_raw(float (&x)[DK / 8][4],
 // default (four at 128 x 128).
 template <int DK, typename TIn, bool VEC>
 struct StepWaves {
-    static constexpr int v = (DK == 128 && sizeof(TIn) == 2 && !VEC) ? 5 : 1;
+    static constexpr int v = (DK == 128 && sizeof(TIn) == 2) ? 5 : 1;
 };
 
 template <int DK, int DV, typename TIn, typename TOut, bool VEC>
@@ -197,21 +218,29 @@ k_delta_step(float *__restrict__ state, int n_slots, const int32_t *__restrict__
         if (err && threadIdx.x == 0) atomicOr(err, HLA_DEVERR_SLOT);
         return;
     }
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x) >> 6;  // uniform
     const int cg = lane & 7, rg = lane >> 3;
     const int col0 = wave * 32 + cg * 4, row0 = rg * RPL;
-    float *S = state + ((size_t)s * H + h) * (DK * DV) + (size_t)row0 * DV + col0;
+    float *head_ptr = state + ((size_t)s * H + h) * (DK * DV);
+    const __amdgpu_buffer_rsrc_t head = head_rsrc(head_ptr, DK * DV * 4);
+    const uint32_t off = (uint32_t)(row0 * DV + col0) * 4;
 
     TokenRaw<DK, TIn, VEC> raw;
     token_load<DK, DV, TIn, VEC>(q, k, v, alpha, beta, (size_t)bh, row0, col0, raw);
     float x[RPL][4];
-    tile_load<RPL>(S, DV, x);
+    tile_load<RPL>(head, off, DV, x);
     float vv[4];
     token_v<TIn>(raw.v2, raw.v4, vv);
     float o[4];
     tile_token_raw<DK, TIn, VEC>(x, raw, vv, raw.b0, o);
-    tile_store<RPL>(S, DV, x);
-    if (out && rg == 0) store_out4(out + (size_t)bh * DV + col0, o);
+    tile_store<RPL>(head_ptr, off, DV, x);
+    if (out) {
+        // the lane index again from the hardware counter rather than kept in a
+        // register through the token (registers decide the waves per SIMD)
+        const int ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        if ((ln >> 3) == 0) store_out4(out + (size_t)bh * DV + wave * 32 + (ln & 7) * 4, o);
+    }
 }
 
 // Several tokens per (request, head) with the tile held in registers
@@ -249,10 +278,12 @@ k_tokens(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int cg = lane & 7, rg = lane >> 3;
     const int col0 = wave * 32 + cg * 4, row0 = rg * RPL;
-    float *S = state + ((size_t)s * H + h) * (DK * DV) + (size_t)row0 * DV + col0;
+    float *head_ptr = state + ((size_t)s * H + h) * (DK * DV);
+    const __amdgpu_buffer_rsrc_t head = head_rsrc(head_ptr, DK * DV * 4);
+    const uint32_t off = (uint32_t)(row0 * DV + col0) * 4;
 
     float x[RPL][4];
-    tile_load<RPL>(S, DV, x);
+    tile_load<RPL>(head, off, DV, x);
     for (int t = 0; t < n; ++t) {
         const size_t tok = ((size_t)b * K + t) * H + h;
         TokenRaw<DK, TIn, VEC> raw;
@@ -272,7 +303,7 @@ k_tokens(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
         tile_token_raw<DK, TIn, VEC>(x, raw, vv, raw.b0, o);
         if (out_b && rg == 0) store_out4(out_b + (size_t)bh * DV + col0, o);
     }
-    tile_store<RPL>(S, DV, x);
+    tile_store<RPL>(head_ptr, off, DV, x);
 }
 
 // ----------------------------------------------------------------- verify
