@@ -15,7 +15,8 @@ LIB = os.path.join(PKG, "libhla.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["hla_host.cpp", "hla_step.hip", "hla_damp.hip", "hla_damp_sr.hip", "hla_dasc.hip"]
+SOURCES = ["hla_host.cpp", "hla_step.hip", "hla_verify.hip", "hla_damp.hip", "hla_damp_sr.hip",
+           "hla_dasc.hip"]
 HEADERS = ["hla_device.h", "hla_internal.h", "hla_damp_kernels.h", "hla_codec.h"]
 
 FLAGS = [

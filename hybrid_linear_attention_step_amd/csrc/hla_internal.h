@@ -60,6 +60,10 @@ struct StepArgs {
 // Returns HLA_OK or the first error found.
 int check_step(const StepArgs &a);
 
+// Launches the verify pass (MODE_VERIFY) for arguments that passed check_step
+// with B > 0; `stream` is a hipStream_t.  Defined with its kernel in hla_verify.hip.
+int run_verify(const StepArgs &a, int32_t *err, void *stream);
+
 struct DampArgs {
     uint16_t *hi;
     int8_t *lo;

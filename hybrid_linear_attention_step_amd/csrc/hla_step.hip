@@ -1,7 +1,7 @@
 // gfx950 kernels for the FP32 gated delta-rule step (GDN scalar decay, KDA
 // per-key-channel decay) and for several tokens per launch: the replay of
-// accepted draft tokens (optionally followed by the bonus token) and the
-// verify pass over all drafts.
+// accepted draft tokens (optionally followed by the bonus token).  The verify
+// pass over all drafts has its own kernel (hla_verify.hip).
 //
 // Operation ("DAMP: Decay-Aware Mixed-Precision Recurrent-State
 // Quantization", §3.1 Eq. (1)-(2)), per (request, head), state S in dk x dv:
@@ -306,231 +306,6 @@ k_tokens(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
     tile_store<RPL>(head_ptr, off, DV, x);
 }
 
-// ----------------------------------------------------------------- verify
-//
-// The verify pass needs the readouts at all K draft positions but never the
-// updated state, so it is evaluated in unrolled form instead of token by
-// token.  With c_t = prod_{s<=t} a_s (cumulative decay, per key channel) and
-// w_st = prod_{s<r<=t} a_r, the recurrence S'_t = Lambda_t S_{t-1},
-// u_t = beta_t (v_t - S'_t^T k_t), S_t = S'_t + k_t u_t^T unrolls to
-//     S'_t = diag(c_t) S_0 + sum_{s<t} diag(w_st) k_s u_s^T, so
-//     u_t = beta_t (v_t - S_0^T (c_t k_t) - sum_{s<t} G_st u_s),
-//     o_t = S_t^T q_t = S_0^T (c_t q_t) + sum_{s<t} E_st u_s + E_tt u_t,
-// with the scalars G_st = sum_i k_s,i w_st,i k_t,i and E_st = sum_i k_s,i
-// w_st,i q_t,i (E_tt = k_t . q_t).  The state then costs two FMAs per
-// element per draft (S_0^T (c_t k_t) and S_0^T (c_t q_t)) instead of four
-// (decay, two sums, rank-1 write); the corrections are O(K^2 dk) per head
-// and the solve O(K^2) per column.  The results equal the token-by-token
-// recurrence up to rounding (a different summation order).
-//
-// Phases per head (workgroup of dv/32 waves, the step's column-slice tile):
-//   1. stage the K drafts' k, q, decay into LDS, form c_t k_t and c_t q_t
-//      (one thread per key channel walks the drafts);
-//   2. (the tile loads are issued right after the staging loads) the pair
-//      sums G_st, E_st are formed while the tile arrives
-//      over chunks of key channels (the products w_st are built incrementally,
-//      never as a ratio of cumulative decays, so tiny decays cannot divide by
-//      an underflowed product);
-//   3. per draft: two FMAs per element, column sums over the 8 row blocks,
-//      S_0^T (c k) and S_0^T (c q) of each column to LDS;
-//   4. one thread per column solves the K drafts in order and writes o_t.
-constexpr int kPairChunks = 16;  // key-channel chunks of the pair sums
-constexpr int kMaxDrafts = 16;   // the entry points accept 1 <= K <= 16
-
-template <int DK, int DV, bool VEC>
-struct VerifyLds {
-    // float offsets into the dynamic LDS block for K drafts
-    int k, q, a, v, b, xk, xq, r0, p0, pg, pe;
-    int total;  // floats
-    __host__ __device__ VerifyLds(int K)
-    {
-        k = 0;
-        q = k + K * DK;
-        a = q + K * DK;
-        v = a + (VEC ? K * DK : 16);
-        b = v + K * DV;
-        xk = b + 16;
-        xq = xk + K * DK;
-        r0 = xq + K * DK;
-        p0 = r0 + K * DV;
-        pg = p0 + K * DV;
-        pe = pg + K * K * kPairChunks;
-        total = pe + K * K * kPairChunks;
-    }
-};
-
-template <int DK, int DV, typename TIn, typename TOut, bool VEC>
-__global__ void __launch_bounds__(2 * DV)
-k_verify(const float *__restrict__ state, int n_slots, const int32_t *__restrict__ slot, int H,
-         int K, const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
-         const float *__restrict__ alpha, const float *__restrict__ beta, TOut *__restrict__ out,
-         int32_t *__restrict__ err)
-{
-    constexpr int NT = 2 * DV, RPL = DK / 8, CH = DK / kPairChunks;
-    extern __shared__ f32x4 verify_lds[];
-    float *L = reinterpret_cast<float *>(verify_lds);
-    const VerifyLds<DK, DV, VEC> at(K);
-    const int bh = blockIdx.x;
-    const int b = bh / H, h = bh - b * H;
-    const int s = slot ? slot[b] : b;
-    if (s < 0) return;  // uniform over the workgroup
-    if (s >= n_slots) {
-        if (err && threadIdx.x == 0) atomicOr(err, HLA_DEVERR_SLOT);
-        return;
-    }
-    const size_t tok0 = (size_t)b * K * H + h;  // draft t is token tok0 + t * H
-    const int tid = threadIdx.x;
-
-    // 1. stage the drafts' k, q, decay, v and beta (every load issued before the
-    //    first LDS write); then c_t k_t and c_t q_t, one thread per key channel
-    constexpr int JK = kMaxDrafts * DK / NT, JV = kMaxDrafts * DV / NT;
-    float rk[JK], rq[JK], ra[JK], rv[JV];
-#pragma unroll
-    for (int j = 0; j < JK; ++j) {
-        const int e = tid + j * NT, t = e / DK, i = e - t * DK;
-        rk[j] = rq[j] = ra[j] = 0.0f;
-        if (t < K) {
-            const size_t g = (tok0 + (size_t)t * H) * DK + i;
-            rk[j] = load_one(k + g);
-            rq[j] = load_one(q + g);
-            if (VEC) ra[j] = alpha[g];
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < JV; ++j) {
-        const int e = tid + j * NT, t = e / DV, i = e - t * DV;
-        rv[j] = t < K ? load_one(v + (tok0 + (size_t)t * H) * DV + i) : 0.0f;
-    }
-    const float rb = tid < K ? beta[tok0 + (size_t)tid * H] : 0.0f;
-    const float rs = !VEC && tid < K ? alpha[tok0 + (size_t)tid * H] : 0.0f;
-    // the tile (read only), issued after the staging loads so that waiting for
-    // those does not wait for it
-    const int lane = tid & 63, wave = tid >> 6;
-    const int cg = lane & 7, rg = lane >> 3;
-    const int col0 = wave * 32 + cg * 4, row0 = rg * RPL;
-    const float *S = state + ((size_t)s * H + h) * (DK * DV) + (size_t)row0 * DV + col0;
-    float x[RPL][4];
-#pragma unroll
-    for (int m = 0; m < RPL; ++m) {
-        const f32x4 t4 = ld_nt(reinterpret_cast<const f32x4 *>(S + (size_t)m * DV));
-        x[m][0] = t4.x; x[m][1] = t4.y; x[m][2] = t4.z; x[m][3] = t4.w;
-    }
-#pragma unroll
-    for (int j = 0; j < JK; ++j) {
-        const int e = tid + j * NT;
-        if (e < K * DK) {
-            L[at.k + e] = rk[j];
-            L[at.q + e] = rq[j];
-            if (VEC) L[at.a + e] = ra[j];
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < JV; ++j) {
-        const int e = tid + j * NT;
-        if (e < K * DV) L[at.v + e] = rv[j];
-    }
-    if (tid < K) {
-        L[at.b + tid] = rb;
-        if (!VEC) L[at.a + tid] = rs;
-    }
-    __syncthreads();
-    for (int i = tid; i < DK; i += NT) {
-        float c = 1.0f;
-        for (int t = 0; t < K; ++t) {
-            c *= VEC ? L[at.a + t * DK + i] : L[at.a + t];
-            L[at.xk + t * DK + i] = c * L[at.k + t * DK + i];
-            L[at.xq + t * DK + i] = c * L[at.q + t * DK + i];
-        }
-    }
-
-    // 2. the pair sums while the tile arrives
-    for (int it = tid; it < K * kPairChunks; it += NT) {
-        const int s0 = it / kPairChunks, ch = it - s0 * kPairChunks;
-        const int i0 = ch * CH;
-        float ks[CH], w[CH];
-        float e_ss = 0.0f;
-#pragma unroll
-        for (int m = 0; m < CH; ++m) {
-            ks[m] = L[at.k + s0 * DK + i0 + m];
-            w[m] = 1.0f;
-            e_ss = fmaf(ks[m], L[at.q + s0 * DK + i0 + m], e_ss);
-        }
-        L[at.pe + (s0 * K + s0) * kPairChunks + ch] = e_ss;
-        for (int t = s0 + 1; t < K; ++t) {
-            float g = 0.0f, e2 = 0.0f;
-#pragma unroll
-            for (int m = 0; m < CH; ++m) {
-                w[m] *= VEC ? L[at.a + t * DK + i0 + m] : L[at.a + t];
-                const float kw = ks[m] * w[m];
-                g = fmaf(kw, L[at.k + t * DK + i0 + m], g);
-                e2 = fmaf(kw, L[at.q + t * DK + i0 + m], e2);
-            }
-            L[at.pg + (s0 * K + t) * kPairChunks + ch] = g;
-            L[at.pe + (s0 * K + t) * kPairChunks + ch] = e2;
-        }
-    }
-    __syncthreads();  // c k, c q and the pair partials are complete
-
-    // 3. S_0^T (c_t k_t) and S_0^T (c_t q_t) per column, two FMAs per element
-    for (int t = 0; t < K; ++t) {
-        float r[4] = {0.f, 0.f, 0.f, 0.f}, p[4] = {0.f, 0.f, 0.f, 0.f};
-        const float *xk = L + at.xk + t * DK + row0;
-        const float *xq = L + at.xq + t * DK + row0;
-#pragma unroll
-        for (int m = 0; m < RPL; m += 4) {
-            const f32x4 kv = *reinterpret_cast<const f32x4 *>(xk + m);
-            const f32x4 qv = *reinterpret_cast<const f32x4 *>(xq + m);
-            const float kk[4] = {kv.x, kv.y, kv.z, kv.w}, qq[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    r[c] = fmaf(kk[j], x[m + j][c], r[c]);
-                    p[c] = fmaf(qq[j], x[m + j][c], p[c]);
-                }
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            r[c] = sum_lane_bits<3>(r[c]);
-            p[c] = sum_lane_bits<3>(p[c]);
-        }
-        if (rg == 0) {
-            *reinterpret_cast<f32x4 *>(L + at.r0 + t * DV + col0) = f32x4{r[0], r[1], r[2], r[3]};
-            *reinterpret_cast<f32x4 *>(L + at.p0 + t * DV + col0) = f32x4{p[0], p[1], p[2], p[3]};
-        }
-    }
-    // pair sums: chunk partials -> G_st, E_st (kept in chunk 0's slot)
-    for (int it = tid; it < K * K; it += NT) {
-        const int s0 = it / K, t = it - s0 * K;
-        if (t < s0) continue;
-        float g = 0.0f, e2 = 0.0f;
-        for (int ch = 0; ch < kPairChunks; ++ch) {
-            if (t > s0) g += L[at.pg + it * kPairChunks + ch];
-            e2 += L[at.pe + it * kPairChunks + ch];
-        }
-        L[at.pg + it * kPairChunks] = g;
-        L[at.pe + it * kPairChunks] = e2;
-    }
-    __syncthreads();
-
-    // 4. one thread per column: the drafts in order
-    if (tid < DV) {
-        float u[16];
-        for (int t = 0; t < K; ++t) {
-            float r = L[at.r0 + t * DV + tid];
-            float o = L[at.p0 + t * DV + tid];
-            for (int s1 = 0; s1 < t; ++s1) {
-                r = fmaf(L[at.pg + (s1 * K + t) * kPairChunks], u[s1], r);
-                o = fmaf(L[at.pe + (s1 * K + t) * kPairChunks], u[s1], o);
-            }
-            const float ut = L[at.b + t] * (L[at.v + t * DV + tid] - r);  // u = beta (v - r)
-            u[t] = ut;
-            o = fmaf(L[at.pe + (t * K + t) * kPairChunks], ut, o);
-            store_one(out + (tok0 + (size_t)t * H) * DV + tid, o);
-        }
-    }
-}
-
 // ----------------------------------------------------------------- dispatch
 
 template <int DK, int DV, typename TIn, typename TOut, bool VEC, int MODE>
@@ -556,13 +331,7 @@ static int launch_typed(const StepArgs &a, int32_t *err, hipStream_t st)
         break;
     case MODE_REPLAY: launch_tokens<DK, DV, TIn, TOut, VEC, MODE_REPLAY>(a, err, st); break;
     case MODE_BONUS: launch_tokens<DK, DV, TIn, TOut, VEC, MODE_BONUS>(a, err, st); break;
-    default: {
-        const size_t lds = (size_t)VerifyLds<DK, DV, VEC>(a.K).total * sizeof(float);
-        hipLaunchKernelGGL((k_verify<DK, DV, TIn, TOut, VEC>), grid, block, lds, st, a.state,
-                           a.n_slots, a.slot, a.H, a.K, (const TIn *)a.q, (const TIn *)a.k,
-                           (const TIn *)a.v, a.alpha, a.beta, (TOut *)a.out, err);
-        break;
-    }
+    default: break;  // MODE_VERIFY runs in its own translation unit
     }
     return hipGetLastError() == hipSuccess ? HLA_OK : HLA_ERR_LAUNCH;
 }
@@ -590,6 +359,7 @@ static int run_step(const StepArgs &a, int32_t *err, void *stream)
     int rc = check_step(a);
     if (rc != HLA_OK || a.B == 0) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (a.mode == MODE_VERIFY) return run_verify(a, err, stream);
     if (a.dk == 128 && a.dv == 128) return launch_dtypes<128, 128>(a, err, st);
     if (a.dk == 128 && a.dv == 64) return launch_dtypes<128, 64>(a, err, st);
     if (a.dk == 64 && a.dv == 128) return launch_dtypes<64, 128>(a, err, st);

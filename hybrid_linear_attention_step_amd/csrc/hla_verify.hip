@@ -1,0 +1,302 @@
+// gfx950 kernel for the verify pass of speculative decoding: the readouts at
+// all K draft positions from the committed state, which is only read.
+//
+// Operation ("Serving recurrent attention", part "Speculative decoding without
+// state snapshots"; the per-token update of "DAMP: Decay-Aware Mixed-Precision
+// Recurrent-State Quantization", §3.1 Eq. (1)-(2)), per (request, head) with
+// state S in dk x dv, for draft t = 1..K:
+//     S'_t = Lambda_t S_{t-1},  u_t = beta_t (v_t - S'_t^T k_t),
+//     S_t = S'_t + k_t u_t^T,  o_t = S_t^T q_t.
+#include <hip/hip_runtime.h>
+
+#include "hla.h"
+#include "hla_device.h"
+#include "hla_internal.h"
+
+namespace hla {
+
+// The verify pass needs the readouts at all K draft positions but never the
+// updated state, so it is evaluated in unrolled form instead of token by
+// token.  With c_t = prod_{s<=t} a_s (cumulative decay, per key channel) and
+// w_st = prod_{s<r<=t} a_r, the recurrence S'_t = Lambda_t S_{t-1},
+// u_t = beta_t (v_t - S'_t^T k_t), S_t = S'_t + k_t u_t^T unrolls to
+//     S'_t = diag(c_t) S_0 + sum_{s<t} diag(w_st) k_s u_s^T, so
+//     u_t = beta_t (v_t - S_0^T (c_t k_t) - sum_{s<t} G_st u_s),
+//     o_t = S_t^T q_t = S_0^T (c_t q_t) + sum_{s<t} E_st u_s + E_tt u_t,
+// with the scalars G_st = sum_i k_s,i w_st,i k_t,i and E_st = sum_i k_s,i
+// w_st,i q_t,i (E_tt = k_t . q_t).  The state then costs two FMAs per
+// element per draft (S_0^T (c_t k_t) and S_0^T (c_t q_t)) instead of four
+// (decay, two sums, rank-1 write); the corrections are O(K^2 dk) per head
+// and the solve O(K^2) per column.  The results equal the token-by-token
+// recurrence up to rounding (a different summation order).
+//
+// Phases per head (workgroup of dv/32 waves, each owning 32 columns):
+//   1. stage the K drafts' k, q, decay, v, beta into LDS and form c_t k_t and
+//      c_t q_t (one thread per key channel walks the drafts), written straight
+//      into the matrix-core operand layout below;
+//   2. (the tile loads are issued once the staged inputs are in LDS) the pair
+//      sums G_st, E_st are formed while the tile arrives, over chunks of key
+//      channels (the products w_st are built incrementally, never as a ratio
+//      of cumulative decays, so tiny decays cannot divide by an underflowed
+//      product);
+//   3. R = S_0^T [c k | c q], a dk-deep contraction with 2K columns, on the
+//      matrix cores: v_mfma_f32_16x16x4f32, FP32 in and FP32 accumulate;
+//   4. one thread per column solves the K drafts in order and writes o_t.
+//
+// Matrix-core layout (16x16x4 FP32, one block): in each instruction lane l
+// supplies A[l % 16][l / 16] and B[l / 16][l % 16] and receives
+// D[4 (l / 16) + i][l % 16], i = 0..3.  Here A = S_0^T restricted to 16 column
+// pairs and 4 rows: lane l = 16 rq + cm holds columns 32 w + 2 cm + {0, 1} of
+// rows 4 s + rq (s = 0 .. dk/4 - 1), loaded as one 8-byte pair per row, so
+// every load instruction of a wave covers 4 rows x 128 contiguous bytes; the
+// two columns of the pair are two M blocks sharing the B operand.  B holds 16
+// of the 2K right-hand columns: with KP = 8 NB padded drafts (NB = 1 for
+// K <= 8, else 2), right-hand column g is c_t k_t (g = t) or c_t q_t
+// (g = KP + t), zero for t >= K.  The output lane l receives columns
+// 32 w + 8 rq + 0..7 of right-hand column 16 nb + cm.
+constexpr int kPairChunks = 16;  // key-channel chunks of the pair sums
+
+__host__ __device__ constexpr int verify_nb(int K) { return K <= 8 ? 1 : 2; }
+
+template <int DK, int DV, bool VEC>
+struct VerifyLds {
+    // float offsets into the dynamic LDS block for K drafts.  r0 / p0 (phases
+    // 3-4) reuse the staging area of k, q and the decay (phases 1-2).
+    int k, q, a, r0, p0, v, b, xb, pg, pe;
+    int total;  // floats
+    __host__ __device__ VerifyLds(int K)
+    {
+        k = 0;
+        q = k + K * DK;
+        a = q + K * DK;
+        const int staged = a + (VEC ? K * DK : 16);
+        r0 = 0;
+        p0 = K * DV;
+        v = staged > 2 * K * DV ? staged : 2 * K * DV;
+        b = v + K * DV;
+        xb = b + 16;                                  // 16-byte aligned
+        pg = xb + verify_nb(K) * DK * 16;
+        pe = pg + K * K * kPairChunks;
+        total = pe + K * K * kPairChunks;
+    }
+};
+
+template <int DK, int DV, typename TIn, typename TOut, bool VEC, int NB>
+__global__ void __launch_bounds__(2 * DV) __attribute__((amdgpu_waves_per_eu(5)))
+k_verify(const float *__restrict__ state, int n_slots, const int32_t *__restrict__ slot, int H,
+         int K, const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
+         const float *__restrict__ alpha, const float *__restrict__ beta, TOut *__restrict__ out,
+         int32_t *__restrict__ err)
+{
+    constexpr int NT = 2 * DV, NS = DK / 4, CH = DK / kPairChunks, KP = 8 * NB;
+    extern __shared__ f32x4 verify_lds[];
+    float *L = reinterpret_cast<float *>(verify_lds);
+    const VerifyLds<DK, DV, VEC> at(K);
+    const int bh = blockIdx.x;
+    const int b = bh / H, h = bh - b * H;
+    const int s = slot ? slot[b] : b;
+    if (s < 0) return;  // uniform over the workgroup
+    if (s >= n_slots) {
+        if (err && threadIdx.x == 0) atomicOr(err, HLA_DEVERR_SLOT);
+        return;
+    }
+    const size_t tok0 = (size_t)b * K * H + h;  // draft t is token tok0 + t * H
+    const int tid = threadIdx.x;
+
+    // 1. stage the drafts' k, q, decay, v and beta (every load issued before the
+    //    first LDS write)
+    constexpr int JK = KP * DK / NT, JV = KP * DV / NT;  // KP >= K drafts staged
+    float rk[JK], rq_[JK], ra[JK], rv[JV];
+#pragma unroll
+    for (int j = 0; j < JK; ++j) {
+        const int e = tid + j * NT, t = e / DK, i = e - t * DK;
+        rk[j] = rq_[j] = ra[j] = 0.0f;
+        if (t < K) {
+            const size_t g = (tok0 + (size_t)t * H) * DK + i;
+            rk[j] = load_one(k + g);
+            rq_[j] = load_one(q + g);
+            if (VEC) ra[j] = alpha[g];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < JV; ++j) {
+        const int e = tid + j * NT, t = e / DV, i = e - t * DV;
+        rv[j] = t < K ? load_one(v + (tok0 + (size_t)t * H) * DV + i) : 0.0f;
+    }
+    const float rb = tid < K ? beta[tok0 + (size_t)tid * H] : 0.0f;
+    const float rs = !VEC && tid < K ? alpha[tok0 + (size_t)tid * H] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < JK; ++j) {
+        const int e = tid + j * NT;
+        if (e < K * DK) {
+            L[at.k + e] = rk[j];
+            L[at.q + e] = rq_[j];
+            if (VEC) L[at.a + e] = ra[j];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < JV; ++j) {
+        const int e = tid + j * NT;
+        if (e < K * DV) L[at.v + e] = rv[j];
+    }
+    if (tid < K) {
+        L[at.b + tid] = rb;
+        if (!VEC) L[at.a + tid] = rs;
+    }
+    __syncthreads();
+    // c_t k_t and c_t q_t of key channel i into the B-operand layout: right-hand
+    // column g of row i goes to block nb = g / 16, step group i / 16, lane
+    // 16 (i % 4) + g % 16, component (i / 4) % 4
+    for (int i = tid; i < DK; i += NT) {
+        float c = 1.0f;
+        const int base = (i >> 4) * 64 + ((i & 3) << 4), comp = (i >> 2) & 3;
+        for (int t = 0; t < KP; ++t) {
+            float xk = 0.0f, xq = 0.0f;
+            if (t < K) {
+                c *= VEC ? L[at.a + t * DK + i] : L[at.a + t];
+                xk = c * L[at.k + t * DK + i];
+                xq = c * L[at.q + t * DK + i];
+            }
+            const int gk = t, gq = KP + t;
+            L[at.xb + (((gk >> 4) * (DK / 16) * 64 + base + (gk & 15)) << 2) + comp] = xk;
+            L[at.xb + (((gq >> 4) * (DK / 16) * 64 + base + (gq & 15)) << 2) + comp] = xq;
+        }
+    }
+
+    // 2. the pair sums while the tile arrives
+    for (int it = tid; it < K * kPairChunks; it += NT) {
+        const int s0 = it / kPairChunks, ch = it - s0 * kPairChunks;
+        const int i0 = ch * CH;
+        float ks[CH], w[CH];
+        float e_ss = 0.0f;
+#pragma unroll
+        for (int m = 0; m < CH; ++m) {
+            ks[m] = L[at.k + s0 * DK + i0 + m];
+            w[m] = 1.0f;
+            e_ss = fmaf(ks[m], L[at.q + s0 * DK + i0 + m], e_ss);
+        }
+        L[at.pe + (s0 * K + s0) * kPairChunks + ch] = e_ss;
+        for (int t = s0 + 1; t < K; ++t) {
+            float g = 0.0f, e2 = 0.0f;
+#pragma unroll
+            for (int m = 0; m < CH; ++m) {
+                w[m] *= VEC ? L[at.a + t * DK + i0 + m] : L[at.a + t];
+                const float kw = ks[m] * w[m];
+                g = fmaf(kw, L[at.k + t * DK + i0 + m], g);
+                e2 = fmaf(kw, L[at.q + t * DK + i0 + m], e2);
+            }
+            L[at.pg + (s0 * K + t) * kPairChunks + ch] = g;
+            L[at.pe + (s0 * K + t) * kPairChunks + ch] = e2;
+        }
+    }
+    // the tile (read only) in the matrix-core layout; issued once the staged
+    // inputs are in LDS, so their registers are free, and it arrives while the
+    // B operand and the pair sums are formed
+    const int lane = tid & 63, wave = tid >> 6;
+    const int cm = lane & 15, rq = lane >> 4;
+    const float *S = state + ((size_t)s * H + h) * (DK * DV) + (size_t)rq * DV + wave * 32 + 2 * cm;
+    float x[NS][2];
+#pragma unroll
+    for (int m = 0; m < NS; ++m) {
+        const u32x2 t2 = ld_nt(reinterpret_cast<const u32x2 *>(S + (size_t)(4 * m) * DV));
+        x[m][0] = __uint_as_float(t2.x);
+        x[m][1] = __uint_as_float(t2.y);
+    }
+    __syncthreads();  // the B operand and the pair partials are complete; k, q, decay are dead
+
+    // 3. S_0^T [c k | c q] on the matrix cores, then to LDS (r0 / p0 replace k / q)
+    const f32x4 *XB = reinterpret_cast<const f32x4 *>(L + at.xb);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g4 = 0; g4 < DK / 16; ++g4) {
+            const f32x4 bq = XB[(nb * (DK / 16) + g4) * 64 + lane];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(x[4 * g4 + j][0], bq[j], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(x[4 * g4 + j][1], bq[j], acc1, 0, 0, 0);
+            }
+        }
+        const int g = 16 * nb + cm, typ = g >= KP, t = g - typ * KP;
+        if (t < K) {
+            float *dst = L + (typ ? at.p0 : at.r0) + t * DV + wave * 32 + 8 * rq;
+            reinterpret_cast<f32x4 *>(dst)[0] = f32x4{acc0[0], acc1[0], acc0[1], acc1[1]};
+            reinterpret_cast<f32x4 *>(dst)[1] = f32x4{acc0[2], acc1[2], acc0[3], acc1[3]};
+        }
+    }
+    // pair sums: chunk partials -> G_st, E_st (kept in chunk 0's slot)
+    for (int it = tid; it < K * K; it += NT) {
+        const int s0 = it / K, t = it - s0 * K;
+        if (t < s0) continue;
+        float g = 0.0f, e2 = 0.0f;
+        for (int ch = 0; ch < kPairChunks; ++ch) {
+            if (t > s0) g += L[at.pg + it * kPairChunks + ch];
+            e2 += L[at.pe + it * kPairChunks + ch];
+        }
+        L[at.pg + it * kPairChunks] = g;
+        L[at.pe + it * kPairChunks] = e2;
+    }
+    __syncthreads();
+
+    // 4. one thread per column: the drafts in order
+    if (tid < DV) {
+        float u[KP];  // K <= KP <= 16
+        for (int t = 0; t < K; ++t) {
+            float r = L[at.r0 + t * DV + tid];
+            float o = L[at.p0 + t * DV + tid];
+            for (int s1 = 0; s1 < t; ++s1) {
+                r = fmaf(L[at.pg + (s1 * K + t) * kPairChunks], u[s1], r);
+                o = fmaf(L[at.pe + (s1 * K + t) * kPairChunks], u[s1], o);
+            }
+            const float ut = L[at.b + t] * (L[at.v + t * DV + tid] - r);  // u = beta (v - r)
+            u[t] = ut;
+            o = fmaf(L[at.pe + (t * K + t) * kPairChunks], ut, o);
+            store_one(out + (tok0 + (size_t)t * H) * DV + tid, o);
+        }
+    }
+}
+
+// ----------------------------------------------------------------- dispatch
+
+template <int DK, int DV, typename TIn, typename TOut, bool VEC>
+static int launch_verify(const StepArgs &a, int32_t *err, hipStream_t st)
+{
+    const dim3 grid((unsigned)((size_t)a.B * a.H)), block(2 * DV);
+    const size_t lds = (size_t)VerifyLds<DK, DV, VEC>(a.K).total * sizeof(float);
+    if (verify_nb(a.K) == 1)
+        hipLaunchKernelGGL((k_verify<DK, DV, TIn, TOut, VEC, 1>), grid, block, lds, st, a.state,
+                           a.n_slots, a.slot, a.H, a.K, (const TIn *)a.q, (const TIn *)a.k,
+                           (const TIn *)a.v, a.alpha, a.beta, (TOut *)a.out, err);
+    else
+        hipLaunchKernelGGL((k_verify<DK, DV, TIn, TOut, VEC, 2>), grid, block, lds, st, a.state,
+                           a.n_slots, a.slot, a.H, a.K, (const TIn *)a.q, (const TIn *)a.k,
+                           (const TIn *)a.v, a.alpha, a.beta, (TOut *)a.out, err);
+    return hipGetLastError() == hipSuccess ? HLA_OK : HLA_ERR_LAUNCH;
+}
+
+template <int DK, int DV>
+static int verify_dtypes(const StepArgs &a, int32_t *err, hipStream_t st)
+{
+    const bool in16 = a.in_dtype == HLA_BF16, out16 = a.out_dtype == HLA_BF16;
+    const bool vec = a.decay == HLA_DECAY_VECTOR;
+#define HLA_VERIFY_T(TI_, TO_)                                                                \
+    return vec ? launch_verify<DK, DV, TI_, TO_, true>(a, err, st)                            \
+               : launch_verify<DK, DV, TI_, TO_, false>(a, err, st);
+    if (in16 && out16) { HLA_VERIFY_T(uint16_t, uint16_t) }
+    if (in16) { HLA_VERIFY_T(uint16_t, float) }
+    if (out16) { HLA_VERIFY_T(float, uint16_t) }
+    HLA_VERIFY_T(float, float)
+#undef HLA_VERIFY_T
+}
+
+int run_verify(const StepArgs &a, int32_t *err, void *stream)
+{
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (a.dk == 128 && a.dv == 128) return verify_dtypes<128, 128>(a, err, st);
+    if (a.dk == 128 && a.dv == 64) return verify_dtypes<128, 64>(a, err, st);
+    if (a.dk == 64 && a.dv == 128) return verify_dtypes<64, 128>(a, err, st);
+    return verify_dtypes<64, 64>(a, err, st);
+}
+
+} // namespace hla
