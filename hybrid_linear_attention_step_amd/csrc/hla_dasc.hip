@@ -213,10 +213,11 @@ k_dasc_copy_units(const uint8_t *__restrict__ scratch, int64_t scratch_stride, i
 // of 256 threads covers 256/CG rows per pass and a few passes, with
 // every pass's loads issued before the first conversion.  The row maximum is a DPP max over the
 // CG lanes; codes and scale come from the shared codec (hla_codec.h).
-// passes per block, measured on the checkpoint workloads (restore: more,
-// smaller blocks beat more rows in flight per lane)
+// passes per block, measured on the checkpoint workloads: pack 4; restore 2
+// for one-row units (KDA channel rows: 4.84 -> 5.49 TB/s), 1 for larger units
+// (GDN heads: 5.90 TB/s at 1, 5.44 at 2; more passes were slower for both)
 constexpr int kInt8PassesPack = 4;
-constexpr int kInt8PassesRestore = 1;
+inline int int8_restore_passes(int unit_rows) { return unit_rows == 1 ? 2 : 1; }
 
 template <int DV>
 __global__ void __launch_bounds__(kCopyThreads)
@@ -278,7 +279,7 @@ k_dasc_pack_int8(const uint8_t *__restrict__ active, int64_t layer_stride, int S
     }
 }
 
-template <int DV>
+template <int DV, int P>
 __global__ void __launch_bounds__(kCopyThreads)
 k_dasc_restore_int8(const int8_t *__restrict__ codes, const float *__restrict__ scales,
                     int S_ckpt, int R_total, const int32_t *__restrict__ unit_pos, int L,
@@ -298,23 +299,35 @@ k_dasc_restore_int8(const int8_t *__restrict__ codes, const float *__restrict__ 
     const uint32_t rows = ((uint32_t)L * (uint32_t)n_units) << log2_rows;
     const uint32_t row_mask = (1u << log2_rows) - 1u;
     uint8_t *dst_base = active_out + (int64_t)dst * n_units * ((int64_t)DV * 4 << log2_rows);
-    uint32_t w0[kInt8PassesRestore], w1[kInt8PassesRestore];
-    float sc[kInt8PassesRestore];
-    float *dptr[kInt8PassesRestore];
+    // Three stages over the lane's P rows, so that no stage waits on a later
+    // one's memory: every unit_pos lookup (with the destination addresses),
+    // then every code / scale load, then the stores (a lookup issued after a
+    // row's code loads could only be used once those loads had returned too).
+    int pos[P];
+    uint32_t rr[P];
+    bool live[P];
+    float *d[P];
 #pragma unroll
-    for (int i = 0; i < kInt8PassesRestore; ++i) {
-        const uint32_t rr = (blockIdx.x * kInt8PassesRestore + i) * RPP + (threadIdx.x >> LCG);
-        dptr[i] = nullptr;
-        w0[i] = w1[i] = 0u;
-        sc[i] = 0.0f;
-        if (rr >= rows) continue;
-        const uint32_t g = rr >> log2_rows, r = rr & row_mask;  // g = l * n_units + u
+    for (int i = 0; i < P; ++i) {
+        rr[i] = (blockIdx.x * P + i) * RPP + (threadIdx.x >> LCG);
+        live[i] = rr[i] < rows;  // uniform over a row's CG lanes
+        const uint32_t g = rr[i] >> log2_rows, r = rr[i] & row_mask;  // g = l * n_units + u
+        pos[i] = live[i] ? unit_pos[g] : -1;
         const uint32_t l = fdiv(g, units);
         const uint32_t u = g - l * units.d;
-        const int pos = unit_pos[g];
-        if (pos >= 0) {
-            if (pos < R_total) {
-                const int64_t in_row = (((int64_t)src * R_total + pos) << log2_rows) + r;
+        d[i] = reinterpret_cast<float *>(dst_base + l * layer_stride +
+                                         ((((int64_t)u << log2_rows) + r) * DV) * 4) + cg * 4;
+    }
+    uint32_t w0[P], w1[P];
+    float sc[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        w0[i] = w1[i] = 0u;
+        sc[i] = 0.0f;
+        if (pos[i] >= 0) {
+            if (pos[i] < R_total) {
+                const int64_t in_row =
+                    (((int64_t)src * R_total + pos[i]) << log2_rows) + (rr[i] & row_mask);
                 const int8_t *crow = codes + in_row * DV;
                 w0[i] = ld_nt(reinterpret_cast<const uint32_t *>(crow + cg * 4));
                 w1[i] = ld_nt(reinterpret_cast<const uint32_t *>(crow + DV / 2 + cg * 4));
@@ -323,17 +336,14 @@ k_dasc_restore_int8(const int8_t *__restrict__ codes, const float *__restrict__ 
                 atomicOr(err, HLA_DEVERR_PLAN);
             }
         }
-        dptr[i] = reinterpret_cast<float *>(dst_base + l * layer_stride +
-                                            ((((int64_t)u << log2_rows) + r) * DV) * 4) +
-                  cg * 4;
     }
 #pragma unroll
-    for (int i = 0; i < kInt8PassesRestore; ++i) {
-        if (!dptr[i]) continue;
+    for (int i = 0; i < P; ++i) {
+        if (!live[i]) continue;
         float y[8];
         decode_int8(w0[i], w1[i], sc[i], y);  // q * s, one FP32 rounding (0 when omitted)
-        st_nt(reinterpret_cast<f32x4 *>(dptr[i]), f32x4{y[0], y[1], y[2], y[3]});
-        st_nt(reinterpret_cast<f32x4 *>(dptr[i] + DV / 2), f32x4{y[4], y[5], y[6], y[7]});
+        st_nt(reinterpret_cast<f32x4 *>(d[i]), f32x4{y[0], y[1], y[2], y[3]});
+        st_nt(reinterpret_cast<f32x4 *>(d[i] + DV / 2), f32x4{y[4], y[5], y[6], y[7]});
     }
 }
 
@@ -478,20 +488,23 @@ int dasc_restore_int8(const int8_t *codes, const float *scales, int S_ckpt, int 
     const int lr = hla::log2_exact(unit_rows);
     const hla::FastDiv un = hla::make_fastdiv((uint32_t)n_units);
     const uint64_t rows = ((uint64_t)L * n_units) << lr;
-    const uint64_t per_block = (uint64_t)(hla::kCopyThreads / (dv / 8)) * hla::kInt8PassesRestore;
+    const int passes = hla::int8_restore_passes(unit_rows);
+    const uint64_t per_block = (uint64_t)(hla::kCopyThreads / (dv / 8)) * passes;
     const unsigned bx = (unsigned)((rows + per_block - 1) / per_block);
     hipStream_t st = static_cast<hipStream_t>(stream);
     for (int p0 = 0; p0 < N; p0 += (int)hla::kMaxGridY) {
         const unsigned by = (unsigned)std::min<int>(N - p0, (int)hla::kMaxGridY);
         const dim3 grid(bx, by), block(hla::kCopyThreads);
-        if (dv == 128)
-            hipLaunchKernelGGL(hla::k_dasc_restore_int8<128>, grid, block, 0, st, codes, scales,
-                               S_ckpt, R_total, unit_pos, L, n_units, un, lr, src_slot, dst_slot,
-                               p0, (uint8_t *)active_out, layer_stride_bytes, S_dst, err_flag);
-        else
-            hipLaunchKernelGGL(hla::k_dasc_restore_int8<64>, grid, block, 0, st, codes, scales,
-                               S_ckpt, R_total, unit_pos, L, n_units, un, lr, src_slot, dst_slot,
-                               p0, (uint8_t *)active_out, layer_stride_bytes, S_dst, err_flag);
+#define HLA_RESTORE8(DV_, P_)                                                                 \
+    hipLaunchKernelGGL((hla::k_dasc_restore_int8<DV_, P_>), grid, block, 0, st, codes, scales,  \
+                       S_ckpt, R_total, unit_pos, L, n_units, un, lr, src_slot, dst_slot, p0,  \
+                       (uint8_t *)active_out, layer_stride_bytes, S_dst, err_flag)
+        if (dv == 128) {
+            if (passes == 2) HLA_RESTORE8(128, 2); else HLA_RESTORE8(128, 1);
+        } else {
+            if (passes == 2) HLA_RESTORE8(64, 2); else HLA_RESTORE8(64, 1);
+        }
+#undef HLA_RESTORE8
         if (hipGetLastError() != hipSuccess) return HLA_ERR_LAUNCH;
     }
     return HLA_OK;
