@@ -69,28 +69,41 @@ k_dasc_pack(const uint8_t *__restrict__ active, int64_t layer_stride, int S_act,
     const uint8_t *src_base = active + (int64_t)src * n_units * unit_bytes;
     uint8_t *dst_base = packed + (int64_t)dst * R_total * unit_bytes;
 
+    // three stages, so that no stage waits on a later one's memory (the wave's
+    // memory counter is in order): the unit lookups, the loads, the stores
+    int unit[kCopyVecs];
+    uint32_t pv[kCopyVecs], offv[kCopyVecs];
+    int layer[kCopyVecs];
+#pragma unroll
+    for (int i = 0; i < kCopyVecs; ++i) {
+        const uint32_t e = base + i * kCopyThreads;
+        unit[i] = -1;
+        if (e >= total) continue;
+        pv[i] = fdiv(e, unit_vecs);
+        offv[i] = e - pv[i] * unit_vecs.d;
+        int lo = 0, hi = L;  // offs[lo] <= p < offs[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if ((uint32_t)offs[mid] <= pv[i]) lo = mid; else hi = mid;
+        }
+        layer[i] = lo;
+        unit[i] = unit_index[pv[i]];
+    }
     u32x4 buf[kCopyVecs];
     uint8_t *dptr[kCopyVecs];
 #pragma unroll
     for (int i = 0; i < kCopyVecs; ++i) {
-        const uint32_t e = base + i * kCopyThreads;
         dptr[i] = nullptr;
-        if (e >= total) continue;
-        const uint32_t p = fdiv(e, unit_vecs);
-        const uint32_t off = e - p * unit_vecs.d;
-        int lo = 0, hi = L;  // offs[lo] <= p < offs[hi]
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if ((uint32_t)offs[mid] <= p) lo = mid; else hi = mid;
-        }
-        const int u = unit_index[p];
+        if (base + i * kCopyThreads >= total) continue;
+        const int u = unit[i];
         if (u < 0 || u >= n_units) {
             if (err) atomicOr(err, HLA_DEVERR_PLAN);
             continue;
         }
-        const uint8_t *s = src_base + lo * layer_stride + (int64_t)u * unit_bytes + (int64_t)off * 16;
+        const uint8_t *s = src_base + layer[i] * layer_stride + (int64_t)u * unit_bytes +
+                           (int64_t)offv[i] * 16;
         buf[i] = ld_nt(reinterpret_cast<const u32x4 *>(s));
-        dptr[i] = dst_base + (int64_t)p * unit_bytes + (int64_t)off * 16;
+        dptr[i] = dst_base + (int64_t)pv[i] * unit_bytes + (int64_t)offv[i] * 16;
     }
 #pragma unroll
     for (int i = 0; i < kCopyVecs; ++i)
@@ -115,27 +128,35 @@ k_dasc_restore(const uint8_t *__restrict__ packed, int S_ckpt, int R_total,
     const uint8_t *src_base = packed + (int64_t)src * R_total * unit_bytes;
     uint8_t *dst_base = active_out + (int64_t)dst * n_units * unit_bytes;
 
-    u32x4 buf[kCopyVecs];
+    // three stages, as in k_dasc_pack: lookups (with the destinations), loads, stores
+    int pos[kCopyVecs];
+    uint32_t offv[kCopyVecs];
     uint8_t *dptr[kCopyVecs];
 #pragma unroll
     for (int i = 0; i < kCopyVecs; ++i) {
         const uint32_t e = base + i * kCopyThreads;
         dptr[i] = nullptr;
+        pos[i] = -1;
         if (e >= total) continue;
         const uint32_t g = fdiv(e, unit_vecs);   // layer * n_units + unit
-        const uint32_t off = e - g * unit_vecs.d;
+        offv[i] = e - g * unit_vecs.d;
         const uint32_t l = fdiv(g, units);
         const uint32_t u = g - l * units.d;
-        const int pos = unit_pos[g];
+        pos[i] = unit_pos[g];
+        dptr[i] = dst_base + (int64_t)l * layer_stride + (int64_t)u * unit_bytes +
+                  (int64_t)offv[i] * 16;
+    }
+    u32x4 buf[kCopyVecs];
+#pragma unroll
+    for (int i = 0; i < kCopyVecs; ++i) {
         buf[i] = u32x4{0u, 0u, 0u, 0u};
-        if (pos >= 0) {
-            if (pos < R_total)
+        if (pos[i] >= 0) {
+            if (pos[i] < R_total)
                 buf[i] = ld_nt(reinterpret_cast<const u32x4 *>(
-                    src_base + (int64_t)pos * unit_bytes + (int64_t)off * 16));
+                    src_base + (int64_t)pos[i] * unit_bytes + (int64_t)offv[i] * 16));
             else if (err)
                 atomicOr(err, HLA_DEVERR_PLAN);
         }
-        dptr[i] = dst_base + (int64_t)l * layer_stride + (int64_t)u * unit_bytes + (int64_t)off * 16;
     }
 #pragma unroll
     for (int i = 0; i < kCopyVecs; ++i)
@@ -180,24 +201,34 @@ k_dasc_copy_units(const uint8_t *__restrict__ scratch, int64_t scratch_stride, i
     const uint8_t *src_base = scratch + (int64_t)src * n_units * unit_bytes;
     uint8_t *dst_base = active + (int64_t)dst * n_units * unit_bytes;
 
+    // three stages, as in k_dasc_pack: unit lookups, loads, stores
+    int unit[kCopyVecs], layer[kCopyVecs];
+    uint32_t offv[kCopyVecs];
+#pragma unroll
+    for (int i = 0; i < kCopyVecs; ++i) {
+        const uint32_t e = base + i * kCopyThreads;
+        unit[i] = -1;
+        if (e >= total) continue;
+        const uint32_t p = fdiv(e, unit_vecs);
+        offv[i] = e - p * unit_vecs.d;
+        layer[i] = layer_of(offs, L, p);
+        unit[i] = unit_index[p];
+    }
     u32x4 buf[kCopyVecs];
     uint8_t *dptr[kCopyVecs];
 #pragma unroll
     for (int i = 0; i < kCopyVecs; ++i) {
-        const uint32_t e = base + i * kCopyThreads;
         dptr[i] = nullptr;
-        if (e >= total) continue;
-        const uint32_t p = fdiv(e, unit_vecs);
-        const uint32_t off = e - p * unit_vecs.d;
-        const int l = layer_of(offs, L, p);
-        const int u = unit_index[p];
+        if (base + i * kCopyThreads >= total) continue;
+        const int u = unit[i];
         if (u < 0 || u >= n_units) {
             if (err) atomicOr(err, HLA_DEVERR_PLAN);
             continue;
         }
-        const int64_t unit_off = (int64_t)u * unit_bytes + (int64_t)off * 16;
-        buf[i] = ld_nt(reinterpret_cast<const u32x4 *>(src_base + l * scratch_stride + unit_off));
-        dptr[i] = dst_base + l * layer_stride + unit_off;
+        const int64_t unit_off = (int64_t)u * unit_bytes + (int64_t)offv[i] * 16;
+        buf[i] = ld_nt(reinterpret_cast<const u32x4 *>(src_base + layer[i] * scratch_stride +
+                                                        unit_off));
+        dptr[i] = dst_base + layer[i] * layer_stride + unit_off;
     }
 #pragma unroll
     for (int i = 0; i < kCopyVecs; ++i)
