@@ -273,29 +273,42 @@ k_dasc_pack_int8(const uint8_t *__restrict__ active, int64_t layer_stride, int S
     const uint32_t rows = (uint32_t)R_total << log2_rows;
     const uint32_t row_mask = (1u << log2_rows) - 1u;
     const uint8_t *src_base = active + (int64_t)src * n_units * ((int64_t)DV * 4 << log2_rows);
-    float x[kInt8PassesPack][8];
-    uint32_t out_row[kInt8PassesPack];
-    bool live[kInt8PassesPack];
+    // three stages, so that no stage waits on a later one's memory (the wave's
+    // memory counter is in order): unit lookups, row loads, quantise + stores
+    constexpr int P = kInt8PassesPack;
+    bool live[P];
+    int unit[P], layer[P];
+    uint32_t rrv[P];
 #pragma unroll
-    for (int i = 0; i < kInt8PassesPack; ++i) {
-        const uint32_t rr = (blockIdx.x * kInt8PassesPack + i) * RPP + (threadIdx.x >> LCG);
-        live[i] = rr < rows;  // uniform over a row's CG lanes
+    for (int i = 0; i < P; ++i) {
+        rrv[i] = (blockIdx.x * P + i) * RPP + (threadIdx.x >> LCG);
+        live[i] = rrv[i] < rows;  // uniform over a row's CG lanes
+        unit[i] = 0;
+        layer[i] = 0;
+        if (!live[i]) continue;
+        const uint32_t p = rrv[i] >> log2_rows;
+        layer[i] = layer_of(offs, L, p);
+        unit[i] = unit_index[p];
+    }
+    float x[P][8];
+    uint32_t out_row[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
         out_row[i] = 0;
         if (!live[i]) continue;
-        const uint32_t p = rr >> log2_rows, r = rr & row_mask;
-        const int l = layer_of(offs, L, p);
-        int u = unit_index[p];
+        const uint32_t r = rrv[i] & row_mask;
+        int u = unit[i];
         if (u < 0 || u >= n_units) {
             if (err) atomicOr(err, HLA_DEVERR_PLAN);
             u = 0;  // keep the lanes of the row together; the flag reports the plan
         }
         const float *row = reinterpret_cast<const float *>(
-            src_base + l * layer_stride + ((((int64_t)u << log2_rows) + r) * DV) * 4);
+            src_base + layer[i] * layer_stride + ((((int64_t)u << log2_rows) + r) * DV) * 4);
         const f32x4 a = ld_nt(reinterpret_cast<const f32x4 *>(row + cg * 4));
         const f32x4 b = ld_nt(reinterpret_cast<const f32x4 *>(row + DV / 2 + cg * 4));
         x[i][0] = a.x; x[i][1] = a.y; x[i][2] = a.z; x[i][3] = a.w;
         x[i][4] = b.x; x[i][5] = b.y; x[i][6] = b.z; x[i][7] = b.w;
-        out_row[i] = ((uint32_t)dst * (uint32_t)R_total << log2_rows) + rr;
+        out_row[i] = ((uint32_t)dst * (uint32_t)R_total << log2_rows) + rrv[i];
     }
 #pragma unroll
     for (int i = 0; i < kInt8PassesPack; ++i) {
