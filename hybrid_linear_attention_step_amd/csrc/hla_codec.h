@@ -94,35 +94,18 @@ __device__ __forceinline__ float encode_int8(const float (&x)[8], float amax, ui
     return s;
 }
 
-#ifndef HLA_ASM_ABSMAX
-#define HLA_ASM_ABSMAX 1
-#endif
-
 // max |x_i| of 8 finite floats.  v_max3_f32 takes |.| source modifiers, so the
 // whole row segment is 3 max3 + 1 max (the compiler's maxnum lowering would
 // first canonicalise every |x_i| in IEEE mode).  max is exact and the inputs
 // are finite FMA results, so the result equals the plain definition.
 __device__ __forceinline__ float row_absmax8(const float (&x)[8])
 {
-#if HLA_ASM_ABSMAX
     float m;
     asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(m) : "v"(x[0]), "v"(x[1]), "v"(x[2]));
     asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(m) : "v"(m), "v"(x[3]), "v"(x[4]));
     asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(m) : "v"(m), "v"(x[5]), "v"(x[6]));
     asm("v_max_f32 %0, %1, |%2|" : "=v"(m) : "v"(m), "v"(x[7]));
     return m;
-#else
-    float hi = fmaxf(x[0], fmaxf(x[1], x[2]));
-    float lo = fminf(x[0], fminf(x[1], x[2]));
-    hi = fmaxf(hi, fmaxf(x[3], x[4]));
-    lo = fminf(lo, fminf(x[3], x[4]));
-    hi = fmaxf(hi, fmaxf(x[5], x[6]));
-    lo = fminf(lo, fminf(x[5], x[6]));
-    hi = fmaxf(hi, x[7]);
-    lo = fminf(lo, x[7]);
-    return fmaxf(hi, -lo);
-#endif
 }
-
 
 } // namespace hla
