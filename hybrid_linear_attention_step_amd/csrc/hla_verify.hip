@@ -34,11 +34,12 @@ namespace hla {
 //   1. stage the K drafts' k, q, decay, v, beta into LDS and form c_t k_t and
 //      c_t q_t (one thread per key channel walks the drafts), written straight
 //      into the matrix-core operand layout below;
-//   2. (the tile loads are issued once the staged inputs are in LDS) the pair
-//      sums G_st, E_st are formed while the tile arrives, over chunks of key
-//      channels (the products w_st are built incrementally, never as a ratio
-//      of cumulative decays, so tiny decays cannot divide by an underflowed
-//      product);
+//   2. the pair sums G_st, E_st over chunks of key channels (the products
+//      w_st are built incrementally, never as a ratio of cumulative decays, so
+//      tiny decays cannot divide by an underflowed product), while the first
+//      half of the tile arrives (issued right behind the staged inputs; the
+//      second half is issued after the pair sums, which keeps the kernel
+//      within five waves per SIMD);
 //   3. R = S_0^T [c k | c q], a dk-deep contraction with 2K columns, on the
 //      matrix cores: v_mfma_f32_16x16x4f32, FP32 in and FP32 accumulate;
 //   4. one thread per column solves the K drafts in order and writes o_t.
@@ -125,6 +126,19 @@ k_verify(const float *__restrict__ state, int n_slots, const int32_t *__restrict
     }
     const float rb = tid < K ? beta[tok0 + (size_t)tid * H] : 0.0f;
     const float rs = !VEC && tid < K ? alpha[tok0 + (size_t)tid * H] : 0.0f;
+    // the tile (read only) in the matrix-core layout: the first half is issued
+    // right behind the staged inputs, the second once the pair sums are done
+    const int lane = tid & 63, wave = tid >> 6;
+    const int cm = lane & 15, rq = lane >> 4;
+    const float *S = state + ((size_t)s * H + h) * (DK * DV) + (size_t)rq * DV + wave * 32 + 2 * cm;
+    constexpr int NS1 = NS / 2;
+    float x[NS][2];
+#pragma unroll
+    for (int m = 0; m < NS1; ++m) {
+        const u32x2 t2 = ld_nt(reinterpret_cast<const u32x2 *>(S + (size_t)(4 * m) * DV));
+        x[m][0] = __uint_as_float(t2.x);
+        x[m][1] = __uint_as_float(t2.y);
+    }
 #pragma unroll
     for (int j = 0; j < JK; ++j) {
         const int e = tid + j * NT;
@@ -189,15 +203,9 @@ k_verify(const float *__restrict__ state, int n_slots, const int32_t *__restrict
             L[at.pe + (s0 * K + t) * kPairChunks + ch] = e2;
         }
     }
-    // the tile (read only) in the matrix-core layout; issued once the staged
-    // inputs are in LDS, so their registers are free, and it arrives while the
-    // B operand and the pair sums are formed
-    const int lane = tid & 63, wave = tid >> 6;
-    const int cm = lane & 15, rq = lane >> 4;
-    const float *S = state + ((size_t)s * H + h) * (DK * DV) + (size_t)rq * DV + wave * 32 + 2 * cm;
-    float x[NS][2];
+    // second half of the tile
 #pragma unroll
-    for (int m = 0; m < NS; ++m) {
+    for (int m = NS1; m < NS; ++m) {
         const u32x2 t2 = ld_nt(reinterpret_cast<const u32x2 *>(S + (size_t)(4 * m) * DV));
         x[m][0] = __uint_as_float(t2.x);
         x[m][1] = __uint_as_float(t2.y);
