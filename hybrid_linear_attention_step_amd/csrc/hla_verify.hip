@@ -247,20 +247,33 @@ k_verify(const float *__restrict__ state, int n_slots, const int32_t *__restrict
     }
     __syncthreads();
 
-    // 4. one thread per column: the drafts in order
+    // 4. one thread per column: the drafts in order.  The loops run to the
+    //    compile-time KP (drafts t >= K skipped) so that every LDS read, none of
+    //    which depends on u, can be issued ahead of the FMA chain.
     if (tid < DV) {
-        float u[KP];  // K <= KP <= 16
-        for (int t = 0; t < K; ++t) {
-            float r = L[at.r0 + t * DV + tid];
-            float o = L[at.p0 + t * DV + tid];
-            for (int s1 = 0; s1 < t; ++s1) {
-                r = fmaf(L[at.pg + (s1 * K + t) * kPairChunks], u[s1], r);
-                o = fmaf(L[at.pe + (s1 * K + t) * kPairChunks], u[s1], o);
+        float r[KP], o[KP], vv[KP], u[KP];
+#pragma unroll
+        for (int t = 0; t < KP; ++t) {
+            r[t] = o[t] = vv[t] = u[t] = 0.0f;
+            if (t < K) {
+                r[t] = L[at.r0 + t * DV + tid];
+                o[t] = L[at.p0 + t * DV + tid];
+                vv[t] = L[at.v + t * DV + tid];
             }
-            const float ut = L[at.b + t] * (L[at.v + t * DV + tid] - r);  // u = beta (v - r)
-            u[t] = ut;
-            o = fmaf(L[at.pe + (t * K + t) * kPairChunks], ut, o);
-            store_one(out + (tok0 + (size_t)t * H) * DV + tid, o);
+        }
+#pragma unroll
+        for (int t = 0; t < KP; ++t) {
+            if (t < K) {
+                float rt = r[t], ot = o[t];
+#pragma unroll
+                for (int s1 = 0; s1 < t; ++s1) {
+                    rt = fmaf(L[at.pg + (s1 * K + t) * kPairChunks], u[s1], rt);
+                    ot = fmaf(L[at.pe + (s1 * K + t) * kPairChunks], u[s1], ot);
+                }
+                u[t] = L[at.b + t] * (vv[t] - rt);  // u = beta (v - r)
+                ot = fmaf(L[at.pe + (t * K + t) * kPairChunks], u[t], ot);
+                store_one(out + (tok0 + (size_t)t * H) * DV + tid, ot);
+            }
         }
     }
 }
