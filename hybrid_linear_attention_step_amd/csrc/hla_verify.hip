@@ -190,7 +190,11 @@ k_verify(const float *__restrict__ state, int n_slots, const int32_t *__restrict
             e_ss = fmaf(ks[m], L[at.q + s0 * DK + i0 + m], e_ss);
         }
         L[at.pe + (s0 * K + s0) * kPairChunks + ch] = e_ss;
-        for (int t = s0 + 1; t < K; ++t) {
+        // t runs to the compile-time KP (skipping t <= s0 and t >= K) so that the
+        // LDS reads of later drafts can issue ahead of the w products' chain
+#pragma unroll
+        for (int t = 1; t < KP; ++t) {
+            if (t <= s0 || t >= K) continue;
             float g = 0.0f, e2 = 0.0f;
 #pragma unroll
             for (int m = 0; m < CH; ++m) {
