@@ -24,7 +24,12 @@
 namespace hla {
 
 constexpr int kCopyThreads = 256;
-constexpr int kCopyVecs = 4;  // 16-byte vectors per lane per block
+// 16-byte vectors per lane per block (measured on the checkpoint workloads: the
+// restore's copy + zero-fill streams best from 8 KiB blocks, 5.53 -> 5.96 TB/s;
+// the pack gains ~1% from them; the copy-back prefers 16 KiB, 5.96 vs 5.71)
+constexpr int kPackVecs = 2;
+constexpr int kRestoreVecs = 2;
+constexpr int kUnitCopyVecs = 4;
 constexpr int kMaxLayers = 1024;
 constexpr unsigned kMaxGridY = 65535;
 
@@ -65,17 +70,17 @@ k_dasc_pack(const uint8_t *__restrict__ active, int64_t layer_stride, int S_act,
         return;
     }
     const uint32_t total = (uint32_t)R_total * unit_vecs.d;
-    const uint32_t base = blockIdx.x * (kCopyThreads * kCopyVecs) + threadIdx.x;
+    const uint32_t base = blockIdx.x * (kCopyThreads * kPackVecs) + threadIdx.x;
     const uint8_t *src_base = active + (int64_t)src * n_units * unit_bytes;
     uint8_t *dst_base = packed + (int64_t)dst * R_total * unit_bytes;
 
     // three stages, so that no stage waits on a later one's memory (the wave's
     // memory counter is in order): the unit lookups, the loads, the stores
-    int unit[kCopyVecs];
-    uint32_t pv[kCopyVecs], offv[kCopyVecs];
-    int layer[kCopyVecs];
+    int unit[kPackVecs];
+    uint32_t pv[kPackVecs], offv[kPackVecs];
+    int layer[kPackVecs];
 #pragma unroll
-    for (int i = 0; i < kCopyVecs; ++i) {
+    for (int i = 0; i < kPackVecs; ++i) {
         const uint32_t e = base + i * kCopyThreads;
         unit[i] = -1;
         if (e >= total) continue;
@@ -89,10 +94,10 @@ k_dasc_pack(const uint8_t *__restrict__ active, int64_t layer_stride, int S_act,
         layer[i] = lo;
         unit[i] = unit_index[pv[i]];
     }
-    u32x4 buf[kCopyVecs];
-    uint8_t *dptr[kCopyVecs];
+    u32x4 buf[kPackVecs];
+    uint8_t *dptr[kPackVecs];
 #pragma unroll
-    for (int i = 0; i < kCopyVecs; ++i) {
+    for (int i = 0; i < kPackVecs; ++i) {
         dptr[i] = nullptr;
         if (base + i * kCopyThreads >= total) continue;
         const int u = unit[i];
@@ -106,7 +111,7 @@ k_dasc_pack(const uint8_t *__restrict__ active, int64_t layer_stride, int S_act,
         dptr[i] = dst_base + (int64_t)pv[i] * unit_bytes + (int64_t)offv[i] * 16;
     }
 #pragma unroll
-    for (int i = 0; i < kCopyVecs; ++i)
+    for (int i = 0; i < kPackVecs; ++i)
         if (dptr[i]) st_nt(reinterpret_cast<u32x4 *>(dptr[i]), buf[i]);
 }
 
@@ -124,16 +129,16 @@ k_dasc_restore(const uint8_t *__restrict__ packed, int S_ckpt, int R_total,
         return;
     }
     const uint32_t total = (uint32_t)L * (uint32_t)n_units * unit_vecs.d;
-    const uint32_t base = blockIdx.x * (kCopyThreads * kCopyVecs) + threadIdx.x;
+    const uint32_t base = blockIdx.x * (kCopyThreads * kRestoreVecs) + threadIdx.x;
     const uint8_t *src_base = packed + (int64_t)src * R_total * unit_bytes;
     uint8_t *dst_base = active_out + (int64_t)dst * n_units * unit_bytes;
 
     // three stages, as in k_dasc_pack: lookups (with the destinations), loads, stores
-    int pos[kCopyVecs];
-    uint32_t offv[kCopyVecs];
-    uint8_t *dptr[kCopyVecs];
+    int pos[kRestoreVecs];
+    uint32_t offv[kRestoreVecs];
+    uint8_t *dptr[kRestoreVecs];
 #pragma unroll
-    for (int i = 0; i < kCopyVecs; ++i) {
+    for (int i = 0; i < kRestoreVecs; ++i) {
         const uint32_t e = base + i * kCopyThreads;
         dptr[i] = nullptr;
         pos[i] = -1;
@@ -146,9 +151,9 @@ k_dasc_restore(const uint8_t *__restrict__ packed, int S_ckpt, int R_total,
         dptr[i] = dst_base + (int64_t)l * layer_stride + (int64_t)u * unit_bytes +
                   (int64_t)offv[i] * 16;
     }
-    u32x4 buf[kCopyVecs];
+    u32x4 buf[kRestoreVecs];
 #pragma unroll
-    for (int i = 0; i < kCopyVecs; ++i) {
+    for (int i = 0; i < kRestoreVecs; ++i) {
         buf[i] = u32x4{0u, 0u, 0u, 0u};
         if (pos[i] >= 0) {
             if (pos[i] < R_total)
@@ -159,7 +164,7 @@ k_dasc_restore(const uint8_t *__restrict__ packed, int S_ckpt, int R_total,
         }
     }
 #pragma unroll
-    for (int i = 0; i < kCopyVecs; ++i)
+    for (int i = 0; i < kRestoreVecs; ++i)
         if (dptr[i]) st_nt(reinterpret_cast<u32x4 *>(dptr[i]), buf[i]);
 }
 
@@ -197,15 +202,15 @@ k_dasc_copy_units(const uint8_t *__restrict__ scratch, int64_t scratch_stride, i
         return;
     }
     const uint32_t total = (uint32_t)R_local * unit_vecs.d;
-    const uint32_t base = blockIdx.x * (kCopyThreads * kCopyVecs) + threadIdx.x;
+    const uint32_t base = blockIdx.x * (kCopyThreads * kUnitCopyVecs) + threadIdx.x;
     const uint8_t *src_base = scratch + (int64_t)src * n_units * unit_bytes;
     uint8_t *dst_base = active + (int64_t)dst * n_units * unit_bytes;
 
     // three stages, as in k_dasc_pack: unit lookups, loads, stores
-    int unit[kCopyVecs], layer[kCopyVecs];
-    uint32_t offv[kCopyVecs];
+    int unit[kUnitCopyVecs], layer[kUnitCopyVecs];
+    uint32_t offv[kUnitCopyVecs];
 #pragma unroll
-    for (int i = 0; i < kCopyVecs; ++i) {
+    for (int i = 0; i < kUnitCopyVecs; ++i) {
         const uint32_t e = base + i * kCopyThreads;
         unit[i] = -1;
         if (e >= total) continue;
@@ -214,10 +219,10 @@ k_dasc_copy_units(const uint8_t *__restrict__ scratch, int64_t scratch_stride, i
         layer[i] = layer_of(offs, L, p);
         unit[i] = unit_index[p];
     }
-    u32x4 buf[kCopyVecs];
-    uint8_t *dptr[kCopyVecs];
+    u32x4 buf[kUnitCopyVecs];
+    uint8_t *dptr[kUnitCopyVecs];
 #pragma unroll
-    for (int i = 0; i < kCopyVecs; ++i) {
+    for (int i = 0; i < kUnitCopyVecs; ++i) {
         dptr[i] = nullptr;
         if (base + i * kCopyThreads >= total) continue;
         const int u = unit[i];
@@ -231,7 +236,7 @@ k_dasc_copy_units(const uint8_t *__restrict__ scratch, int64_t scratch_stride, i
         dptr[i] = dst_base + layer[i] * layer_stride + unit_off;
     }
 #pragma unroll
-    for (int i = 0; i < kCopyVecs; ++i)
+    for (int i = 0; i < kUnitCopyVecs; ++i)
         if (dptr[i]) st_nt(reinterpret_cast<u32x4 *>(dptr[i]), buf[i]);
 }
 
@@ -407,8 +412,8 @@ int dasc_pack(const void *active, int64_t layer_stride_bytes, int S_act, int L, 
     if (N == 0 || R_total == 0) return HLA_OK;
     const hla::FastDiv uv = hla::make_fastdiv((uint32_t)(unit_bytes / 16));
     const uint64_t total = (uint64_t)R_total * uv.d;
-    const unsigned bx = (unsigned)((total + hla::kCopyThreads * hla::kCopyVecs - 1) /
-                                   (hla::kCopyThreads * hla::kCopyVecs));
+    const unsigned bx = (unsigned)((total + hla::kCopyThreads * hla::kPackVecs - 1) /
+                                   (hla::kCopyThreads * hla::kPackVecs));
     hipStream_t st = static_cast<hipStream_t>(stream);
     for (int p0 = 0; p0 < N; p0 += (int)hla::kMaxGridY) {
         const unsigned by = (unsigned)std::min<int>(N - p0, (int)hla::kMaxGridY);
@@ -432,8 +437,8 @@ int dasc_restore(const void *packed, int S_ckpt, int R_total, const int32_t *uni
     const hla::FastDiv uv = hla::make_fastdiv((uint32_t)(unit_bytes / 16));
     const hla::FastDiv un = hla::make_fastdiv((uint32_t)n_units);
     const uint64_t total = (uint64_t)L * n_units * uv.d;
-    const unsigned bx = (unsigned)((total + hla::kCopyThreads * hla::kCopyVecs - 1) /
-                                   (hla::kCopyThreads * hla::kCopyVecs));
+    const unsigned bx = (unsigned)((total + hla::kCopyThreads * hla::kRestoreVecs - 1) /
+                                   (hla::kCopyThreads * hla::kRestoreVecs));
     hipStream_t st = static_cast<hipStream_t>(stream);
     for (int p0 = 0; p0 < N; p0 += (int)hla::kMaxGridY) {
         const unsigned by = (unsigned)std::min<int>(N - p0, (int)hla::kMaxGridY);
@@ -472,8 +477,8 @@ int dasc_refresh_local(const void *scratch, int64_t scratch_layer_stride_bytes, 
     if (N == 0 || R_local == 0) return HLA_OK;
     const hla::FastDiv uv = hla::make_fastdiv((uint32_t)(unit_bytes / 16));
     const uint64_t total = (uint64_t)R_local * uv.d;
-    const unsigned bx = (unsigned)((total + hla::kCopyThreads * hla::kCopyVecs - 1) /
-                                   (hla::kCopyThreads * hla::kCopyVecs));
+    const unsigned bx = (unsigned)((total + hla::kCopyThreads * hla::kUnitCopyVecs - 1) /
+                                   (hla::kCopyThreads * hla::kUnitCopyVecs));
     hipStream_t st = static_cast<hipStream_t>(stream);
     for (int p0 = 0; p0 < N; p0 += (int)hla::kMaxGridY) {
         const unsigned by = (unsigned)std::min<int>(N - p0, (int)hla::kMaxGridY);
