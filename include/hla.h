@@ -306,9 +306,12 @@ HLA_API int replay_accepted_bonus(float *state, int n_slots, const int32_t *slot
  * verify_drafts -- the recurrent layer's part of the target model's verify
  * pass over K draft tokens ([K3] "Speculative decoding without state
  * snapshots": the committed state must not absorb drafts that may be
- * rejected).  For every request, the committed state is advanced through all
- * K draft tokens in order in registers and the readout after each token is
- * written to out[b, t]; the state in memory is only read.  The same
+ * rejected).  For every request, out[b, t] is the readout after the committed
+ * state has been advanced through draft tokens 0..t in order; the state in
+ * memory is only read.  The kernel evaluates the drafts in unrolled form (the
+ * state enters only through S^T [c_t k_t | c_t q_t], c_t the cumulative decay,
+ * computed on the matrix cores in FP32), so the readouts equal a token-by-token
+ * replay's up to FP32 summation order, not bit for bit.  The same
  * projections, kept by the caller, are what replay_accepted later replays.
  *
  * state    device float32 [n_slots, H, dk, dv], read only.
