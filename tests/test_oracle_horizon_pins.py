@@ -178,3 +178,18 @@ def test_refresh_local_copies_local_units_only(orc):
     assert np.array_equal(out[:, untouched], active[:, untouched])
     out2 = orc.dasc_refresh_local(scratch, active.copy(), np.zeros_like(local), src, dst)
     assert np.array_equal(out2, active)
+
+
+def test_refresh_local_all_local_is_a_slot_copy(orc):
+    """With every unit local the copy-back is a whole-slot copy from scratch into the
+    active slot (numpy slice assignment), per layer; other slots untouched."""
+    g = rng(76)
+    L, S_, n_units, ub = 2, 3, 5, 48
+    scratch = g.integers(0, 256, size=(L, S_, n_units, ub), dtype=np.uint8)
+    active = g.integers(0, 256, size=(L, S_ + 2, n_units, ub), dtype=np.uint8)
+    local = np.ones((L, n_units), np.uint8)
+    src = np.array([2, 0], np.int32)
+    dst = np.array([4, 1], np.int32)
+    want = active.copy()
+    want[:, dst] = scratch[:, src]
+    assert np.array_equal(orc.dasc_refresh_local(scratch, active.copy(), local, src, dst), want)
