@@ -45,38 +45,6 @@ __device__ __forceinline__ T ld_nt(const T *p) { return __builtin_nontemporal_lo
 template <typename T>
 __device__ __forceinline__ void st_nt(T *p, T v) { __builtin_nontemporal_store(v, p); }
 
-// Load N consecutive input elements (fp32 or bf16 bits) as float.  The
-// address must be 16-byte aligned; N a multiple of 4 (fp32) or 8 (bf16).
-template <int N>
-__device__ __forceinline__ void load_in(const float *p, float (&d)[N])
-{
-    static_assert(N % 4 == 0, "fp32 rows load in 16-byte pieces");
-#pragma unroll
-    for (int i = 0; i < N / 4; ++i) {
-        f32x4 t = reinterpret_cast<const f32x4 *>(p)[i];
-        d[4 * i + 0] = t.x; d[4 * i + 1] = t.y; d[4 * i + 2] = t.z; d[4 * i + 3] = t.w;
-    }
-}
-
-template <int N>
-__device__ __forceinline__ void load_in(const uint16_t *p, float (&d)[N])
-{
-    if constexpr (N % 8 == 0) {
-#pragma unroll
-        for (int i = 0; i < N / 8; ++i) {
-            u32x4 t = reinterpret_cast<const u32x4 *>(p)[i];
-            d[8 * i + 0] = bf16_lo(t.x); d[8 * i + 1] = bf16_hi(t.x);
-            d[8 * i + 2] = bf16_lo(t.y); d[8 * i + 3] = bf16_hi(t.y);
-            d[8 * i + 4] = bf16_lo(t.z); d[8 * i + 5] = bf16_hi(t.z);
-            d[8 * i + 6] = bf16_lo(t.w); d[8 * i + 7] = bf16_hi(t.w);
-        }
-    } else {
-        static_assert(N == 4, "bf16 rows load in 8- or 16-byte pieces");
-        u32x2 t = *reinterpret_cast<const u32x2 *>(p);
-        d[0] = bf16_lo(t.x); d[1] = bf16_hi(t.x); d[2] = bf16_lo(t.y); d[3] = bf16_hi(t.y);
-    }
-}
-
 __device__ __forceinline__ float load_one(const float *p) { return *p; }
 __device__ __forceinline__ float load_one(const uint16_t *p) { return __uint_as_float((uint32_t)*p << 16); }
 
