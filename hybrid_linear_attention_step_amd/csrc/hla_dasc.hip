@@ -3,9 +3,9 @@
 // App. B): pack the retained units of active slots into a flat checkpoint
 // buffer, and restore a checkpoint into private slots with the omitted units
 // zero-filled.  Both are pure byte movement, so they are written as 16-byte
-// vector streams: grid.y = (src, dst) pair, grid.x = 4 KiB-per-wave chunks of
-// that pair's bytes, four 16-byte vectors in flight per lane, nontemporal
-// loads and stores (each byte is touched once).  The ragged index arithmetic
+// vector streams: grid.y = (src, dst) pair, grid.x = chunks of that pair's
+// bytes (two or four 16-byte vectors per lane, see below), nontemporal loads
+// and stores (each byte is touched once).  The ragged index arithmetic
 // (vector -> unit, unit -> layer) uses precomputed magic-number division and
 // a binary search over the L+1 layer offsets held in LDS.
 //
