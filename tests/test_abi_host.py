@@ -315,3 +315,17 @@ def test_selection_and_int8_validation(L):
         == ALIAS
     assert L.dasc_refresh_local(*dict(cb, unit_bytes=65540).values()) == ALIGN
 
+
+
+def test_binding_rejects_host_tensors_and_bad_dtypes():
+    """The Python binding refuses CPU tensors and wrong element types before any call
+    into the library (nothing here touches a GPU)."""
+    torch = pytest.importorskip("torch")
+    import hybrid_linear_attention_step_amd as hla
+
+    z = lambda *s, **kw: torch.zeros(*s, **kw)  # noqa: E731
+    st = z(2, 2, 64, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        hla.gdn_step(st, z(2, 2, 64), z(2, 2, 64), z(2, 2, 64), z(2, 2), z(2, 2))
+    with pytest.raises(ValueError):
+        hla.damp_quantize(z(2, 2, 64, 64, dtype=torch.float64), None, 8)
