@@ -178,3 +178,64 @@ def test_dasc_wr_flow(kind):
     gm = glob[:, None, :, None].expand(shape)
     assert torch.equal(a2[gm], c2[gm])
     assert torch.equal(a2[~gm], s2[~gm])
+
+
+def test_gdn_checkpoint_workload_head_units():
+    """4 layers x 512 request states x 32 heads of 128 x 128 FP32 (4 GiB), the seeded
+    ragged head selection (64 of 128 heads): INT8 pack of all 512 states, restore into
+    512 private slots.  Every retained value within half a quantisation step (plus the
+    GPU quantiser's rounding slack), every omitted head zero; 3 sampled pairs against the
+    oracle."""
+    hla = need_gpu()
+    cfg = synth.CONFIGS["dasc_gdn"]
+    mask = synth.dasc_masks(cfg)
+    offsets, unit_index, unit_pos, R = hla.dasc_plan(mask)
+    L, S_, nu, ur, dv = cfg.L, cfg.slots, cfg.H, cfg.dk, cfg.dv
+    gen = torch.Generator(device="cuda").manual_seed(cfg.seed)
+    act = torch.randn((L, S_, nu, ur, dv), device="cuda", generator=gen) * 0.05
+    codes = torch.empty((S_, R, ur, dv), dtype=torch.int8, device="cuda")
+    scales = torch.empty((S_, R, ur), device="cuda")
+    ids = dev(np.arange(S_, dtype=np.int32))
+    stride = S_ * nu * ur * dv * 4
+    hla.dasc_pack_int8(act, stride, S_, L, nu, ur, dv, dev(offsets), dev(unit_index), R, ids, ids,
+                       codes, scales, S_)
+    out = torch.full_like(act, float("nan"))
+    hla.dasc_restore_int8(codes, scales, S_, R, dev(unit_pos.reshape(-1)), L, nu, ur, dv, ids,
+                          ids, out, stride, S_)
+    keep = torch.from_numpy(mask.astype(bool)).cuda()[:, None, :, None, None].expand_as(act)
+    step = act.abs().amax(-1, keepdim=True) / 127
+    bound = (0.5 + 5e-5) * step + act.abs() * 2.0 ** -23
+    assert bool(((out - act).abs() <= bound)[keep].all())
+    assert bool((out[~keep] == 0).all())
+    g = np.random.default_rng(4)
+    for s in g.choice(S_, size=3, replace=False):
+        a_s = act[:, s:s + 1].cpu().numpy()
+        c_o, s_o = oracle.dasc_pack_int8(a_s, offsets, unit_index, np.zeros(1, np.int32),
+                                         np.zeros(1, np.int32), 1)
+        assert np.array_equal(scales[s].cpu().numpy(), s_o[0])
+        diff = np.abs(codes[s].cpu().numpy().astype(int) - c_o[0].astype(int))
+        assert diff.max() <= 1 and (diff > 0).mean() <= CODE_FRAC
+
+
+def test_kda_refresh_local_workload():
+    """The dasc-wr copy-back at the KDA checkpoint workload (512 states, 12,260 local
+    channel rows of 16,384 over 4 layers): local rows take the scratch values, global
+    rows keep theirs, bit for bit, over the whole 4 GiB."""
+    hla = need_gpu()
+    cfg = synth.CONFIGS["dasc_kda"]
+    A, d = synth.gate_params(cfg)
+    _, m3 = hla.dasc_static_horizon(A, d, hla.GATE_SOFTPLUS, cfg.a_s, cfg.W_max)
+    mask = m3.reshape(cfg.L, cfg.H * cfg.dk)
+    lo_off, lo_idx, _, R_loc = hla.dasc_plan(1 - mask)
+    L, S_, nu, dv = cfg.L, cfg.slots, cfg.H * cfg.dk, cfg.dv
+    gen = torch.Generator(device="cuda").manual_seed(cfg.seed + 1)
+    scratch = torch.randn((L, S_, nu, dv), device="cuda", generator=gen)
+    active = torch.randn((L, S_, nu, dv), device="cuda", generator=gen)
+    before = active.clone()
+    ids = dev(np.arange(S_, dtype=np.int32))
+    stride = S_ * nu * dv * 4
+    hla.dasc_refresh_local(scratch, stride, S_, active, stride, S_, L, nu, dv * 4, dev(lo_off),
+                           dev(lo_idx), R_loc, ids, ids)
+    loc = torch.from_numpy((1 - mask).astype(bool)).cuda()[:, None, :, None].expand_as(active)
+    assert torch.equal(active[loc], scratch[loc])
+    assert torch.equal(active[~loc], before[~loc])
