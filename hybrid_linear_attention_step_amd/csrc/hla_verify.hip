@@ -59,8 +59,20 @@ constexpr int kPairChunks = 16;  // key-channel chunks of the pair sums
 
 __host__ __device__ constexpr int verify_nb(int K) { return K <= 8 ? 1 : 2; }
 
+// LDS strides chosen against bank conflicts (32 banks of 4 bytes): a staged
+// draft row (k, q, per-channel decay) is dk + 16 floats, so the pair sums' 16
+// lanes of one draft and the next draft's 16 lanes fall on different halves
+// of the banks; an r0 / p0 row is dv + 4 floats, so the matrix-core output
+// lanes of different right-hand columns start on different banks; a B-operand
+// group (16 key channels, 64 lanes x 16 bytes) is 260 floats, and lane l's 16
+// bytes sit in slot l ^ 2 (l / 16), so the writes of the 64 channels of a wave
+// (which differ in group and in l / 16) spread over all banks while every
+// matrix-core read is still one whole contiguous group.
 template <int DK, int DV, bool VEC>
 struct VerifyLds {
+    static constexpr int KS = DK + 16;   // staged draft row
+    static constexpr int RS = DV + 4;    // r0 / p0 row
+    static constexpr int XG = 64 * 4 + 4;  // B-operand group of 16 key channels
     // float offsets into the dynamic LDS block for K drafts.  r0 / p0 (phases
     // 3-4) reuse the staging area of k, q and the decay (phases 1-2).
     int k, q, a, r0, p0, v, b, xb, pg, pe;
@@ -68,19 +80,22 @@ struct VerifyLds {
     __host__ __device__ VerifyLds(int K)
     {
         k = 0;
-        q = k + K * DK;
-        a = q + K * DK;
-        const int staged = a + (VEC ? K * DK : 16);
+        q = k + K * KS;
+        a = q + K * KS;
+        const int staged = a + (VEC ? K * KS : 16);
         r0 = 0;
-        p0 = K * DV;
-        v = staged > 2 * K * DV ? staged : 2 * K * DV;
+        p0 = K * RS;
+        v = staged > 2 * K * RS ? staged : 2 * K * RS;
         b = v + K * DV;
         xb = b + 16;                                  // 16-byte aligned
-        pg = xb + verify_nb(K) * DK * 16;
+        pg = xb + verify_nb(K) * (DK / 16) * XG;
         pe = pg + K * K * kPairChunks;
         total = pe + K * K * kPairChunks;
     }
 };
+
+// B-operand slot of matrix-core lane l (see VerifyLds)
+__device__ __forceinline__ int xb_slot(int l) { return l ^ ((l >> 4) << 1); }
 
 template <int DK, int DV, typename TIn, typename TOut, bool VEC, int NB>
 __global__ void __launch_bounds__(2 * DV) __attribute__((amdgpu_waves_per_eu(5)))
@@ -90,6 +105,8 @@ k_verify(const float *__restrict__ state, int n_slots, const int32_t *__restrict
          int32_t *__restrict__ err)
 {
     constexpr int NT = 2 * DV, NS = DK / 4, CH = DK / kPairChunks, KP = 8 * NB;
+    constexpr int KS = VerifyLds<DK, DV, VEC>::KS, RS = VerifyLds<DK, DV, VEC>::RS;
+    constexpr int XG = VerifyLds<DK, DV, VEC>::XG;
     extern __shared__ f32x4 verify_lds[];
     float *L = reinterpret_cast<float *>(verify_lds);
     const VerifyLds<DK, DV, VEC> at(K);
@@ -141,11 +158,11 @@ k_verify(const float *__restrict__ state, int n_slots, const int32_t *__restrict
     }
 #pragma unroll
     for (int j = 0; j < JK; ++j) {
-        const int e = tid + j * NT;
-        if (e < K * DK) {
-            L[at.k + e] = rk[j];
-            L[at.q + e] = rq_[j];
-            if (VEC) L[at.a + e] = ra[j];
+        const int e = tid + j * NT, t = e / DK, i = e - t * DK;
+        if (t < K) {
+            L[at.k + t * KS + i] = rk[j];
+            L[at.q + t * KS + i] = rq_[j];
+            if (VEC) L[at.a + t * KS + i] = ra[j];
         }
     }
 #pragma unroll
@@ -159,35 +176,36 @@ k_verify(const float *__restrict__ state, int n_slots, const int32_t *__restrict
     }
     __syncthreads();
     // c_t k_t and c_t q_t of key channel i into the B-operand layout: right-hand
-    // column g of row i goes to block nb = g / 16, step group i / 16, lane
-    // 16 (i % 4) + g % 16, component (i / 4) % 4
+    // column g of row i is lane l = 16 (i % 4) + g % 16 of group (g / 16, i / 16),
+    // component (i / 4) % 4, stored in slot xb_slot(l)
     for (int i = tid; i < DK; i += NT) {
         float c = 1.0f;
-        const int base = (i >> 4) * 64 + ((i & 3) << 4), comp = (i >> 2) & 3;
+        const int grp = i >> 4, kk = i & 3, comp = (i >> 2) & 3;
         for (int t = 0; t < KP; ++t) {
             float xk = 0.0f, xq = 0.0f;
             if (t < K) {
-                c *= VEC ? L[at.a + t * DK + i] : L[at.a + t];
-                xk = c * L[at.k + t * DK + i];
-                xq = c * L[at.q + t * DK + i];
+                c *= VEC ? L[at.a + t * KS + i] : L[at.a + t];
+                xk = c * L[at.k + t * KS + i];
+                xq = c * L[at.q + t * KS + i];
             }
             const int gk = t, gq = KP + t;
-            L[at.xb + (((gk >> 4) * (DK / 16) * 64 + base + (gk & 15)) << 2) + comp] = xk;
-            L[at.xb + (((gq >> 4) * (DK / 16) * 64 + base + (gq & 15)) << 2) + comp] = xq;
+            L[at.xb + ((gk >> 4) * (DK / 16) + grp) * XG + 4 * xb_slot(16 * kk + (gk & 15)) + comp] = xk;
+            L[at.xb + ((gq >> 4) * (DK / 16) + grp) * XG + 4 * xb_slot(16 * kk + (gq & 15)) + comp] = xq;
         }
     }
 
     // 2. the pair sums while the tile arrives
+    // (chunk ch takes key channels ch, ch + 16, ch + 32, ...: the 16 lanes of one
+    // draft read 16 consecutive floats)
     for (int it = tid; it < K * kPairChunks; it += NT) {
         const int s0 = it / kPairChunks, ch = it - s0 * kPairChunks;
-        const int i0 = ch * CH;
         float ks[CH], w[CH];
         float e_ss = 0.0f;
 #pragma unroll
         for (int m = 0; m < CH; ++m) {
-            ks[m] = L[at.k + s0 * DK + i0 + m];
+            ks[m] = L[at.k + s0 * KS + ch + kPairChunks * m];
             w[m] = 1.0f;
-            e_ss = fmaf(ks[m], L[at.q + s0 * DK + i0 + m], e_ss);
+            e_ss = fmaf(ks[m], L[at.q + s0 * KS + ch + kPairChunks * m], e_ss);
         }
         L[at.pe + (s0 * K + s0) * kPairChunks + ch] = e_ss;
         // t runs to the compile-time KP (skipping t <= s0 and t >= K) so that the
@@ -198,10 +216,11 @@ k_verify(const float *__restrict__ state, int n_slots, const int32_t *__restrict
             float g = 0.0f, e2 = 0.0f;
 #pragma unroll
             for (int m = 0; m < CH; ++m) {
-                w[m] *= VEC ? L[at.a + t * DK + i0 + m] : L[at.a + t];
+                const int i = ch + kPairChunks * m;
+                w[m] *= VEC ? L[at.a + t * KS + i] : L[at.a + t];
                 const float kw = ks[m] * w[m];
-                g = fmaf(kw, L[at.k + t * DK + i0 + m], g);
-                e2 = fmaf(kw, L[at.q + t * DK + i0 + m], e2);
+                g = fmaf(kw, L[at.k + t * KS + i], g);
+                e2 = fmaf(kw, L[at.q + t * KS + i], e2);
             }
             L[at.pg + (s0 * K + t) * kPairChunks + ch] = g;
             L[at.pe + (s0 * K + t) * kPairChunks + ch] = e2;
@@ -223,7 +242,7 @@ k_verify(const float *__restrict__ state, int n_slots, const int32_t *__restrict
         f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int g4 = 0; g4 < DK / 16; ++g4) {
-            const f32x4 bq = XB[(nb * (DK / 16) + g4) * 64 + lane];
+            const f32x4 bq = XB[(nb * (DK / 16) + g4) * (XG / 4) + xb_slot(lane)];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(x[4 * g4 + j][0], bq[j], acc0, 0, 0, 0);
@@ -232,7 +251,7 @@ k_verify(const float *__restrict__ state, int n_slots, const int32_t *__restrict
         }
         const int g = 16 * nb + cm, typ = g >= KP, t = g - typ * KP;
         if (t < K) {
-            float *dst = L + (typ ? at.p0 : at.r0) + t * DV + wave * 32 + 8 * rq;
+            float *dst = L + (typ ? at.p0 : at.r0) + t * RS + wave * 32 + 8 * rq;
             reinterpret_cast<f32x4 *>(dst)[0] = f32x4{acc0[0], acc1[0], acc0[1], acc1[1]};
             reinterpret_cast<f32x4 *>(dst)[1] = f32x4{acc0[2], acc1[2], acc0[3], acc1[3]};
         }
@@ -260,8 +279,8 @@ k_verify(const float *__restrict__ state, int n_slots, const int32_t *__restrict
         for (int t = 0; t < KP; ++t) {
             r[t] = o[t] = vv[t] = u[t] = 0.0f;
             if (t < K) {
-                r[t] = L[at.r0 + t * DV + tid];
-                o[t] = L[at.p0 + t * DV + tid];
+                r[t] = L[at.r0 + t * RS + tid];
+                o[t] = L[at.p0 + t * RS + tid];
                 vv[t] = L[at.v + t * DV + tid];
             }
         }
