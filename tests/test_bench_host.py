@@ -1,0 +1,62 @@
+"""Host-side contract of bench.py (no GPU): the single-GPU refusal, the algorithmic byte
+counts the roofline divides by (recounted here from the per-head layouts), and the rule
+that a counter-derived traffic figure is only used for the kernel source it was taken on."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr and p.stdout == ""
+
+
+def test_step_bytes_recounted_per_head():
+    # batch 256 x 32 heads x 128 x 128 FP32 state, bf16 q/k/v, fp32 decay/beta/readout
+    heads = 256 * 32
+    state = 128 * 128 * 4                      # 65,536 B per head, read and written
+    inputs = 3 * 128 * 2                       # q, k, v in bf16
+    gdn = heads * (2 * state + inputs + 4 + 4 + 128 * 4)
+    kda = heads * (2 * state + inputs + 128 * 4 + 4 + 128 * 4)
+    assert bench.step_bytes(256, 32, 128, 128, 2, False) == gdn == 1_084_293_120
+    assert bench.step_bytes(256, 32, 128, 128, 2, True) == kda == 1_088_454_656
+
+
+def test_damp_bytes_recounted_per_head():
+    heads = 256 * 32
+    # K_hi = 16 FP16 rows, 112 INT8 rows with one FP32 scale each: 18,880 B per head
+    packed = 16 * 128 * 2 + 112 * 128 + 112 * 4
+    assert packed == 18_880
+    per_row = heads * (2 * packed + 3 * 128 * 2 + 128 * 4 + 4 + 128 * 4)
+    assert bench.damp_bytes(256, 32, 128, 128, 16, 2, True) == per_row == 324_042_752
+    # group-32 scales (4 per INT8 row) and the value tables (c' and pi, 32 x 128 x 8 B once)
+    packed32 = 16 * 128 * 2 + 112 * (128 + 4 * 4)
+    g32 = heads * (2 * packed32 + 3 * 128 * 2 + 128 * 4 + 4 + 128 * 4) + 32 * 128 * 8
+    assert bench.damp_bytes(256, 32, 128, 128, 16, 2, True, 32, True) == g32
+
+
+def test_speculative_bytes_recounted():
+    n = np.array([0, 3, 8, 1], np.int32)
+    H, dk, dv = 2, 64, 32
+    tok_in = (2 * dk + dv) * 4 + 4 + 4           # fp32 q, k, v, scalar decay, beta
+    # replay: states with at least one accepted token read + written, accepted tokens'
+    # inputs read and readouts written
+    assert bench.replay_bytes(n, H, dk, dv, 4) == 3 * H * 2 * dk * dv * 4 + 12 * H * (tok_in + dv * 4)
+    # verify: every state read once, every draft's inputs read and readout written
+    assert bench.verify_bytes(4, 8, H, dk, dv, 4) == 4 * H * dk * dv * 4 + 4 * 8 * H * (tok_in + dv * 4)
+    # replay + bonus: every state read + written, accepted inputs read, bonus in + out
+    assert bench.bonus_bytes(n, H, dk, dv, 4) == (4 * H * 2 * dk * dv * 4 + 12 * H * tok_in
+                                                  + 4 * H * (tok_in + dv * 4))
+
+
+def test_traffic_only_for_the_profiled_source():
+    assert bench.traffic_from_profile("gdn_step", ["bench.py"]) is None
+    assert bench.traffic_from_profile("no_such_kernel", bench.STEP_SOURCES) is None
