@@ -369,6 +369,18 @@ k_dasc_restore_int8(const int8_t *__restrict__ codes, const float *__restrict__ 
     }
     uint32_t w0[P], w1[P];
     float sc[P];
+    // With one row per lane (head units: a workgroup's rows share one unit) an
+    // omitted row's zeros go out right behind its lookup, ahead of any load:
+    // 5.88 -> 6.12 TB/s on the GDN checkpoint workload.  With two rows per lane
+    // (channel-row units) the same order measured 12% slower (the compiler then
+    // splits the rows' loads apart), so there the zeros stay in the last stage.
+    constexpr bool zeros_first = P == 1;
+    if constexpr (zeros_first) {
+        if (live[0] && pos[0] < 0) {
+            st_nt(reinterpret_cast<f32x4 *>(d[0]), f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+            st_nt(reinterpret_cast<f32x4 *>(d[0] + DV / 2), f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+        }
+    }
 #pragma unroll
     for (int i = 0; i < P; ++i) {
         w0[i] = w1[i] = 0u;
@@ -388,7 +400,7 @@ k_dasc_restore_int8(const int8_t *__restrict__ codes, const float *__restrict__ 
     }
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-        if (!live[i]) continue;
+        if (!live[i] || (zeros_first && pos[i] < 0)) continue;
         float y[8];
         decode_int8(w0[i], w1[i], sc[i], y);  // q * s, one FP32 rounding (0 when omitted)
         st_nt(reinterpret_cast<f32x4 *>(d[i]), f32x4{y[0], y[1], y[2], y[3]});
