@@ -371,9 +371,10 @@ k_dasc_restore_int8(const int8_t *__restrict__ codes, const float *__restrict__ 
     float sc[P];
     // With one row per lane (head units: a workgroup's rows share one unit) an
     // omitted row's zeros go out right behind its lookup, ahead of any load:
-    // 5.88 -> 6.12 TB/s on the GDN checkpoint workload.  With two rows per lane
-    // (channel-row units) the same order measured 12% slower (the compiler then
-    // splits the rows' loads apart), so there the zeros stay in the last stage.
+    // 5.88 -> 6.1 TB/s on the GDN checkpoint workload.  With two rows per lane
+    // (channel-row units, a wave mixing omitted and retained rows) the same order
+    // measured 12% slower, a wave's zero stores delaying its loads, so there the
+    // zeros stay in the last stage.
     constexpr bool zeros_first = P == 1;
     if constexpr (zeros_first) {
         if (live[0] && pos[0] < 0) {
