@@ -1,0 +1,108 @@
+"""Seeded random configurations of the checkpoint kernels against the oracle: layer
+count, units per layer, unit size, keep probability (empty and full masks included),
+checkpoint / private slot maps.  FP32 pack / restore bit-exact; INT8 pack: scales
+bit-exact, codes off by at most 1 on at most 0.1% of values; INT8 restore of the oracle's
+checkpoint bit-exact.  Slots no pair names keep their sentinel bytes."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import dev, host, need_gpu, torch
+
+pytestmark = pytest.mark.gpu
+N_CASES = 10
+CODE_FRAC = 1e-3
+
+
+def _keep(g):
+    u = g.random()
+    return 0.0 if u < 0.1 else 1.0 if u < 0.2 else float(g.uniform(0.05, 0.95))
+
+
+def _maps(g, S_src, S_dst):
+    N = int(g.integers(1, min(S_src, S_dst) + 1))
+    return (g.permutation(S_src)[:N].astype(np.int32), g.permutation(S_dst)[:N].astype(np.int32))
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_pack_restore_fp32(i):
+    hla = need_gpu()
+    g = np.random.default_rng(7100 + i)
+    ub = int(g.choice([16, 48, 512, 1040, 4096, 65536]))
+    L = int(g.integers(1, 6))
+    n_units = int(g.integers(1, 41 if ub <= 4096 else 5))
+    S_act = int(g.integers(1, 7))
+    active = g.integers(0, 256, size=(L, S_act, n_units, ub), dtype=np.uint8)
+    mask = (g.random((L, n_units)) < _keep(g)).astype(np.uint8)
+    offsets, unit_index, unit_pos, R = hla.dasc_plan(mask)
+    S_ckpt = S_act + int(g.integers(0, 3))
+    src, dst = _maps(g, S_act, S_ckpt)
+    packed = torch.full((max(S_ckpt * R * ub, 16),), 0xCD, dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    act_d = dev(active.reshape(-1))
+    hla.dasc_pack(act_d, S_act * n_units * ub, S_act, L, n_units, ub, dev(offsets),
+                  dev(unit_index), R, dev(src), dev(dst), packed, S_ckpt, err_flag=err)
+    ref = oracle.dasc_pack(active, offsets, unit_index, src, dst, S_ckpt)
+    got = host(packed)[: S_ckpt * R * ub].reshape(S_ckpt, R, ub)
+    for d_ in dst:
+        assert np.array_equal(got[d_], ref[d_])
+    others = sorted(set(range(S_ckpt)) - set(dst.tolist()))
+    assert (got[others] == 0xCD).all()
+    S_dst = S_act + int(g.integers(0, 3))
+    src2, dst2 = _maps(g, S_ckpt, S_dst)
+    out0 = g.integers(0, 256, size=(L, S_dst, n_units, ub), dtype=np.uint8)
+    out = dev(out0.reshape(-1))
+    ckpt = dev(ref.reshape(-1)) if R else dev(np.zeros(16, np.uint8))  # no unit kept: any buffer
+    hla.dasc_restore(ckpt, S_ckpt, R, dev(unit_pos.reshape(-1)), L, n_units, ub,
+                     dev(src2), dev(dst2), out, S_dst * n_units * ub, S_dst, err_flag=err)
+    ref_out = out0.copy()
+    oracle.dasc_restore(ref, offsets, unit_index, L, n_units, src2, dst2, ref_out)
+    assert np.array_equal(host(out).reshape(ref_out.shape), ref_out)
+    assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_pack_restore_int8(i):
+    hla = need_gpu()
+    g = np.random.default_rng(7200 + i)
+    unit_rows = int(g.choice([1, 2, 4, 8, 128]))
+    dv = int(g.choice([64, 128]))
+    L = int(g.integers(1, 5))
+    n_units = int(g.integers(1, 41 if unit_rows <= 8 else 6))
+    S_ = int(g.integers(1, 6))
+    act = (g.standard_normal((L, S_, n_units, unit_rows, dv)) * g.uniform(0.01, 2.0)).astype(
+        np.float32)
+    mask = (g.random((L, n_units)) < _keep(g)).astype(np.uint8)
+    offsets, unit_index, unit_pos, R = hla.dasc_plan(mask)
+    S_ckpt = S_ + int(g.integers(0, 3))
+    src, dst = _maps(g, S_, S_ckpt)
+    codes = torch.full((max(S_ckpt * R * unit_rows * dv, 16),), 99, dtype=torch.int8,
+                       device="cuda")
+    scales = torch.full((max(S_ckpt * R * unit_rows, 4),), -1.0, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hla.dasc_pack_int8(dev(act), S_ * n_units * unit_rows * dv * 4, S_, L, n_units, unit_rows,
+                       dv, dev(offsets), dev(unit_index), R, dev(src), dev(dst), codes, scales,
+                       S_ckpt, err_flag=err)
+    c_o, s_o = oracle.dasc_pack_int8(act, offsets, unit_index, src, dst, S_ckpt)
+    n_c, n_s = S_ckpt * R * unit_rows * dv, S_ckpt * R * unit_rows
+    c_g = host(codes)[:n_c].reshape(c_o.shape)
+    s_g = host(scales)[:n_s].reshape(s_o.shape)
+    for d_ in dst:
+        assert np.array_equal(s_g[d_], s_o[d_])
+        diff = np.abs(c_g[d_].astype(int) - c_o[d_].astype(int))
+        assert diff.max(initial=0) <= 1 and (diff.size == 0 or (diff > 0).mean() <= CODE_FRAC)
+    others = [s for s in range(S_ckpt) if s not in dst]
+    assert (c_g[others] == 99).all() and (s_g[others] == -1.0).all()
+    S_dst = S_ + int(g.integers(0, 3))
+    src2, dst2 = _maps(g, S_ckpt, S_dst)
+    out0 = np.full((L, S_dst, n_units, unit_rows, dv), 3.5, np.float32)
+    out = dev(out0)
+    hla.dasc_restore_int8(dev(c_o.reshape(-1)) if R else dev(np.zeros(16, np.int8)),  # R = 0:
+                          dev(s_o.reshape(-1)) if R else dev(np.zeros(4, np.float32)),  # any buffer
+                          S_ckpt, R, dev(unit_pos.reshape(-1)), L, n_units, unit_rows, dv,
+                          dev(src2), dev(dst2), out, S_dst * n_units * unit_rows * dv * 4, S_dst,
+                          err_flag=err)
+    ref = oracle.dasc_restore_int8(c_o, s_o, offsets, unit_index, L, n_units, src2, dst2,
+                                   out0.copy())
+    assert np.array_equal(host(out), ref)
+    assert int(err.item()) == 0
