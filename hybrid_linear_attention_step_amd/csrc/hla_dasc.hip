@@ -281,7 +281,7 @@ k_dasc_pack_int8(const uint8_t *__restrict__ active, int64_t layer_stride, int S
     // three stages, so that no stage waits on a later one's memory (the wave's
     // memory counter is in order): unit lookups, row loads, quantise + stores
     constexpr int P = kInt8PassesPack;
-    bool live[P];
+    bool live[P], skip[P];
     int unit[P], layer[P];
     uint32_t rrv[P];
 #pragma unroll
@@ -300,12 +300,16 @@ k_dasc_pack_int8(const uint8_t *__restrict__ active, int64_t layer_stride, int S
 #pragma unroll
     for (int i = 0; i < P; ++i) {
         out_row[i] = 0;
+        skip[i] = false;
         if (!live[i]) continue;
         const uint32_t r = rrv[i] & row_mask;
         int u = unit[i];
         if (u < 0 || u >= n_units) {
+            // the row's lanes still load (unit 0) and exchange their maximum together;
+            // nothing is stored for it, and the flag reports the plan
             if (err) atomicOr(err, HLA_DEVERR_PLAN);
-            u = 0;  // keep the lanes of the row together; the flag reports the plan
+            u = 0;
+            skip[i] = true;
         }
         const float *row = reinterpret_cast<const float *>(
             src_base + layer[i] * layer_stride + ((((int64_t)u << log2_rows) + r) * DV) * 4);
@@ -321,6 +325,7 @@ k_dasc_pack_int8(const uint8_t *__restrict__ active, int64_t layer_stride, int S
         const float amax = max_low_lane_bits<LCG>(row_absmax8(x[i]));
         uint32_t w0, w1;
         const float s = encode_int8(x[i], amax, w0, w1);
+        if (skip[i]) continue;
         int8_t *crow = codes + (int64_t)out_row[i] * DV;
         st_nt(reinterpret_cast<uint32_t *>(crow + cg * 4), w0);
         st_nt(reinterpret_cast<uint32_t *>(crow + DV / 2 + cg * 4), w1);

@@ -71,7 +71,8 @@ enum hla_decay { HLA_DECAY_SCALAR = 0, HLA_DECAY_VECTOR = 1 };
 enum hla_device_error {
     HLA_DEVERR_SLOT = 1,    /* slot / src / dst index >= its bound: pair skipped */
     HLA_DEVERR_ACCEPT = 2,  /* n_accept outside [0, K]: clamped                  */
-    HLA_DEVERR_PLAN = 4     /* plan table entry out of range: unit skipped       */
+    HLA_DEVERR_PLAN = 4     /* plan table entry out of range: unit skipped (a
+                               restore writes that unit as zeros)               */
 };
 
 /* Static, NUL-terminated description of a status code.  Thread-safe. */
@@ -245,7 +246,8 @@ HLA_API int dasc_pack(const void *active, int64_t layer_stride_bytes, int S_act,
  * unit_pos    device int32 [L * n_units] from dasc_plan.
  * active_out  device, layer l at active_out + l * layer_stride_bytes, each
  *             layer [S_dst, n_units, unit_bytes].
- * Errors: as dasc_pack. */
+ * Errors: as dasc_pack; a unit_pos entry >= R_total sets HLA_DEVERR_PLAN and
+ * that unit is written as zeros. */
 HLA_API int dasc_restore(const void *packed, int S_ckpt, int R_total, const int32_t *unit_pos,
                  int L, int n_units, int64_t unit_bytes, const int32_t *src_slot,
                  const int32_t *dst_slot, int N, void *active_out,

@@ -239,3 +239,65 @@ def test_kda_refresh_local_workload():
     loc = torch.from_numpy((1 - mask).astype(bool)).cuda()[:, None, :, None].expand_as(active)
     assert torch.equal(active[loc], scratch[loc])
     assert torch.equal(active[~loc], before[~loc])
+
+
+@pytest.mark.parametrize("unit_rows", [1, 128])
+def test_int8_device_errors(unit_rows):
+    """Bad device-side indices in the INT8 checkpoint kernels: a source or destination
+    slot past its bound sets HLA_DEVERR_SLOT and skips that pair only; a unit_index entry
+    past the units sets HLA_DEVERR_PLAN; a unit_pos entry past the packed rows sets
+    HLA_DEVERR_PLAN and that unit is restored as zeros, every other unit as the oracle's
+    restore (channel rows and head units take different kernel paths)."""
+    hla = need_gpu()
+    g = np.random.default_rng(4400 + unit_rows)
+    L, S_, n_units, dv = 2, 3, 6, 128
+    act = (g.standard_normal((L, S_, n_units, unit_rows, dv)) * 0.05).astype(np.float32)
+    mask = np.ones((L, n_units), np.uint8)
+    mask[0, 2] = 0
+    offsets, unit_index, unit_pos, R = hla.dasc_plan(mask)
+    stride = _stride(S_, n_units, unit_rows, dv)
+    codes = torch.zeros((S_, R, unit_rows, dv), dtype=torch.int8, device="cuda")
+    scales = torch.zeros((S_, R, unit_rows), device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    # pack: pair 1 names a source slot past S_act; pair 0 is packed as the oracle packs it
+    hla.dasc_pack_int8(dev(act), stride, S_, L, n_units, unit_rows, dv, dev(offsets),
+                       dev(unit_index), R, dev(np.array([1, 9], np.int32)),
+                       dev(np.array([0, 2], np.int32)), codes, scales, S_, err_flag=err)
+    assert int(err.item()) == hla.DEVERR_SLOT
+    c_o, s_o = oracle.dasc_pack_int8(act, offsets, unit_index, np.array([1], np.int32),
+                                     np.array([0], np.int32), S_)
+    assert np.array_equal(host(scales)[0], s_o[0])
+    assert (host(codes)[2] == 0).all() and (host(scales)[2] == 0).all()
+    err.zero_()
+    bad_index = unit_index.copy()
+    bad_index[1] = n_units + 3
+    hla.dasc_pack_int8(dev(act), stride, S_, L, n_units, unit_rows, dv, dev(offsets),
+                       dev(bad_index), R, dev(np.array([0], np.int32)),
+                       dev(np.array([1], np.int32)), codes, scales, S_, err_flag=err)
+    assert int(err.item()) == hla.DEVERR_PLAN
+    # that packed position is left as it was (zeros here); the others hold the pack
+    c1, s1 = oracle.dasc_pack_int8(act, offsets, unit_index, np.array([0], np.int32),
+                                   np.array([1], np.int32), S_)
+    s1[1, 1] = 0.0
+    c1[1, 1] = 0
+    assert np.array_equal(host(scales)[1], s1[1])
+    assert (host(codes)[1, 1] == 0).all()
+    # restore of the oracle's checkpoint with one unit_pos entry past R_total, and a second
+    # pair whose destination slot is past S_dst
+    c_o, s_o = oracle.dasc_pack_int8(act, offsets, unit_index, np.array([1], np.int32),
+                                     np.array([0], np.int32), S_)
+    bad_pos = unit_pos.reshape(-1).copy()
+    bad_u = n_units + 4                        # layer 1, unit 4: retained
+    assert bad_pos[bad_u] >= 0
+    bad_pos[bad_u] = R + 7
+    out0 = np.full((L, S_, n_units, unit_rows, dv), 3.5, np.float32)
+    out = dev(out0)
+    err.zero_()
+    hla.dasc_restore_int8(dev(c_o), dev(s_o), S_, R, dev(bad_pos), L, n_units, unit_rows, dv,
+                          dev(np.array([0, 0], np.int32)), dev(np.array([2, 5], np.int32)), out,
+                          stride, S_, err_flag=err)
+    assert int(err.item()) == hla.DEVERR_PLAN | hla.DEVERR_SLOT
+    ref = oracle.dasc_restore_int8(c_o, s_o, offsets, unit_index, L, n_units,
+                                   np.array([0], np.int32), np.array([2], np.int32), out0.copy())
+    ref[1, 2, 4] = 0.0                          # the unit with the bad position reads as zeros
+    assert np.array_equal(host(out), ref)
