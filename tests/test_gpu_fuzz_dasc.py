@@ -106,3 +106,62 @@ def test_random_pack_restore_int8(i):
                                    out0.copy())
     assert np.array_equal(host(out), ref)
     assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_random_refresh_local(i):
+    """The dasc-wr copy-back of the local units (the inverted mask's plan) from scratch
+    slots into active slots, bit-exact; every other byte of the active state untouched."""
+    hla = need_gpu()
+    g = np.random.default_rng(7300 + i)
+    ub = int(g.choice([16, 48, 512, 1040, 4096]))
+    L, n_units = int(g.integers(1, 5)), int(g.integers(1, 41))
+    S_s, S_a = int(g.integers(1, 5)), int(g.integers(1, 7))
+    scratch = g.integers(0, 256, size=(L, S_s, n_units, ub), dtype=np.uint8)
+    active = g.integers(0, 256, size=(L, S_a, n_units, ub), dtype=np.uint8)
+    local = 1 - (g.random((L, n_units)) < _keep(g)).astype(np.uint8)
+    offsets, unit_index, _, R_local = hla.dasc_plan(local)
+    src, dst = _maps(g, S_s, S_a)
+    act_d = dev(active.reshape(-1))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hla.dasc_refresh_local(dev(scratch.reshape(-1)), S_s * n_units * ub, S_s, act_d,
+                           S_a * n_units * ub, S_a, L, n_units, ub, dev(offsets),
+                           dev(unit_index), R_local, dev(src), dev(dst), err_flag=err)
+    ref = oracle.dasc_refresh_local(scratch, active.copy(), local, src, dst)
+    assert np.array_equal(host(act_d).reshape(active.shape), ref)
+    assert int(err.item()) == 0
+
+
+def test_refresh_local_device_errors():
+    """A pair whose scratch or active slot is past its bound is skipped (HLA_DEVERR_SLOT);
+    a local-plan entry past the units is skipped (HLA_DEVERR_PLAN); the rest is copied."""
+    hla = need_gpu()
+    g = np.random.default_rng(7399)
+    L, S_s, S_a, n_units, ub = 2, 3, 4, 9, 64
+    scratch = g.integers(0, 256, size=(L, S_s, n_units, ub), dtype=np.uint8)
+    active = g.integers(0, 256, size=(L, S_a, n_units, ub), dtype=np.uint8)
+    local = np.zeros((L, n_units), np.uint8)
+    local[0, [1, 4]] = 1
+    local[1, [0, 8]] = 1
+    offsets, unit_index, _, R_local = hla.dasc_plan(local)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    act_d = dev(active.reshape(-1))
+    src, dst = np.array([0, 7, 1], np.int32), np.array([2, 0, 9], np.int32)
+    hla.dasc_refresh_local(dev(scratch.reshape(-1)), S_s * n_units * ub, S_s, act_d,
+                           S_a * n_units * ub, S_a, L, n_units, ub, dev(offsets),
+                           dev(unit_index), R_local, dev(src), dev(dst), err_flag=err)
+    assert int(err.item()) == hla.DEVERR_SLOT
+    ref = oracle.dasc_refresh_local(scratch, active.copy(), local, src[:1], dst[:1])
+    assert np.array_equal(host(act_d).reshape(active.shape), ref)
+    # a plan entry naming unit 12 of 9: that unit is skipped, the others are copied
+    bad = unit_index.copy()
+    bad[2] = 12                                # layer 1's first local unit (unit 0)
+    act2 = dev(active.reshape(-1))
+    err.zero_()
+    hla.dasc_refresh_local(dev(scratch.reshape(-1)), S_s * n_units * ub, S_s, act2,
+                           S_a * n_units * ub, S_a, L, n_units, ub, dev(offsets), dev(bad),
+                           R_local, dev(src[:1]), dev(dst[:1]), err_flag=err)
+    assert int(err.item()) == hla.DEVERR_PLAN
+    ref2 = ref.copy()
+    ref2[1, 2, 0] = active[1, 2, 0]            # not copied
+    assert np.array_equal(host(act2).reshape(active.shape), ref2)
