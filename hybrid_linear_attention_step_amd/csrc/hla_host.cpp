@@ -11,6 +11,14 @@ namespace hla {
 
 static const size_t kMaxIndex = (size_t)INT_MAX;
 
+// Products and sums of sizes in int64, refused (false) where they would overflow.
+static bool mul_ok(int64_t a, int64_t b, int64_t &out) { return !__builtin_mul_overflow(a, b, &out); }
+static bool mul3_ok(int64_t a, int64_t b, int64_t c, int64_t &out)
+{
+    int64_t t;
+    return mul_ok(a, b, t) && mul_ok(t, c, out);
+}
+
 int check_step(const StepArgs &a)
 {
     const bool multi = a.mode != MODE_STEP;
@@ -27,7 +35,8 @@ int check_step(const StepArgs &a)
     if (bonus && (!a.qb || !a.kb || !a.vb || !a.alpha_b || !a.beta_b)) return HLA_ERR_NULL;
     if (!a.slot && a.n_slots < a.B) return HLA_ERR_SHAPE;
     if (!head_dim_ok(a.dk) || !head_dim_ok(a.dv)) return HLA_ERR_UNSUPPORTED;
-    if ((size_t)a.B * a.H > kMaxIndex) return HLA_ERR_SHAPE;
+    if ((size_t)a.B * a.H > kMaxIndex || (size_t)a.n_slots * a.H > kMaxIndex)
+        return HLA_ERR_SHAPE;
     const bool vec = a.decay == HLA_DECAY_VECTOR;
     if (!aligned16(a.state) || !aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v) ||
         (a.out && !aligned16(a.out)) || (vec && !aligned16(a.alpha)))
@@ -78,7 +87,8 @@ int check_damp(const DampArgs &a)
         !a.alpha || !a.beta)
         return HLA_ERR_NULL;
     if (!a.slot && a.n_slots < a.B) return HLA_ERR_SHAPE;
-    if ((size_t)a.B * a.H > kMaxIndex) return HLA_ERR_SHAPE;
+    if ((size_t)a.B * a.H > kMaxIndex || (size_t)a.n_slots * a.H > kMaxIndex)
+        return HLA_ERR_SHAPE;
     if ((a.hi && !aligned16(a.hi)) || (a.lo && !aligned16(a.lo)) || !aligned16(a.q) ||
         !aligned16(a.k) || !aligned16(a.v) || (a.out && !aligned16(a.out)))
         return HLA_ERR_ALIGN;
@@ -164,14 +174,19 @@ int check_dasc(const void *active, int64_t layer_stride_bytes, int S_act, int L,
         return HLA_ERR_NULL;
     if (unit_bytes % 16 != 0 || layer_stride_bytes % 16 != 0) return HLA_ERR_ALIGN;
     if (!aligned16(active) || !aligned16(packed)) return HLA_ERR_ALIGN;
-    const int64_t layer_bytes = (int64_t)S_act * n_units * unit_bytes;
-    if (L > 1 && layer_stride_bytes < layer_bytes) return HLA_ERR_SHAPE;
     // per-pair vector counts must fit the kernels' 32-bit indexing
     const int64_t unit_vecs = unit_bytes / 16;
-    const int64_t per_pair = unit_vecs * (int64_t)L * n_units;
-    if (per_pair > (int64_t)INT_MAX || unit_vecs > (int64_t)INT_MAX) return HLA_ERR_SHAPE;
-    Range act{active, (size_t)((L - 1) * layer_stride_bytes + layer_bytes)};
-    Range pk{packed, (size_t)S_ckpt * R_total * unit_bytes};
+    int64_t per_pair, layer_bytes, span, pk_bytes;
+    if (!mul3_ok(unit_vecs, L, n_units, per_pair) || per_pair > (int64_t)INT_MAX)
+        return HLA_ERR_SHAPE;
+    if (!mul3_ok(S_act, n_units, unit_bytes, layer_bytes)) return HLA_ERR_SHAPE;
+    if (L > 1 && layer_stride_bytes < layer_bytes) return HLA_ERR_SHAPE;
+    if (!mul_ok(L - 1, layer_stride_bytes, span) ||
+        __builtin_add_overflow(span, layer_bytes, &span) ||
+        !mul3_ok(S_ckpt, R_total, unit_bytes, pk_bytes))
+        return HLA_ERR_SHAPE;
+    Range act{active, (size_t)span};
+    Range pk{packed, (size_t)pk_bytes};
     if (overlaps(act, pk)) return HLA_ERR_ALIAS;
     return HLA_OK;
 }
@@ -192,12 +207,18 @@ int check_dasc_int8(const void *active, int64_t layer_stride_bytes, int S_act, i
     if (rc != HLA_OK || N == 0) return rc;
     if (!scales) return HLA_ERR_NULL;
     if ((reinterpret_cast<uintptr_t>(scales) & 3u) != 0) return HLA_ERR_ALIGN;
-    // checkpoint rows must fit the kernels' 32-bit row indexing
-    if ((int64_t)S_ckpt * R_total * unit_rows > (int64_t)INT_MAX) return HLA_ERR_SHAPE;
-    const int64_t layer_bytes = (int64_t)S_act * n_units * unit_bytes;
-    Range act{active, (size_t)((L - 1) * layer_stride_bytes + layer_bytes)};
-    Range cd{codes, (size_t)S_ckpt * R_total * unit_rows * dv};
-    Range sc{scales, (size_t)S_ckpt * R_total * unit_rows * sizeof(float)};
+    // checkpoint rows must fit the kernels' 32-bit row indexing (so the code and scale
+    // byte counts below fit as well)
+    int64_t ck_rows, layer_bytes, span;
+    if (!mul3_ok(S_ckpt, R_total, unit_rows, ck_rows) || ck_rows > (int64_t)INT_MAX)
+        return HLA_ERR_SHAPE;
+    if (!mul3_ok(S_act, n_units, unit_bytes, layer_bytes) ||
+        !mul_ok(L - 1, layer_stride_bytes, span) ||
+        __builtin_add_overflow(span, layer_bytes, &span))
+        return HLA_ERR_SHAPE;
+    Range act{active, (size_t)span};
+    Range cd{codes, (size_t)ck_rows * dv};
+    Range sc{scales, (size_t)ck_rows * sizeof(float)};
     if (overlaps(act, cd) || overlaps(act, sc) || overlaps(cd, sc)) return HLA_ERR_ALIAS;
     return HLA_OK;
 }
