@@ -181,16 +181,27 @@ HLA_API int damp_step(uint16_t *hi, int8_t *lo, float *lo_scale, int n_slots,
               int out_dtype, int32_t *err_flag, void *stream);
 
 /* damp_quantize -- pack an FP32 state S [n_slots, H, dk, dv] (device, original
- * coordinates) into the three regions above: T = S D^-1 P_V^T (FP32 division),
- * then the same quantiser.  The FP32 input is only read. */
+ * coordinates) into the three regions above: T = S D^-1 P_V^T (FP32 division,
+ * [DAMP] App. A.3 Eq. (17)), then the quantiser of [DAMP] §3.2 Eq. (5)-(6)
+ * for the INT8 groups and nearest-even FP16 for the K_hi selected rows
+ * ([DAMP] §5.2, App. A.4).  The FP32 input is only read; hi, lo and lo_scale
+ * are caller-owned device buffers, entirely written.  Nothing is allocated.
+ * Errors: NULL for a missing buffer the layout needs; SHAPE for n_slots < 0,
+ * H <= 0 or K_hi outside [0, dk]; UNSUPPORTED for dk, dv outside {64, 128}
+ * or a group other than dv or 32; ALIGN for a state, hi or lo pointer that
+ * is not 16-byte aligned; ALIAS when the packed regions overlap the state,
+ * each other or the plan tables.  n_slots == 0 launches nothing. */
 HLA_API int damp_quantize(const float *state, int n_slots, int H, int dk, int dv,
                   const int32_t *key_perm, int K_hi, int group, const int32_t *val_perm,
                   const float *val_scale, uint16_t *hi, int8_t *lo, float *lo_scale,
                   void *stream);
 
 /* damp_dequantize -- reconstruct the FP32 state in original coordinates from
- * the packed regions: FP16 values exactly, INT8 values as code * group scale,
- * then S[i][pi(j)] = T[i][j] * c'_j. */
+ * the packed regions ([DAMP] §3.2, App. A.3 Eq. (17) inverted): FP16 values
+ * exactly, INT8 values as code * group scale (one FP32 rounding), then
+ * S[i][pi(j)] = T[i][j] * c'_j.  The packed regions are only read; state is
+ * a caller-owned device buffer, entirely written.  Errors: as damp_quantize
+ * (ALIAS when the state overlaps a packed region or a plan table). */
 HLA_API int damp_dequantize(const uint16_t *hi, const int8_t *lo, const float *lo_scale,
                     int n_slots, int H, int dk, int dv, const int32_t *key_perm,
                     int K_hi, int group, const int32_t *val_perm, const float *val_scale,
@@ -272,6 +283,8 @@ HLA_API int dasc_restore(const void *packed, int S_ckpt, int R_total, const int3
  * out      device [B, K, H, dv] of out_dtype or NULL: the readout after each
  *          replayed token; rows t >= n_b are left untouched.
  * 1 <= K <= 16.  state, slot, err_flag as gdn_step.
+ * Errors: as gdn_step, plus SHAPE for K outside [1, 16] and NULL for a
+ * missing n_accept.
  * ---------------------------------------------------------------------- */
 HLA_API int replay_accepted(float *state, int n_slots, const int32_t *slot, int B, int H,
                     int dk, int dv, int K, const void *q, const void *k, const void *v,
