@@ -19,6 +19,12 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert "one GPU" in p.stderr and p.stdout == ""
 
 
+def test_unknown_only_names_are_refused():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--only", "gdn,dmap"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode == 2 and "dmap" in p.stderr and p.stdout == ""
+
+
 def test_step_bytes_recounted_per_head():
     # batch 256 x 32 heads x 128 x 128 FP32 state, bf16 q/k/v, fp32 decay/beta/readout
     heads = 256 * 32
