@@ -15,7 +15,7 @@ import os
 
 from ._build import LIB as LIB_PATH
 
-HLA_F32, HLA_BF16 = 0, 1
+HLA_F32, HLA_BF16, HLA_F16 = 0, 1, 2
 DECAY_SCALAR, DECAY_VECTOR = 0, 1
 DEVERR_SLOT, DEVERR_ACCEPT, DEVERR_PLAN = 1, 2, 4
 
@@ -120,12 +120,12 @@ def _dev(t, name, dtypes, ndim=None):
 
 def _code(dtype) -> int:
     torch = _torch()
-    return {torch.float32: HLA_F32, torch.bfloat16: HLA_BF16}[dtype]
+    return {torch.float32: HLA_F32, torch.bfloat16: HLA_BF16, torch.float16: HLA_F16}[dtype]
 
 
 def _in_dtypes():
     torch = _torch()
-    return (torch.float32, torch.bfloat16)
+    return (torch.float32, torch.bfloat16, torch.float16)
 
 
 def _i32():

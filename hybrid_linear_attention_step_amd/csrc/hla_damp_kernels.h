@@ -441,17 +441,19 @@ inline void launch_damp(const DampArgs &a, int32_t *err, hipStream_t st)
 template <class F>
 inline void damp_dispatch(const DampArgs &a, int32_t *err, hipStream_t st)
 {
-    const bool in16 = a.in_dtype == HLA_BF16, out16 = a.out_dtype == HLA_BF16;
     const bool vec = a.decay == HLA_DECAY_VECTOR;
 #define HLA_DAMP_T(DK_, DV_, TI_, TO_)                                                        \
     if (vec) F::template run<DK_, DV_, TI_, TO_, true>(a, err, st);                            \
     else F::template run<DK_, DV_, TI_, TO_, false>(a, err, st);
+#define HLA_DAMP_O(DK_, DV_, TI_)                                                             \
+    if (a.out_dtype == HLA_BF16) { HLA_DAMP_T(DK_, DV_, TI_, uint16_t) }                      \
+    else if (a.out_dtype == HLA_F16) { HLA_DAMP_T(DK_, DV_, TI_, f16_t) }                     \
+    else { HLA_DAMP_T(DK_, DV_, TI_, float) }
 #define HLA_DAMP_S(DK_, DV_)                                                                  \
     if (a.dk == DK_ && a.dv == DV_) {                                                         \
-        if (in16 && out16) { HLA_DAMP_T(DK_, DV_, uint16_t, uint16_t) }                        \
-        else if (in16) { HLA_DAMP_T(DK_, DV_, uint16_t, float) }                               \
-        else if (out16) { HLA_DAMP_T(DK_, DV_, float, uint16_t) }                              \
-        else { HLA_DAMP_T(DK_, DV_, float, float) }                                            \
+        if (a.in_dtype == HLA_BF16) { HLA_DAMP_O(DK_, DV_, uint16_t) }                        \
+        else if (a.in_dtype == HLA_F16) { HLA_DAMP_O(DK_, DV_, f16_t) }                       \
+        else { HLA_DAMP_O(DK_, DV_, float) }                                                   \
         return;                                                                               \
     }
     HLA_DAMP_S(128, 128)
@@ -459,6 +461,7 @@ inline void damp_dispatch(const DampArgs &a, int32_t *err, hipStream_t st)
     HLA_DAMP_S(64, 128)
     HLA_DAMP_S(64, 64)
 #undef HLA_DAMP_S
+#undef HLA_DAMP_O
 #undef HLA_DAMP_T
 }
 

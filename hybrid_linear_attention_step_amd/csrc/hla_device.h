@@ -37,6 +37,27 @@ __device__ __forceinline__ uint32_t f32_to_half_bits(float f)
     return (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)f);
 }
 
+// A binary16 input or output element.  bf16 elements are carried as plain
+// uint16_t bit patterns; this distinct type selects the binary16 conversions.
+struct f16_t {
+    uint16_t bits;
+};
+template <typename T> struct is_f16 { static constexpr bool value = false; };
+template <> struct is_f16<f16_t> { static constexpr bool value = true; };
+
+// The low / high element of a 32-bit word holding two 2-byte inputs of type T
+// (bf16 bits or binary16).
+template <typename T> __device__ __forceinline__ float lo16(uint32_t w)
+{
+    if constexpr (is_f16<T>::value) return half_bits_to_f32(w & 0xffffu);
+    else return bf16_lo(w);
+}
+template <typename T> __device__ __forceinline__ float hi16(uint32_t w)
+{
+    if constexpr (is_f16<T>::value) return half_bits_to_f32(w >> 16);
+    else return bf16_hi(w);
+}
+
 // ------------------------------------------------------------ loads / stores
 
 template <typename T>
@@ -47,8 +68,9 @@ __device__ __forceinline__ void st_nt(T *p, T v) { __builtin_nontemporal_store(v
 
 __device__ __forceinline__ float load_one(const float *p) { return *p; }
 __device__ __forceinline__ float load_one(const uint16_t *p) { return __uint_as_float((uint32_t)*p << 16); }
+__device__ __forceinline__ float load_one(const f16_t *p) { return half_bits_to_f32(p->bits); }
 
-// Store 4 consecutive outputs (fp32: 16 bytes, bf16: 8 bytes).
+// Store 4 consecutive outputs (fp32: 16 bytes, bf16 / binary16: 8 bytes).
 __device__ __forceinline__ void store_out4(float *p, const float (&o)[4])
 {
     f32x4 t = {o[0], o[1], o[2], o[3]};
@@ -60,8 +82,15 @@ __device__ __forceinline__ void store_out4(uint16_t *p, const float (&o)[4])
                f32_to_bf16(o[2]) | (f32_to_bf16(o[3]) << 16)};
     *reinterpret_cast<u32x2 *>(p) = t;
 }
+__device__ __forceinline__ void store_out4(f16_t *p, const float (&o)[4])
+{
+    u32x2 t = {f32_to_half_bits(o[0]) | (f32_to_half_bits(o[1]) << 16),
+               f32_to_half_bits(o[2]) | (f32_to_half_bits(o[3]) << 16)};
+    *reinterpret_cast<u32x2 *>(p) = t;
+}
 __device__ __forceinline__ void store_one(float *p, float o) { *p = o; }
 __device__ __forceinline__ void store_one(uint16_t *p, float o) { *p = (uint16_t)f32_to_bf16(o); }
+__device__ __forceinline__ void store_one(f16_t *p, float o) { p->bits = (uint16_t)f32_to_half_bits(o); }
 
 // ------------------------------------------------------------ lane exchange
 

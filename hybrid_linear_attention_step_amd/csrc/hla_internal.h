@@ -24,8 +24,8 @@ inline bool overlaps(Range a, Range b)
 }
 
 inline bool head_dim_ok(int d) { return d == 64 || d == 128; }
-inline bool dtype_ok(int t) { return t == HLA_F32 || t == HLA_BF16; }
-inline size_t dtype_bytes(int t) { return t == HLA_BF16 ? 2 : 4; }
+inline bool dtype_ok(int t) { return t == HLA_F32 || t == HLA_BF16 || t == HLA_F16; }
+inline size_t dtype_bytes(int t) { return t == HLA_F32 ? 4 : 2; }
 
 // What a step-kernel launch does with its tokens.
 enum StepMode {

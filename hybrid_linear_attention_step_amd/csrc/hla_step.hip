@@ -82,7 +82,7 @@ struct TokenRaw {
     static constexpr int QW = RPL * (int)sizeof(TIn) / 16;  // 16-byte words per row block
     u32x4 k[QW], q[QW];
     u32x4 a[VEC ? RPL / 4 : 1];
-    u32x2 v2;  // bf16 v
+    u32x2 v2;  // 2-byte v (bf16 or binary16)
     u32x4 v4;  // fp32 v
     float a0, b0;
 };
@@ -119,7 +119,8 @@ template <typename TIn>
 __device__ __forceinline__ void token_v(const u32x2 &v2, const u32x4 &v4, float (&vv)[4])
 {
     if constexpr (sizeof(TIn) == 2) {
-        vv[0] = bf16_lo(v2.x); vv[1] = bf16_hi(v2.x); vv[2] = bf16_lo(v2.y); vv[3] = bf16_hi(v2.y);
+        vv[0] = lo16<TIn>(v2.x); vv[1] = hi16<TIn>(v2.x);
+        vv[2] = lo16<TIn>(v2.y); vv[3] = hi16<TIn>(v2.y);
     } else {
         vv[0] = __uint_as_float(v4.x); vv[1] = __uint_as_float(v4.y);
         vv[2] = __uint_as_float(v4.z); vv[3] = __uint_as_float(v4.w);
@@ -127,9 +128,9 @@ __device__ __forceinline__ void token_v(const u32x2 &v2, const u32x4 &v4, float 
 }
 
 // Row m of the lane's k or q block as loaded (the 16-byte words of
-// TokenRaw), converted at the point of use: a bf16 pair shares one register
-// until it is needed, which keeps the step's register count low enough for
-// five waves per SIMD with bf16 inputs.
+// TokenRaw), converted at the point of use: a pair of 2-byte inputs shares one
+// register until it is needed, which keeps the step's register count low
+// enough for five waves per SIMD with bf16 (or binary16) inputs.
 template <typename TIn, int QW>
 __device__ __forceinline__ float raw_row(const u32x4 (&w)[QW], int m)
 {
@@ -137,7 +138,7 @@ __device__ __forceinline__ float raw_row(const u32x4 (&w)[QW], int m)
         const u32x4 &t = w[m / 8];
         const int c = (m % 8) / 2;
         const uint32_t word = c == 0 ? t.x : c == 1 ? t.y : c == 2 ? t.z : t.w;
-        return (m & 1) ? bf16_hi(word) : bf16_lo(word);
+        return (m & 1) ? hi16<TIn>(word) : lo16<TIn>(word);
     } else {
         const u32x4 &t = w[m / 4];
         const int c = m % 4;
@@ -346,12 +347,15 @@ static int launch_decay(const StepArgs &a, int32_t *err, hipStream_t st)
 template <int DK, int DV>
 static int launch_dtypes(const StepArgs &a, int32_t *err, hipStream_t st)
 {
-    const bool in16 = a.in_dtype == HLA_BF16, out16 = a.out_dtype == HLA_BF16;
-    if (in16)
-        return out16 ? launch_decay<DK, DV, uint16_t, uint16_t>(a, err, st)
-                     : launch_decay<DK, DV, uint16_t, float>(a, err, st);
-    return out16 ? launch_decay<DK, DV, float, uint16_t>(a, err, st)
-                 : launch_decay<DK, DV, float, float>(a, err, st);
+    // element types: float (HLA_F32), uint16_t bf16 bits (HLA_BF16), f16_t (HLA_F16)
+#define HLA_STEP_OUT(TI_)                                                                     \
+    return a.out_dtype == HLA_BF16  ? launch_decay<DK, DV, TI_, uint16_t>(a, err, st)        \
+           : a.out_dtype == HLA_F16 ? launch_decay<DK, DV, TI_, f16_t>(a, err, st)           \
+                                    : launch_decay<DK, DV, TI_, float>(a, err, st);
+    if (a.in_dtype == HLA_BF16) { HLA_STEP_OUT(uint16_t) }
+    if (a.in_dtype == HLA_F16) { HLA_STEP_OUT(f16_t) }
+    HLA_STEP_OUT(float)
+#undef HLA_STEP_OUT
 }
 
 static int run_step(const StepArgs &a, int32_t *err, void *stream)

@@ -322,15 +322,18 @@ static int launch_verify(const StepArgs &a, int32_t *err, hipStream_t st)
 template <int DK, int DV>
 static int verify_dtypes(const StepArgs &a, int32_t *err, hipStream_t st)
 {
-    const bool in16 = a.in_dtype == HLA_BF16, out16 = a.out_dtype == HLA_BF16;
     const bool vec = a.decay == HLA_DECAY_VECTOR;
 #define HLA_VERIFY_T(TI_, TO_)                                                                \
     return vec ? launch_verify<DK, DV, TI_, TO_, true>(a, err, st)                            \
                : launch_verify<DK, DV, TI_, TO_, false>(a, err, st);
-    if (in16 && out16) { HLA_VERIFY_T(uint16_t, uint16_t) }
-    if (in16) { HLA_VERIFY_T(uint16_t, float) }
-    if (out16) { HLA_VERIFY_T(float, uint16_t) }
-    HLA_VERIFY_T(float, float)
+#define HLA_VERIFY_OUT(TI_)                                                                   \
+    if (a.out_dtype == HLA_BF16) { HLA_VERIFY_T(TI_, uint16_t) }                              \
+    if (a.out_dtype == HLA_F16) { HLA_VERIFY_T(TI_, f16_t) }                                  \
+    HLA_VERIFY_T(TI_, float)
+    if (a.in_dtype == HLA_BF16) { HLA_VERIFY_OUT(uint16_t) }
+    if (a.in_dtype == HLA_F16) { HLA_VERIFY_OUT(f16_t) }
+    HLA_VERIFY_OUT(float)
+#undef HLA_VERIFY_OUT
 #undef HLA_VERIFY_T
 }
 

@@ -61,8 +61,9 @@ enum hla_status {
     HLA_ERR_LAUNCH = 8       /* the kernel launch failed                       */
 };
 
-/* Element types of q, k, v (in_dtype) and of the readout o (out_dtype). */
-enum hla_dtype { HLA_F32 = 0, HLA_BF16 = 1 };
+/* Element types of q, k, v (in_dtype) and of the readout o (out_dtype): FP32,
+ * bf16, or IEEE binary16; 2-byte outputs are rounded to nearest even. */
+enum hla_dtype { HLA_F32 = 0, HLA_BF16 = 1, HLA_F16 = 2 };
 
 /* Decay granularity: one scalar per head (GDN) or one per key channel (KDA). */
 enum hla_decay { HLA_DECAY_SCALAR = 0, HLA_DECAY_VECTOR = 1 };

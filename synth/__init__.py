@@ -44,12 +44,15 @@ def bf16_bits_to_f32(b) -> np.ndarray:
 
 
 def to_stored(x64: np.ndarray, dtype: str) -> np.ndarray:
-    """Round a float64 draw to its stored representation ('f32' or 'bf16' bits)."""
+    """Round a float64 draw to its stored representation ('f32', 'bf16' bits or 'f16'
+    binary16), through float32, round to nearest even at each step."""
     x32 = x64.astype(np.float32)
     if dtype == "f32":
         return x32
     if dtype == "bf16":
         return f32_to_bf16_bits(x32)
+    if dtype == "f16":
+        return x32.astype(np.float16)
     raise ValueError(dtype)
 
 
@@ -59,6 +62,8 @@ def stored_to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
         return np.asarray(x, np.float32).astype(np.float64)
     if dtype == "bf16":
         return bf16_bits_to_f32(x).astype(np.float64)
+    if dtype == "f16":
+        return np.asarray(x, np.float16).astype(np.float64)
     raise ValueError(dtype)
 
 
@@ -73,7 +78,7 @@ class Config:
     dk: int
     dv: int
     steps: int
-    in_dtype: str  # 'f32' or 'bf16'
+    in_dtype: str  # 'f32', 'bf16' or 'f16'
     decay: str  # 'scalar' (GDN) or 'vector' (KDA)
     alpha_lo: float = 0.90
     alpha_hi: float = 0.9999

@@ -44,7 +44,7 @@ def f64_inputs(x: dict, in_dtype: str) -> dict:
 
 
 def host(t) -> np.ndarray:
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         return t.float().cpu().numpy().astype(np.float64)
     return t.cpu().numpy()
 

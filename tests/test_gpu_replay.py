@@ -20,7 +20,7 @@ def _cfg(kind, dk, dv, in_dtype, B, K, H=3):
 
 
 @pytest.mark.parametrize("kind", ["gdn", "kda"])
-@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (128, 64)])
 def test_replay_matches_oracle_with_clamping(kind, in_dtype, dk, dv):
     hla = need_gpu()

@@ -31,7 +31,7 @@ def _bonus(cfg, layer):
 
 
 @pytest.mark.parametrize("kind", ["gdn", "kda"])
-@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (128, 64), (64, 128)])
 def test_verify_matches_oracle_and_reads_only(kind, in_dtype, dk, dv):
     hla = need_gpu()
@@ -74,7 +74,7 @@ def test_verify_readouts_match_full_acceptance_replay(kind):
 
 
 @pytest.mark.parametrize("kind", ["gdn", "kda"])
-@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128)])
 def test_replay_bonus_matches_oracle(kind, in_dtype, dk, dv):
     hla = need_gpu()

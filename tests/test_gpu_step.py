@@ -41,7 +41,7 @@ def test_gdn_toy_workload_32_steps():
 
 
 @pytest.mark.parametrize("kind", ["gdn", "kda"])
-@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
 def test_ragged_batch_with_slot_map(kind, in_dtype, dk, dv):
     """Odd batch and head counts, a permuted slot map with a padding request, every
@@ -71,20 +71,31 @@ def test_ragged_batch_with_slot_map(kind, in_dtype, dk, dv):
         assert np.array_equal(got[s], S0[s])
 
 
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("kind", ["gdn", "kda"])
-def test_bf16_readout(kind):
+def test_two_byte_readout(kind, out_dtype):
+    """bf16 / binary16 readouts: within one rounding of the oracle, and bit for bit the
+    round-to-nearest-even of the same step's FP32 readout (run on a copy of the state)."""
     hla = need_gpu()
     cfg = synth.shrink(synth.CONFIGS[f"{kind}_serving"], B=4, H=8)
     S64 = synth.initial_state(cfg).astype(np.float64)
     st = dev(synth.initial_state(cfg))
+    tdt = torch.bfloat16 if out_dtype == "bf16" else torch.float16
+    rel = 2.0 ** -8 if out_dtype == "bf16" else 2.0 ** -11
     for step in range(3):
         x = synth.step_inputs(cfg, step)
-        out = torch.empty((cfg.B, cfg.H, cfg.dv), dtype=torch.bfloat16, device="cuda")
-        _run(hla, kind, st, dev_inputs(x, cfg.in_dtype), out=out)
+        xd = dev_inputs(x, cfg.in_dtype)
+        st32 = st.clone()
+        o32 = _run(hla, kind, st32, xd)
+        out = torch.empty((cfg.B, cfg.H, cfg.dv), dtype=tdt, device="cuda")
+        _run(hla, kind, st, xd, out=out)
         o_ref = _orc(kind, S64, f64_inputs(x, cfg.in_dtype))
         o = host(out)
-        bound = 2.0 ** -8 * np.abs(o_ref) + TOL * np.abs(o_ref).max(axis=-1, keepdims=True)
+        bound = (rel * np.abs(o_ref) + TOL * np.abs(o_ref).max(axis=-1, keepdims=True)
+                 + 2.0 ** -24)
         assert (np.abs(o - o_ref) <= bound).all()
+        assert torch.equal(out, o32.to(tdt))   # torch's casts round to nearest even
+        assert torch.equal(st, st32)
 
 
 @pytest.mark.parametrize("name", ["gdn_serving", "kda_serving"])
