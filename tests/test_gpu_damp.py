@@ -90,6 +90,19 @@ def test_step_teacher_forced(decay, dk, dv, K_hi, use_perm):
     _assert_bars(w)
 
 
+@pytest.mark.parametrize("in_dtype", ["f32", "f16"])
+def test_step_teacher_forced_input_types(in_dtype):
+    """FP32 and IEEE binary16 projections (the serving shape's inputs are bf16) through
+    the serving layout (K_hi = 16 of 128, per-channel decay, permuted plan)."""
+    hla = need_gpu()
+    base = synth.CONFIGS["damp_kda"]
+    cfg = synth.shrink(base, B=5, H=3, in_dtype=in_dtype, seed=base.seed + 404)
+    perm = _perm(np.random.default_rng(404), cfg.H, cfg.dk)
+    slot = np.array([3, -1, 0, 5, 1], np.int32)
+    w = _teacher_forced(hla, cfg, perm, steps=4, slot=slot, n_slots=6)
+    _assert_bars(w)
+
+
 def test_workload_plan_teacher_forced():
     """The mixed-precision workload's own plan (16 FP16 rows per head biased to slow
     decay), 32 heads, bf16 inputs, per-channel decay."""
