@@ -243,7 +243,7 @@ const char *hla_status_str(int status)
     }
 }
 
-int hla_version(void) { return 100; }
+int hla_version(void) { return 101; }
 
 // Ragged plan ([dasc] App. B, Scheme 2): r_l retained units per layer,
 // o_0 = 0, o_{l+1} = o_l + r_l, retained units of layer l at flat positions

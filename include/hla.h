@@ -79,7 +79,7 @@ enum hla_device_error {
 /* Static, NUL-terminated description of a status code.  Thread-safe. */
 HLA_API const char *hla_status_str(int status);
 
-/* Library ABI version (major * 100 + minor). */
+/* Library ABI version (major * 100 + minor): 101 (1.01 added HLA_F16). */
 HLA_API int hla_version(void);
 
 /* -------------------------------------------------------------------------
