@@ -92,35 +92,8 @@ def _torch():
     return torch
 
 
-def _stream(stream):
-    torch = _torch()
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
-
-
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
-
-
-def _dev(t, name, dtypes, ndim=None):
-    torch = _torch()
-    if not isinstance(t, torch.Tensor):
-        raise TypeError(f"{name}: expected a torch.Tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name}: must be a GPU tensor, got {t.device}")
-    if t.dtype not in dtypes:
-        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name}: must be contiguous")
-    if ndim is not None and t.dim() != ndim:
-        raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
-    return t
-
-
-def _code(dtype) -> int:
-    torch = _torch()
-    return {torch.float32: HLA_F32, torch.bfloat16: HLA_BF16, torch.float16: HLA_F16}[dtype]
 
 
 def _in_dtypes():
@@ -136,86 +109,181 @@ def _f32():
     return (_torch().float32,)
 
 
-def _opt_out(out, shape, device, want_out):
+def _code(dtype) -> int:
     torch = _torch()
-    if out is None and want_out:
-        out = torch.empty(shape, dtype=torch.float32, device=device)
-    if out is not None:
-        _dev(out, "out", _in_dtypes(), len(shape))
+    return {torch.float32: HLA_F32, torch.bfloat16: HLA_BF16, torch.float16: HLA_F16}[dtype]
+
+
+class _Args:
+    """The tensor arguments of one call, checked before anything reaches the library.
+
+    Element type, contiguity and the full shape (or, for byte-level buffers, the size)
+    are checked as each tensor is added; devices are checked together by on_gpu() once
+    every shape has passed, so that a mis-shaped tensor is reported as such whatever
+    device it is on.  The library sizes every access from the sizes it is given, so a
+    tensor smaller than those sizes, or one in host memory, would be read or written out
+    of bounds by a kernel: both are refused here."""
+
+    def __init__(self, fn: str):
+        self.fn = fn
+        self.ts = []
+
+    def _fail(self, exc, msg):
+        raise exc(f"{self.fn}: {msg}")
+
+    def t(self, x, name, dtypes=None, shape=None, ndim=None, optional=False):
+        """A tensor of one of `dtypes` (None: any), contiguous, of exactly `shape` (None
+        entries match any size) or with `ndim` dimensions.  Returns x (None when optional
+        and absent)."""
+        torch = _torch()
+        if x is None:
+            if optional:
+                return None
+            self._fail(ValueError, f"{name} is required")
+        if not isinstance(x, torch.Tensor):
+            self._fail(TypeError, f"{name}: expected a torch.Tensor, got {type(x).__name__}")
+        if dtypes is not None and x.dtype not in dtypes:
+            self._fail(TypeError, f"{name}: dtype {x.dtype} not in {dtypes}")
+        if not x.is_contiguous():
+            self._fail(ValueError, f"{name}: must be contiguous")
+        if shape is not None:
+            ndim = len(shape)
+        if ndim is not None and x.dim() != ndim:
+            self._fail(ValueError, f"{name}: expected {ndim} dimensions, got shape "
+                                   f"{tuple(x.shape)}")
+        if shape is not None and any(e is not None and int(e) != int(g)
+                                     for e, g in zip(shape, x.shape)):
+            want = tuple("*" if e is None else int(e) for e in shape)
+            self._fail(ValueError, f"{name}: expected shape {want}, got {tuple(x.shape)}")
+        self.ts.append((name, x))
+        return x
+
+    def nbytes(self, x, name, need, dtypes=None, optional=False):
+        """A contiguous buffer of at least `need` bytes (any shape)."""
+        x = self.t(x, name, dtypes, optional=optional)
+        if x is not None and need > 0 and x.numel() * x.element_size() < need:
+            self._fail(ValueError, f"{name}: {x.numel() * x.element_size()} bytes, the call "
+                                   f"addresses {need}")
+        return x
+
+    def flag(self, x):
+        """The optional device error flag: int32, at least one element."""
+        x = self.t(x, "err_flag", _i32(), optional=True)
+        if x is not None and x.numel() < 1:
+            self._fail(ValueError, "err_flag: needs one int32 element")
+        return x
+
+    def on_gpu(self, stream=None):
+        """Every tensor on one GPU, the one the launch stream belongs to."""
+        torch = _torch()
+        for name, x in self.ts:
+            if x.device.type != "cuda":
+                self._fail(ValueError, f"{name}: must be a GPU tensor, got {x.device}")
+        devs = {x.device for _, x in self.ts}
+        if len(devs) > 1:
+            self._fail(ValueError, f"tensors on several devices: {sorted(map(str, devs))}")
+        if devs:
+            d = next(iter(devs))
+            sd = (stream.device if stream is not None
+                  else torch.device("cuda", torch.cuda.current_device()))
+            if d != sd:
+                self._fail(ValueError, f"tensors on {d}, launch stream on {sd}")
+
+    def stream(self, stream):
+        self.on_gpu(stream)
+        if stream is None:
+            stream = _torch().cuda.current_stream()
+        return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _alpha_shape(lead, decay_kind, dk):
+    """Decay shape: one scalar per head, or one per key channel; None (left to the library,
+    which refuses the code) for an unknown decay kind."""
+    if decay_kind == DECAY_SCALAR:
+        return lead
+    if decay_kind == DECAY_VECTOR:
+        return lead + (dk,)
+    return None
+
+
+def _decay_arg(a, x, name, lead, decay_kind, dk):
+    shape = _alpha_shape(lead, decay_kind, dk)
+    return a.t(x, name, _f32(), shape=shape) if shape is not None else a.t(x, name, _f32())
+
+
+def _new_out(out, shape, like):
+    if out is None:
+        out = _torch().empty(shape, dtype=_torch().float32, device=like.device)
     return out
 
 
-def _step(name, state, q, k, v, alpha, beta, out, slot, err_flag, stream, want_out):
-    _dev(state, "state", _f32(), 4)
+def _step(name, decay_kind, state, q, k, v, alpha, beta, out, slot, err_flag, stream,
+          want_out):
+    a = _Args(name)
+    a.t(state, "state", _f32(), ndim=4)
     S, H, dk, dv = state.shape
-    _dev(q, "q", _in_dtypes(), 3)
+    a.t(q, "q", _in_dtypes(), shape=(None, H, dk))
     B = q.shape[0]
-    _dev(k, "k", (q.dtype,), 3)
-    _dev(v, "v", (q.dtype,), 3)
-    _dev(alpha, "alpha", _f32())
-    _dev(beta, "beta", _f32(), 2)
-    if slot is not None:
-        _dev(slot, "slot", _i32(), 1)
-    if err_flag is not None:
-        _dev(err_flag, "err_flag", _i32())
-    out = _opt_out(out, (B, H, dv), state.device, want_out)
+    a.t(k, "k", (q.dtype,), shape=(B, H, dk))
+    a.t(v, "v", (q.dtype,), shape=(B, H, dv))
+    _decay_arg(a, alpha, "alpha", (B, H), decay_kind, dk)
+    a.t(beta, "beta", _f32(), shape=(B, H))
+    a.t(slot, "slot", _i32(), shape=(B,), optional=True)
+    a.flag(err_flag)
+    a.t(out, "out", _in_dtypes(), shape=(B, H, dv), optional=True)
+    st = a.stream(stream)
+    if want_out:
+        out = _new_out(out, (B, H, dv), state)
     _call(name, _ptr(state), S, _ptr(slot), B, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
           _code(q.dtype), _ptr(alpha), _ptr(beta), _ptr(out),
-          _code(out.dtype) if out is not None else HLA_F32, _ptr(err_flag), _stream(stream))
+          _code(out.dtype) if out is not None else HLA_F32, _ptr(err_flag), st)
     return out
 
 
 def gdn_step(state, q, k, v, alpha, beta, out=None, slot=None, err_flag=None, stream=None,
              want_out=True):
-    """GDN decode step in place on `state` [S,H,dk,dv] fp32; returns o [B,H,dv]."""
-    return _step("gdn_step", state, q, k, v, alpha, beta, out, slot, err_flag, stream, want_out)
+    """GDN decode step in place on `state` [S,H,dk,dv] fp32 (alpha [B,H]); returns o
+    [B,H,dv]."""
+    return _step("gdn_step", DECAY_SCALAR, state, q, k, v, alpha, beta, out, slot, err_flag,
+                 stream, want_out)
 
 
 def kda_step(state, q, k, v, alpha, beta, out=None, slot=None, err_flag=None, stream=None,
              want_out=True):
     """KDA decode step (alpha [B,H,dk]) in place on `state`; returns o [B,H,dv]."""
-    return _step("kda_step", state, q, k, v, alpha, beta, out, slot, err_flag, stream, want_out)
+    return _step("kda_step", DECAY_VECTOR, state, q, k, v, alpha, beta, out, slot, err_flag,
+                 stream, want_out)
+
+
+def _drafts(a, state, q, k, v, alpha, beta, decay_kind, slot, err_flag):
+    """Shared checks of the multi-token entry points; returns (S, H, dk, dv, B, K)."""
+    a.t(state, "state", _f32(), ndim=4)
+    S, H, dk, dv = state.shape
+    a.t(q, "q", _in_dtypes(), shape=(None, None, H, dk))
+    B, K = q.shape[:2]
+    a.t(k, "k", (q.dtype,), shape=(B, K, H, dk))
+    a.t(v, "v", (q.dtype,), shape=(B, K, H, dv))
+    _decay_arg(a, alpha, "alpha", (B, K, H), decay_kind, dk)
+    a.t(beta, "beta", _f32(), shape=(B, K, H))
+    a.t(slot, "slot", _i32(), shape=(B,), optional=True)
+    a.flag(err_flag)
+    return S, H, dk, dv, B, K
 
 
 def replay_accepted(state, q, k, v, alpha, beta, n_accept, decay_kind, out=None, slot=None,
                     err_flag=None, stream=None, want_out=True):
     """Replay the first n_accept[b] of K cached draft projections into each state."""
-    _dev(state, "state", _f32(), 4)
-    S, H, dk, dv = state.shape
-    _dev(q, "q", _in_dtypes(), 4)
-    B, K = q.shape[:2]
-    _dev(k, "k", (q.dtype,), 4)
-    _dev(v, "v", (q.dtype,), 4)
-    _dev(alpha, "alpha", _f32())
-    _dev(beta, "beta", _f32(), 3)
-    _dev(n_accept, "n_accept", _i32(), 1)
-    if slot is not None:
-        _dev(slot, "slot", _i32(), 1)
-    if err_flag is not None:
-        _dev(err_flag, "err_flag", _i32())
-    out = _opt_out(out, (B, K, H, dv), state.device, want_out)
+    a = _Args("replay_accepted")
+    S, H, dk, dv, B, K = _drafts(a, state, q, k, v, alpha, beta, decay_kind, slot, err_flag)
+    a.t(n_accept, "n_accept", _i32(), shape=(B,))
+    a.t(out, "out", _in_dtypes(), shape=(B, K, H, dv), optional=True)
+    st = a.stream(stream)
+    if want_out:
+        out = _new_out(out, (B, K, H, dv), state)
     _call("replay_accepted", _ptr(state), S, _ptr(slot), B, H, dk, dv, K, _ptr(q), _ptr(k),
           _ptr(v), _code(q.dtype), _ptr(alpha), int(decay_kind), _ptr(beta), _ptr(n_accept),
-          _ptr(out), _code(out.dtype) if out is not None else HLA_F32, _ptr(err_flag),
-          _stream(stream))
+          _ptr(out), _code(out.dtype) if out is not None else HLA_F32, _ptr(err_flag), st)
     return out
-
-
-def _drafts(state, q, k, v, alpha, beta, slot, err_flag):
-    """Shared checks of the multi-token entry points; returns (S, H, dk, dv, B, K)."""
-    _dev(state, "state", _f32(), 4)
-    S, H, dk, dv = state.shape
-    _dev(q, "q", _in_dtypes(), 4)
-    B, K = q.shape[:2]
-    _dev(k, "k", (q.dtype,), 4)
-    _dev(v, "v", (q.dtype,), 4)
-    _dev(alpha, "alpha", _f32())
-    _dev(beta, "beta", _f32(), 3)
-    if slot is not None:
-        _dev(slot, "slot", _i32(), 1)
-    if err_flag is not None:
-        _dev(err_flag, "err_flag", _i32())
-    return S, H, dk, dv, B, K
 
 
 def replay_accepted_bonus(state, q, k, v, alpha, beta, n_accept, decay_kind, q_bonus, k_bonus,
@@ -223,24 +291,29 @@ def replay_accepted_bonus(state, q, k, v, alpha, beta, n_accept, decay_kind, q_b
                           err_flag=None, stream=None, want_out_bonus=True):
     """Replay the first n_accept[b] drafts, then the bonus token ([B, H, .] inputs), in one
     pass over the state.  Returns the bonus token's readout [B, H, dv] (or None)."""
-    S, H, dk, dv, B, K = _drafts(state, q, k, v, alpha, beta, slot, err_flag)
-    _dev(n_accept, "n_accept", _i32(), 1)
-    _dev(q_bonus, "q_bonus", (q.dtype,), 3)
-    _dev(k_bonus, "k_bonus", (q.dtype,), 3)
-    _dev(v_bonus, "v_bonus", (q.dtype,), 3)
-    _dev(alpha_bonus, "alpha_bonus", _f32())
-    _dev(beta_bonus, "beta_bonus", _f32(), 2)
-    if out is not None:
-        _dev(out, "out", _in_dtypes(), 4)
-    out_bonus = _opt_out(out_bonus, (B, H, dv), state.device, want_out_bonus)
+    a = _Args("replay_accepted_bonus")
+    S, H, dk, dv, B, K = _drafts(a, state, q, k, v, alpha, beta, decay_kind, slot, err_flag)
+    a.t(n_accept, "n_accept", _i32(), shape=(B,))
+    a.t(q_bonus, "q_bonus", (q.dtype,), shape=(B, H, dk))
+    a.t(k_bonus, "k_bonus", (q.dtype,), shape=(B, H, dk))
+    a.t(v_bonus, "v_bonus", (q.dtype,), shape=(B, H, dv))
+    _decay_arg(a, alpha_bonus, "alpha_bonus", (B, H), decay_kind, dk)
+    a.t(beta_bonus, "beta_bonus", _f32(), shape=(B, H))
+    a.t(out, "out", _in_dtypes(), shape=(B, K, H, dv), optional=True)
+    a.t(out_bonus, "out_bonus", _in_dtypes(), shape=(B, H, dv), optional=True)
     if out is not None and out_bonus is not None and out.dtype != out_bonus.dtype:
-        raise TypeError("out and out_bonus must have the same dtype")
+        raise TypeError("replay_accepted_bonus: out and out_bonus must have the same dtype")
+    st = a.stream(stream)
+    if want_out_bonus:
+        out_bonus = _new_out(out_bonus, (B, H, dv), state)
+        if out is not None and out.dtype != out_bonus.dtype:
+            raise TypeError("replay_accepted_bonus: out and out_bonus must have the same dtype")
     od = out_bonus if out_bonus is not None else out
     _call("replay_accepted_bonus", _ptr(state), S, _ptr(slot), B, H, dk, dv, K, _ptr(q),
           _ptr(k), _ptr(v), _code(q.dtype), _ptr(alpha), int(decay_kind), _ptr(beta),
           _ptr(n_accept), _ptr(out), _ptr(q_bonus), _ptr(k_bonus), _ptr(v_bonus),
           _ptr(alpha_bonus), _ptr(beta_bonus), _ptr(out_bonus),
-          _code(od.dtype) if od is not None else HLA_F32, _ptr(err_flag), _stream(stream))
+          _code(od.dtype) if od is not None else HLA_F32, _ptr(err_flag), st)
     return out_bonus
 
 
@@ -248,11 +321,14 @@ def verify_drafts(state, q, k, v, alpha, beta, decay_kind, out=None, slot=None, 
                   stream=None):
     """Readouts at all K draft positions from the committed state (which is only read).
     Returns out [B, K, H, dv]."""
-    S, H, dk, dv, B, K = _drafts(state, q, k, v, alpha, beta, slot, err_flag)
-    out = _opt_out(out, (B, K, H, dv), state.device, True)
+    a = _Args("verify_drafts")
+    S, H, dk, dv, B, K = _drafts(a, state, q, k, v, alpha, beta, decay_kind, slot, err_flag)
+    a.t(out, "out", _in_dtypes(), shape=(B, K, H, dv), optional=True)
+    st = a.stream(stream)
+    out = _new_out(out, (B, K, H, dv), state)
     _call("verify_drafts", _ptr(state), S, _ptr(slot), B, H, dk, dv, K, _ptr(q), _ptr(k),
           _ptr(v), _code(q.dtype), _ptr(alpha), int(decay_kind), _ptr(beta), _ptr(out),
-          _code(out.dtype), _ptr(err_flag), _stream(stream))
+          _code(out.dtype), _ptr(err_flag), st)
     return out
 
 
@@ -266,11 +342,28 @@ def _damp_group(lo_scale, dv):
     raise ValueError(f"lo_scale shape {tuple(lo_scale.shape)} fits no scale group of dv={dv}")
 
 
-def _sr_tables(val_perm, val_scale):
-    if val_perm is not None:
-        _dev(val_perm, "val_perm", _i32(), 2)
-    if val_scale is not None:
-        _dev(val_scale, "val_scale", _f32(), 2)
+def _hi_dtypes():
+    torch = _torch()
+    return (torch.int16, torch.uint16, torch.float16)
+
+
+def _packed(a, hi, lo, lo_scale, S, H, dk, dv, K_hi):
+    """The three packed regions of S slots x H heads; returns the scale group."""
+    if not 0 <= K_hi <= dk:
+        raise ValueError(f"{a.fn}: K_hi = {K_hi} outside [0, dk = {dk}]")
+    a.t(hi, "hi", _hi_dtypes(), shape=(S, H, K_hi, dv))
+    a.t(lo, "lo", (_torch().int8,), shape=(S, H, dk - K_hi, dv))
+    a.t(lo_scale, "lo_scale", _f32())
+    g = _damp_group(lo_scale, dv)
+    a.t(lo_scale, "lo_scale", _f32(),
+        shape=(S, H, dk - K_hi) if g == dv else (S, H, dk - K_hi, dv // g))
+    return g
+
+
+def _plans(a, key_perm, val_perm, val_scale, H, dk, dv):
+    a.t(key_perm, "key_perm", _i32(), shape=(H, dk), optional=True)
+    a.t(val_perm, "val_perm", _i32(), shape=(H, dv), optional=True)
+    a.t(val_scale, "val_scale", _f32(), shape=(H, dv), optional=True)
 
 
 def damp_step(hi, lo, lo_scale, key_perm, K_hi, q, k, v, alpha, decay_kind, beta, out=None,
@@ -279,32 +372,28 @@ def damp_step(hi, lo, lo_scale, key_perm, K_hi, q, k, v, alpha, decay_kind, beta
     """One fused dequantise -> update -> requantise step on the packed state (in place).
     The scale group (per row or per 32 values) is read off lo_scale's shape; val_perm /
     val_scale [H, dv] select the value transform (None: untransformed)."""
-    torch = _torch()
-    _dev(hi, "hi", (torch.int16, torch.uint16, torch.float16), 4)
-    _dev(lo, "lo", (torch.int8,), 4)
-    _dev(lo_scale, "lo_scale", _f32())
+    a = _Args("damp_step")
+    if not isinstance(hi, _torch().Tensor) or hi.dim() != 4:
+        raise ValueError("damp_step: hi must be a 4-dimensional tensor [S, H, K_hi, dv]")
     S, H, _, dv = hi.shape
-    group = _damp_group(lo_scale, dv)
-    _dev(q, "q", _in_dtypes(), 3)
+    a.t(q, "q", _in_dtypes(), shape=(None, H, None))
     B, _, dk = q.shape
-    _dev(k, "k", (q.dtype,), 3)
-    _dev(v, "v", (q.dtype,), 3)
-    _dev(alpha, "alpha", _f32())
-    _dev(beta, "beta", _f32(), 2)
-    if key_perm is not None:
-        _dev(key_perm, "key_perm", _i32(), 2)
-    _sr_tables(val_perm, val_scale)
-    if slot is not None:
-        _dev(slot, "slot", _i32(), 1)
-    if err_flag is not None:
-        _dev(err_flag, "err_flag", _i32())
-    if lo.shape[2] != dk - K_hi or hi.shape[2] != K_hi:
-        raise ValueError("hi/lo row counts do not match K_hi and dk")
-    out = _opt_out(out, (B, H, dv), hi.device, want_out)
+    group = _packed(a, hi, lo, lo_scale, S, H, dk, dv, K_hi)
+    a.t(k, "k", (q.dtype,), shape=(B, H, dk))
+    a.t(v, "v", (q.dtype,), shape=(B, H, dv))
+    _decay_arg(a, alpha, "alpha", (B, H), decay_kind, dk)
+    a.t(beta, "beta", _f32(), shape=(B, H))
+    _plans(a, key_perm, val_perm, val_scale, H, dk, dv)
+    a.t(slot, "slot", _i32(), shape=(B,), optional=True)
+    a.flag(err_flag)
+    a.t(out, "out", _in_dtypes(), shape=(B, H, dv), optional=True)
+    st = a.stream(stream)
+    if want_out:
+        out = _new_out(out, (B, H, dv), hi)
     _call("damp_step", _ptr(hi), _ptr(lo), _ptr(lo_scale), S, _ptr(key_perm), K_hi, group,
           _ptr(val_perm), _ptr(val_scale), _ptr(slot), B, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
           _code(q.dtype), _ptr(alpha), int(decay_kind), _ptr(beta), _ptr(out),
-          _code(out.dtype) if out is not None else HLA_F32, _ptr(err_flag), _stream(stream))
+          _code(out.dtype) if out is not None else HLA_F32, _ptr(err_flag), st)
     return out
 
 
@@ -320,34 +409,48 @@ def damp_alloc(S, H, dk, dv, K_hi, device="cuda", group=None):
 
 def damp_quantize(state, key_perm, K_hi, hi=None, lo=None, lo_scale=None, stream=None,
                   group=None, val_perm=None, val_scale=None):
-    _dev(state, "state", _f32(), 4)
+    """Pack an FP32 state [S,H,dk,dv] into (hi, lo, lo_scale); the three regions are
+    allocated when none is given (group None: one scale per row)."""
+    a = _Args("damp_quantize")
+    a.t(state, "state", _f32(), ndim=4)
     S, H, dk, dv = state.shape
-    if hi is None:
-        hi, lo, lo_scale = damp_alloc(S, H, dk, dv, K_hi, state.device, group)
-    g = _damp_group(lo_scale, dv)
-    if group is not None and int(group) != g:
-        raise ValueError("lo_scale shape does not match group")
-    if key_perm is not None:
-        _dev(key_perm, "key_perm", _i32(), 2)
-    _sr_tables(val_perm, val_scale)
+    given = [x is not None for x in (hi, lo, lo_scale)]
+    if any(given) and not all(given):
+        raise ValueError("damp_quantize: give all of hi, lo and lo_scale, or none")
+    if all(given):
+        g = _packed(a, hi, lo, lo_scale, S, H, dk, dv, K_hi)
+        if group is not None and int(group) != g:
+            raise ValueError("damp_quantize: lo_scale shape does not match group")
+    else:
+        if not 0 <= K_hi <= dk:
+            raise ValueError(f"damp_quantize: K_hi = {K_hi} outside [0, dk = {dk}]")
+        g = dv if group is None else int(group)
+    _plans(a, key_perm, val_perm, val_scale, H, dk, dv)
+    st = a.stream(stream)
+    if not all(given):
+        if g <= 0 or dv % g:
+            raise ValueError(f"damp_quantize: group {g} does not divide dv = {dv}")
+        hi, lo, lo_scale = damp_alloc(S, H, dk, dv, K_hi, state.device, g)
     _call("damp_quantize", _ptr(state), S, H, dk, dv, _ptr(key_perm), K_hi, g, _ptr(val_perm),
-          _ptr(val_scale), _ptr(hi), _ptr(lo), _ptr(lo_scale), _stream(stream))
+          _ptr(val_scale), _ptr(hi), _ptr(lo), _ptr(lo_scale), st)
     return hi, lo, lo_scale
 
 
 def damp_dequantize(hi, lo, lo_scale, key_perm, K_hi, dk, out=None, stream=None,
                     val_perm=None, val_scale=None):
-    torch = _torch()
+    """Reconstruct the FP32 state [S,H,dk,dv] (original coordinates) from the packed
+    regions."""
+    a = _Args("damp_dequantize")
+    if not isinstance(hi, _torch().Tensor) or hi.dim() != 4:
+        raise ValueError("damp_dequantize: hi must be a 4-dimensional tensor [S, H, K_hi, dv]")
     S, H, _, dv = hi.shape
-    g = _damp_group(lo_scale, dv)
-    if out is None:
-        out = torch.empty((S, H, dk, dv), dtype=torch.float32, device=hi.device)
-    _dev(out, "state", _f32(), 4)
-    if key_perm is not None:
-        _dev(key_perm, "key_perm", _i32(), 2)
-    _sr_tables(val_perm, val_scale)
+    g = _packed(a, hi, lo, lo_scale, S, H, dk, dv, K_hi)
+    _plans(a, key_perm, val_perm, val_scale, H, dk, dv)
+    a.t(out, "state", _f32(), shape=(S, H, dk, dv), optional=True)
+    st = a.stream(stream)
+    out = _new_out(out, (S, H, dk, dv), hi)
     _call("damp_dequantize", _ptr(hi), _ptr(lo), _ptr(lo_scale), S, H, dk, dv, _ptr(key_perm),
-          K_hi, g, _ptr(val_perm), _ptr(val_scale), _ptr(out), _stream(stream))
+          K_hi, g, _ptr(val_perm), _ptr(val_scale), _ptr(out), st)
     return out
 
 
@@ -367,53 +470,98 @@ def dasc_plan(mask):
     return offsets, unit_index[:R.value].copy(), unit_pos.reshape(L, n), R.value
 
 
+def _span(L, stride, S, n_units, unit_bytes):
+    """Bytes a layered state buffer must hold: layer L-1 starts at (L-1)*stride and holds
+    S slots of n_units units."""
+    if min(L, S, n_units, unit_bytes) <= 0 or stride < 0:
+        return 0
+    return (L - 1) * stride + S * n_units * unit_bytes
+
+
+def _pairs(a, src_slot, dst_slot):
+    a.t(src_slot, "src_slot", _i32(), ndim=1)
+    a.t(dst_slot, "dst_slot", _i32(), shape=(src_slot.numel(),))
+    return src_slot.numel()
+
+
+def _unit_index(a, unit_index, R):
+    """The retained-unit list [R]; an empty list is passed as NULL."""
+    if unit_index is None or (R == 0 and unit_index.numel() == 0):
+        return None
+    return a.t(unit_index, "unit_index", _i32(), shape=(R,))
+
+
 def dasc_pack(active, layer_stride_bytes, S_act, L, n_units, unit_bytes, offsets, unit_index,
               R_total, src_slot, dst_slot, packed, S_ckpt, err_flag=None, stream=None):
-    """Byte-level pack; `active` and `packed` are device tensors (any dtype)."""
-    for t, nm in ((offsets, "offsets"), (src_slot, "src_slot"), (dst_slot, "dst_slot")):
-        _dev(t, nm, _i32(), 1)
+    """Byte-level pack; `active` and `packed` are device tensors (any dtype) at least as
+    large as the geometry given."""
+    a = _Args("dasc_pack")
+    a.nbytes(active, "active", _span(L, layer_stride_bytes, S_act, n_units, unit_bytes))
+    a.t(offsets, "offsets", _i32(), shape=(max(L, 0) + 1,))
+    idx = _unit_index(a, unit_index, R_total)
+    N = _pairs(a, src_slot, dst_slot)
+    a.nbytes(packed, "packed", max(S_ckpt, 0) * max(R_total, 0) * max(unit_bytes, 0))
+    a.flag(err_flag)
     _call("dasc_pack", _ptr(active), int(layer_stride_bytes), S_act, L, n_units, int(unit_bytes),
-          _ptr(offsets), _ptr(unit_index) if unit_index.numel() else None, R_total,
-          _ptr(src_slot), _ptr(dst_slot), src_slot.numel(), _ptr(packed), S_ckpt,
-          _ptr(err_flag), _stream(stream))
+          _ptr(offsets), _ptr(idx), R_total, _ptr(src_slot), _ptr(dst_slot), N, _ptr(packed),
+          S_ckpt, _ptr(err_flag), a.stream(stream))
 
 
 def dasc_restore(packed, S_ckpt, R_total, unit_pos, L, n_units, unit_bytes, src_slot, dst_slot,
                  active_out, layer_stride_bytes, S_dst, err_flag=None, stream=None):
-    for t, nm in ((src_slot, "src_slot"), (dst_slot, "dst_slot")):
-        _dev(t, nm, _i32(), 1)
-    _dev(unit_pos, "unit_pos", _i32())
+    """Byte-level restore with zero-fill of the omitted units."""
+    a = _Args("dasc_restore")
+    a.nbytes(packed, "packed", max(S_ckpt, 0) * max(R_total, 0) * max(unit_bytes, 0))
+    a.t(unit_pos, "unit_pos", _i32())
+    if unit_pos.numel() != max(L, 0) * max(n_units, 0):
+        raise ValueError(f"dasc_restore: unit_pos has {unit_pos.numel()} entries, the plan "
+                         f"has L * n_units = {L * n_units}")
+    N = _pairs(a, src_slot, dst_slot)
+    a.nbytes(active_out, "active_out", _span(L, layer_stride_bytes, S_dst, n_units, unit_bytes))
+    a.flag(err_flag)
     _call("dasc_restore", _ptr(packed), S_ckpt, R_total, _ptr(unit_pos), L, n_units,
-          int(unit_bytes), _ptr(src_slot), _ptr(dst_slot), src_slot.numel(), _ptr(active_out),
-          int(layer_stride_bytes), S_dst, _ptr(err_flag), _stream(stream))
+          int(unit_bytes), _ptr(src_slot), _ptr(dst_slot), N, _ptr(active_out),
+          int(layer_stride_bytes), S_dst, _ptr(err_flag), a.stream(stream))
 
 
 def dasc_pack_int8(active, layer_stride_bytes, S_act, L, n_units, unit_rows, dv, offsets,
                    unit_index, R_total, src_slot, dst_slot, codes, scales, S_ckpt, err_flag=None,
                    stream=None):
     """Quantise-once pack of the retained units of an FP32 state into (codes, scales)."""
-    for t, nm in ((offsets, "offsets"), (src_slot, "src_slot"), (dst_slot, "dst_slot")):
-        _dev(t, nm, _i32(), 1)
-    torch = _torch()
-    _dev(codes, "codes", (torch.int8,))
-    _dev(scales, "scales", _f32())
+    a = _Args("dasc_pack_int8")
+    a.nbytes(active, "active", _span(L, layer_stride_bytes, S_act, n_units, unit_rows * dv * 4),
+             _f32())
+    a.t(offsets, "offsets", _i32(), shape=(max(L, 0) + 1,))
+    idx = _unit_index(a, unit_index, R_total)
+    N = _pairs(a, src_slot, dst_slot)
+    rows = max(S_ckpt, 0) * max(R_total, 0) * max(unit_rows, 0)
+    a.nbytes(codes, "codes", rows * max(dv, 0), (_torch().int8,))
+    a.nbytes(scales, "scales", rows * 4, _f32())
+    a.flag(err_flag)
     _call("dasc_pack_int8", _ptr(active), int(layer_stride_bytes), S_act, L, n_units, unit_rows,
-          dv, _ptr(offsets), _ptr(unit_index) if unit_index.numel() else None, R_total,
-          _ptr(src_slot), _ptr(dst_slot), src_slot.numel(), _ptr(codes), _ptr(scales), S_ckpt,
-          _ptr(err_flag), _stream(stream))
+          dv, _ptr(offsets), _ptr(idx), R_total, _ptr(src_slot), _ptr(dst_slot), N,
+          _ptr(codes), _ptr(scales), S_ckpt, _ptr(err_flag), a.stream(stream))
 
 
 def dasc_restore_int8(codes, scales, S_ckpt, R_total, unit_pos, L, n_units, unit_rows, dv,
                       src_slot, dst_slot, active_out, layer_stride_bytes, S_dst, err_flag=None,
                       stream=None):
     """Dequantise-once restore into FP32 active slots, omitted units zero."""
-    for t, nm in ((src_slot, "src_slot"), (dst_slot, "dst_slot")):
-        _dev(t, nm, _i32(), 1)
-    _dev(unit_pos, "unit_pos", _i32())
-    _dev(active_out, "active_out", _f32())
+    a = _Args("dasc_restore_int8")
+    rows = max(S_ckpt, 0) * max(R_total, 0) * max(unit_rows, 0)
+    a.nbytes(codes, "codes", rows * max(dv, 0), (_torch().int8,))
+    a.nbytes(scales, "scales", rows * 4, _f32())
+    a.t(unit_pos, "unit_pos", _i32())
+    if unit_pos.numel() != max(L, 0) * max(n_units, 0):
+        raise ValueError(f"dasc_restore_int8: unit_pos has {unit_pos.numel()} entries, the "
+                         f"plan has L * n_units = {L * n_units}")
+    N = _pairs(a, src_slot, dst_slot)
+    a.nbytes(active_out, "active_out",
+             _span(L, layer_stride_bytes, S_dst, n_units, unit_rows * dv * 4), _f32())
+    a.flag(err_flag)
     _call("dasc_restore_int8", _ptr(codes), _ptr(scales), S_ckpt, R_total, _ptr(unit_pos), L,
-          n_units, unit_rows, dv, _ptr(src_slot), _ptr(dst_slot), src_slot.numel(),
-          _ptr(active_out), int(layer_stride_bytes), S_dst, _ptr(err_flag), _stream(stream))
+          n_units, unit_rows, dv, _ptr(src_slot), _ptr(dst_slot), N, _ptr(active_out),
+          int(layer_stride_bytes), S_dst, _ptr(err_flag), a.stream(stream))
 
 
 GATE_SOFTPLUS, GATE_BOUNDED = 0, 1
@@ -454,11 +602,15 @@ def dasc_refresh_local(scratch, scratch_layer_stride_bytes, S_scratch, active,
                        stream=None):
     """Copy the local units (plan of the inverted mask) from scratch slots into active
     slots; everything else in the active slots is left alone."""
-    for t, nm in ((offsets_local, "offsets"), (src_slot, "src_slot"), (dst_slot, "dst_slot")):
-        _dev(t, nm, _i32(), 1)
+    a = _Args("dasc_refresh_local")
+    a.nbytes(scratch, "scratch",
+             _span(L, scratch_layer_stride_bytes, S_scratch, n_units, unit_bytes))
+    a.nbytes(active, "active", _span(L, layer_stride_bytes, S_act, n_units, unit_bytes))
+    a.t(offsets_local, "offsets", _i32(), shape=(max(L, 0) + 1,))
+    idx = _unit_index(a, unit_index_local, R_local)
+    N = _pairs(a, src_slot, dst_slot)
+    a.flag(err_flag)
     _call("dasc_refresh_local", _ptr(scratch), int(scratch_layer_stride_bytes), S_scratch,
           _ptr(active), int(layer_stride_bytes), S_act, L, n_units, int(unit_bytes),
-          _ptr(offsets_local), _ptr(unit_index_local) if unit_index_local.numel() else None,
-          R_local, _ptr(src_slot), _ptr(dst_slot), src_slot.numel(), _ptr(err_flag),
-          _stream(stream))
-
+          _ptr(offsets_local), _ptr(idx), R_local, _ptr(src_slot), _ptr(dst_slot), N,
+          _ptr(err_flag), a.stream(stream))

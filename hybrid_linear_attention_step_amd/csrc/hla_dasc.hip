@@ -425,6 +425,10 @@ int dasc_pack(const void *active, int64_t layer_stride_bytes, int S_act, int L, 
 {
     int rc = hla::check_dasc(active, layer_stride_bytes, S_act, L, n_units, unit_bytes, offsets,
                              unit_index, R_total, src_slot, dst_slot, N, packed, S_ckpt);
+    if (rc == HLA_OK && N > 0)
+        rc = hla::check_dasc_tables(
+            hla::Range{packed, (size_t)((int64_t)S_ckpt * R_total * unit_bytes)}, hla::Range{},
+            offsets, L, unit_index, R_total, nullptr, 0, src_slot, dst_slot, N);
     if (rc != HLA_OK) return rc;
     if (L > hla::kMaxLayers) return HLA_ERR_UNSUPPORTED;
     if (N == 0 || R_total == 0) return HLA_OK;
@@ -451,6 +455,11 @@ int dasc_restore(const void *packed, int S_ckpt, int R_total, const int32_t *uni
 {
     int rc = hla::check_dasc(active_out, layer_stride_bytes, S_dst, L, n_units, unit_bytes,
                              unit_pos, unit_pos, R_total, src_slot, dst_slot, N, packed, S_ckpt);
+    if (rc == HLA_OK && N > 0)
+        rc = hla::check_dasc_tables(
+            hla::Range{active_out,
+                       (size_t)hla::dasc_span(layer_stride_bytes, L, S_dst, n_units, unit_bytes)},
+            hla::Range{}, nullptr, L, nullptr, 0, unit_pos, n_units, src_slot, dst_slot, N);
     if (rc != HLA_OK || N == 0) return rc;
     const hla::FastDiv uv = hla::make_fastdiv((uint32_t)(unit_bytes / 16));
     const hla::FastDiv un = hla::make_fastdiv((uint32_t)n_units);
@@ -489,6 +498,10 @@ int dasc_refresh_local(const void *scratch, int64_t scratch_layer_stride_bytes, 
             (L - 1) * scratch_layer_stride_bytes + (int64_t)S_scratch * n_units * unit_bytes;
         if (hla::overlaps(hla::Range{active, (size_t)span_a}, hla::Range{scratch, (size_t)span_s}))
             rc = HLA_ERR_ALIAS;
+        if (rc == HLA_OK)
+            rc = hla::check_dasc_tables(hla::Range{active, (size_t)span_a}, hla::Range{},
+                                        offsets, L, unit_index, R_local, nullptr, 0, src_slot,
+                                        dst_slot, N);
     }
     if (rc != HLA_OK) return rc;
     if (L > hla::kMaxLayers) return HLA_ERR_UNSUPPORTED;
@@ -517,6 +530,12 @@ int dasc_pack_int8(const float *active, int64_t layer_stride_bytes, int S_act, i
     int rc = hla::check_dasc_int8(active, layer_stride_bytes, S_act, L, n_units, unit_rows, dv,
                                   offsets, unit_index, R_total, src_slot, dst_slot, N, codes,
                                   scales, S_ckpt);
+    if (rc == HLA_OK && N > 0) {
+        const size_t rows = (size_t)S_ckpt * R_total * unit_rows;
+        rc = hla::check_dasc_tables(hla::Range{codes, rows * dv},
+                                    hla::Range{scales, rows * sizeof(float)}, offsets, L,
+                                    unit_index, R_total, nullptr, 0, src_slot, dst_slot, N);
+    }
     if (rc != HLA_OK) return rc;
     if (L > hla::kMaxLayers) return HLA_ERR_UNSUPPORTED;
     if (N == 0 || R_total == 0) return HLA_OK;
@@ -551,6 +570,11 @@ int dasc_restore_int8(const int8_t *codes, const float *scales, int S_ckpt, int 
     int rc = hla::check_dasc_int8(active_out, layer_stride_bytes, S_dst, L, n_units, unit_rows,
                                   dv, unit_pos, unit_pos, R_total, src_slot, dst_slot, N, codes,
                                   scales, S_ckpt);
+    if (rc == HLA_OK && N > 0)
+        rc = hla::check_dasc_tables(
+            hla::Range{active_out, (size_t)hla::dasc_span(layer_stride_bytes, L, S_dst, n_units,
+                                                          (int64_t)unit_rows * dv * 4)},
+            hla::Range{}, nullptr, L, nullptr, 0, unit_pos, n_units, src_slot, dst_slot, N);
     if (rc != HLA_OK || N == 0) return rc;
     const int lr = hla::log2_exact(unit_rows);
     const hla::FastDiv un = hla::make_fastdiv((uint32_t)n_units);

@@ -191,6 +191,20 @@ int check_dasc(const void *active, int64_t layer_stride_bytes, int S_act, int L,
     return HLA_OK;
 }
 
+int check_dasc_tables(Range w0, Range w1, const int32_t *offsets, int L,
+                      const int32_t *unit_index, int R, const int32_t *unit_pos, int n_units,
+                      const int32_t *src_slot, const int32_t *dst_slot, int N)
+{
+    const Range tables[] = {{offsets, (size_t)(L + 1) * sizeof(int32_t)},
+                            {unit_index, (size_t)R * sizeof(int32_t)},
+                            {unit_pos, (size_t)L * n_units * sizeof(int32_t)},
+                            {src_slot, (size_t)N * sizeof(int32_t)},
+                            {dst_slot, (size_t)N * sizeof(int32_t)}};
+    for (const Range &t : tables)
+        if (overlaps(w0, t) || overlaps(w1, t)) return HLA_ERR_ALIAS;
+    return HLA_OK;
+}
+
 int check_dasc_int8(const void *active, int64_t layer_stride_bytes, int S_act, int L,
                     int n_units, int unit_rows, int dv, const void *table_a,
                     const void *table_b, int R_total, const int32_t *src_slot,

@@ -112,6 +112,22 @@ int check_dasc(const void *active, int64_t layer_stride_bytes, int S_act, int L,
                const int32_t *src_slot, const int32_t *dst_slot, int N, const void *packed,
                int S_ckpt);
 
+// The plan tables and slot maps a checkpoint kernel reads while it writes
+// (offsets [L+1], unit_index [R], unit_pos [L*n_units], src/dst [N]; NULL
+// entries are skipped) must not overlap what the call writes (w0, w1):
+// HLA_ERR_ALIAS if one does.
+int check_dasc_tables(Range w0, Range w1, const int32_t *offsets, int L,
+                      const int32_t *unit_index, int R, const int32_t *unit_pos, int n_units,
+                      const int32_t *src_slot, const int32_t *dst_slot, int N);
+
+// Bytes from the first byte of layer 0 to the end of layer L-1 of a layered
+// state (arguments already validated by check_dasc / check_dasc_int8).
+inline int64_t dasc_span(int64_t layer_stride_bytes, int L, int S, int n_units,
+                         int64_t unit_bytes)
+{
+    return (int64_t)(L - 1) * layer_stride_bytes + (int64_t)S * n_units * unit_bytes;
+}
+
 // INT8 checkpoints: a unit is unit_rows (a power of two, <= 256) rows of dv
 // (64 or 128) FP32 values; codes [S_ckpt, R_total, unit_rows, dv] int8 and
 // scales [S_ckpt, R_total, unit_rows] float32.

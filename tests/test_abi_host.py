@@ -201,6 +201,17 @@ def test_dasc_validation(L):
     assert pk(N=0) == OK
     assert L.dasc_restore(f(), 8, 64, None, 4, 32, 65536, f(), f(), 8, f(), 512 * 32 * 65536,
                           512, None, None) == NULL
+    # an output written over a plan table or slot map the kernel reads while it writes
+    pkd = f()
+    for table in ("offsets", "unit_index", "src", "dst"):
+        assert pk(packed=pkd, **{table: ctypes.c_void_p(pkd.value + 4096)}) == ALIAS, table
+    rs = dict(packed=f(), S_ckpt=8, R=64, unit_pos=f(), L=4, n_units=32, unit_bytes=65536,
+              src=f(), dst=f(), N=8, out=f(), stride=512 * 32 * 65536, S_dst=512, err=None,
+              stream=None)
+    out = f()
+    for table in ("unit_pos", "src", "dst"):
+        a = dict(rs, out=out, **{table: ctypes.c_void_p(out.value + 3 * 512 * 32 * 65536)})
+        assert L.dasc_restore(*a.values()) == ALIAS, table
 
 
 def test_dasc_plan_matches_oracle(L, orc):
@@ -306,6 +317,13 @@ def test_selection_and_int8_validation(L):
               S_dst=512, err=None, stream=None)
     assert L.dasc_restore_int8(*dict(rs, dv=32).values()) == UNSUP
     assert L.dasc_restore_int8(*dict(rs, unit_pos=None).values()) == NULL
+    out = f()
+    assert L.dasc_restore_int8(*dict(rs, out=out, unit_pos=ctypes.c_void_p(out.value + 64))
+                               .values()) == ALIAS
+    sc = f()
+    assert pk(scales=sc, dst=ctypes.c_void_p(sc.value + 16)) == ALIAS
+    cd = f()
+    assert pk(codes=cd, offsets=ctypes.c_void_p(cd.value + 1024)) == ALIAS
     # copy-back: the scratch and active states must not overlap
     st = f()
     cb = dict(scratch=st, s_stride=64 * 32 * 65536, S_s=64, active=f(), stride=512 * 32 * 65536,
@@ -314,6 +332,9 @@ def test_selection_and_int8_validation(L):
     assert L.dasc_refresh_local(*dict(cb, active=ctypes.c_void_p(st.value + 65536)).values()) \
         == ALIAS
     assert L.dasc_refresh_local(*dict(cb, unit_bytes=65540).values()) == ALIGN
+    act = f()
+    assert L.dasc_refresh_local(*dict(cb, active=act, unit_index=ctypes.c_void_p(act.value + 64))
+                                .values()) == ALIAS
 
 
 
@@ -327,5 +348,184 @@ def test_binding_rejects_host_tensors_and_bad_dtypes():
     st = z(2, 2, 64, 64)
     with pytest.raises(ValueError, match="GPU"):
         hla.gdn_step(st, z(2, 2, 64), z(2, 2, 64), z(2, 2, 64), z(2, 2), z(2, 2))
-    with pytest.raises(ValueError):
+    with pytest.raises(TypeError, match="dtype"):
         hla.damp_quantize(z(2, 2, 64, 64, dtype=torch.float64), None, 8)
+
+
+# ---------------------------------------------------------------- binding argument checks
+#
+# The C entry points size every access from the sizes they are given, so the binding must
+# refuse a tensor whose shape disagrees with those sizes, or that lives in host memory,
+# before the call.  Shapes are checked before devices, so these run on CPU tensors.
+
+def _t():
+    return pytest.importorskip("torch")
+
+
+def _step_args(torch, B=3, H=2, dk=64, dv=64, kda=False):
+    z = torch.zeros
+    return dict(state=z(B, H, dk, dv), q=z(B, H, dk), k=z(B, H, dk), v=z(B, H, dv),
+                alpha=z(B, H, dk) if kda else z(B, H), beta=z(B, H))
+
+
+@pytest.mark.parametrize("kda", [False, True])
+@pytest.mark.parametrize("bad,shape", [
+    ("q", (3, 2, 32)), ("k", (3, 3, 64)), ("v", (2, 2, 64)), ("beta", (3, 1)),
+    ("alpha", (3, 2, 64, 1)),
+])
+def test_binding_rejects_misshaped_step_operands(kda, bad, shape):
+    torch = _t()
+    a = _step_args(torch, kda=kda)
+    a[bad] = torch.zeros(shape)
+    fn = hla.kda_step if kda else hla.gdn_step
+    with pytest.raises(ValueError, match=bad):
+        fn(**a)
+
+
+def test_binding_rejects_wrong_decay_shape_and_lengths():
+    torch = _t()
+    a = _step_args(torch)
+    with pytest.raises(ValueError, match="alpha"):  # KDA given a GDN-shaped decay
+        hla.kda_step(**a)
+    with pytest.raises(ValueError, match="alpha"):  # GDN given a KDA-shaped decay
+        hla.gdn_step(**_step_args(torch, kda=True))
+    with pytest.raises(ValueError, match="slot"):
+        hla.gdn_step(**a, slot=torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="out"):
+        hla.gdn_step(**a, out=torch.zeros(3, 2, 32))
+    with pytest.raises(ValueError, match="err_flag"):
+        hla.gdn_step(**a, err_flag=torch.zeros(0, dtype=torch.int32))
+    with pytest.raises(ValueError, match="GPU"):    # right shapes, host memory
+        hla.gdn_step(**a)
+
+
+def _draft_args(torch, B=3, K=4, H=2, dk=64, dv=64):
+    z = torch.zeros
+    return dict(state=z(B, H, dk, dv), q=z(B, K, H, dk), k=z(B, K, H, dk), v=z(B, K, H, dv),
+                alpha=z(B, K, H), beta=z(B, K, H))
+
+
+def test_binding_rejects_misshaped_draft_operands():
+    torch = _t()
+    i32 = torch.int32
+    a = _draft_args(torch)
+    n = torch.zeros(3, dtype=i32)
+    with pytest.raises(ValueError, match="n_accept"):
+        hla.replay_accepted(**a, n_accept=torch.zeros(4, dtype=i32), decay_kind=0)
+    with pytest.raises(ValueError, match="alpha"):
+        hla.replay_accepted(**a, n_accept=n, decay_kind=1)
+    with pytest.raises(ValueError, match="out"):
+        hla.replay_accepted(**a, n_accept=n, decay_kind=0, out=torch.zeros(3, 3, 2, 64))
+    with pytest.raises(ValueError, match="v"):
+        hla.verify_drafts(**dict(a, v=torch.zeros(3, 4, 2, 32)), decay_kind=0)
+    z = torch.zeros
+    bonus = dict(q_bonus=z(3, 2, 64), k_bonus=z(3, 2, 64), v_bonus=z(3, 2, 64),
+                 alpha_bonus=z(3, 2), beta_bonus=z(3, 2))
+    with pytest.raises(ValueError, match="k_bonus"):
+        hla.replay_accepted_bonus(**a, n_accept=n, decay_kind=0,
+                                  **dict(bonus, k_bonus=z(3, 2, 32)))
+    with pytest.raises(ValueError, match="alpha_bonus"):
+        hla.replay_accepted_bonus(**a, n_accept=n, decay_kind=0,
+                                  **dict(bonus, alpha_bonus=z(3, 2, 64)))
+    with pytest.raises(ValueError, match="GPU"):
+        hla.replay_accepted_bonus(**a, n_accept=n, decay_kind=0, **bonus)
+
+
+def test_binding_checks_packed_state_operands():
+    torch = _t()
+    S, H, dk, dv, K_hi = 3, 2, 64, 64, 8
+    hi, lo, sc = hla.damp_alloc(S, H, dk, dv, K_hi, device="cpu")
+    z = torch.zeros
+    x = dict(q=z(S, H, dk), k=z(S, H, dk), v=z(S, H, dv), alpha=z(S, H, dk), beta=z(S, H))
+    with pytest.raises(ValueError, match="lo"):
+        hla.damp_step(hi, lo[:, :, 1:].contiguous(), sc, None, K_hi, decay_kind=1, **x)
+    with pytest.raises(ValueError, match="lo_scale"):
+        hla.damp_step(hi, lo, z(S, H, dk - K_hi + 1), None, K_hi, decay_kind=1, **x)
+    with pytest.raises(ValueError, match="key_perm"):
+        hla.damp_step(hi, lo, sc, z(H, dk - 1, dtype=torch.int32), K_hi, decay_kind=1, **x)
+    with pytest.raises(ValueError, match="alpha"):
+        hla.damp_step(hi, lo, sc, None, K_hi, decay_kind=0, **x)
+    with pytest.raises(ValueError, match="K_hi"):
+        hla.damp_step(hi, lo, sc, None, dk + 1, decay_kind=1, **x)
+    with pytest.raises(ValueError, match="GPU"):
+        hla.damp_step(hi, lo, sc, None, K_hi, decay_kind=1, **x)
+    # quantise / dequantise check caller-supplied packed regions and the state alike
+    st = z(S, H, dk, dv)
+    with pytest.raises(ValueError, match="GPU"):
+        hla.damp_quantize(st, None, K_hi, hi=hi, lo=lo, lo_scale=sc)
+    with pytest.raises(ValueError, match="hi"):
+        hla.damp_quantize(st, None, K_hi, hi=hi[:2].contiguous(), lo=lo, lo_scale=sc)
+    with pytest.raises(ValueError, match="all of"):
+        hla.damp_quantize(st, None, K_hi, hi=hi)
+    with pytest.raises(ValueError, match="GPU"):
+        hla.damp_dequantize(hi, lo, sc, None, K_hi, dk)
+    with pytest.raises(ValueError, match="state"):
+        hla.damp_dequantize(hi, lo, sc, None, K_hi, dk, out=z(S, H, dk, dv + 1))
+    with pytest.raises(ValueError, match="val_scale"):
+        hla.damp_dequantize(hi, lo, sc, None, K_hi, dk, val_scale=z(H, dv - 1))
+
+
+def test_binding_checks_checkpoint_buffer_sizes():
+    torch = _t()
+    i32 = torch.int32
+    L, S, n_units, ub = 2, 3, 4, 32
+    stride = S * n_units * ub
+    active = torch.zeros(L * stride, dtype=torch.uint8)
+    offsets = torch.tensor([0, 2, 4], dtype=i32)
+    idx = torch.tensor([0, 1, 2, 3], dtype=i32)
+    ids = torch.arange(S, dtype=i32)
+    packed = torch.zeros(S * 4 * ub, dtype=torch.uint8)
+    pk = dict(active=active, layer_stride_bytes=stride, S_act=S, L=L, n_units=n_units,
+              unit_bytes=ub, offsets=offsets, unit_index=idx, R_total=4, src_slot=ids,
+              dst_slot=ids, packed=packed, S_ckpt=S)
+    with pytest.raises(ValueError, match="active"):
+        hla.dasc_pack(**dict(pk, active=active[:-16]))
+    with pytest.raises(ValueError, match="packed"):
+        hla.dasc_pack(**dict(pk, packed=packed[:-16]))
+    with pytest.raises(ValueError, match="offsets"):
+        hla.dasc_pack(**dict(pk, offsets=offsets[:2]))
+    with pytest.raises(ValueError, match="unit_index"):
+        hla.dasc_pack(**dict(pk, unit_index=idx[:3]))
+    with pytest.raises(ValueError, match="dst_slot"):
+        hla.dasc_pack(**dict(pk, dst_slot=ids[:2]))
+    with pytest.raises(ValueError, match="GPU"):
+        hla.dasc_pack(**pk)
+    pos = torch.arange(L * n_units, dtype=i32)
+    rs = dict(packed=packed, S_ckpt=S, R_total=4, unit_pos=pos, L=L, n_units=n_units,
+              unit_bytes=ub, src_slot=ids, dst_slot=ids, active_out=active,
+              layer_stride_bytes=stride, S_dst=S)
+    with pytest.raises(ValueError, match="unit_pos"):
+        hla.dasc_restore(**dict(rs, unit_pos=pos[:-1]))
+    with pytest.raises(ValueError, match="active_out"):
+        hla.dasc_restore(**dict(rs, S_dst=S + 1))
+    with pytest.raises(ValueError, match="GPU"):
+        hla.dasc_restore(**rs)
+    # INT8 checkpoints: codes and scales sized by rows, the FP32 state by the geometry
+    rows, dv = 2, 4
+    act32 = torch.zeros(L * S * n_units * rows * dv)
+    codes = torch.zeros(S * 4 * rows * dv, dtype=torch.int8)
+    scales = torch.zeros(S * 4 * rows)
+    p8 = dict(active=act32, layer_stride_bytes=S * n_units * rows * dv * 4, S_act=S, L=L,
+              n_units=n_units, unit_rows=rows, dv=dv, offsets=offsets, unit_index=idx,
+              R_total=4, src_slot=ids, dst_slot=ids, codes=codes, scales=scales, S_ckpt=S)
+    with pytest.raises(ValueError, match="scales"):
+        hla.dasc_pack_int8(**dict(p8, scales=scales[:-1]))
+    with pytest.raises(ValueError, match="codes"):
+        hla.dasc_pack_int8(**dict(p8, codes=codes[:-1]))
+    with pytest.raises(TypeError, match="active"):
+        hla.dasc_pack_int8(**dict(p8, active=act32.double()))
+    r8 = dict(codes=codes, scales=scales, S_ckpt=S, R_total=4, unit_pos=pos, L=L,
+              n_units=n_units, unit_rows=rows, dv=dv, src_slot=ids, dst_slot=ids,
+              active_out=act32, layer_stride_bytes=S * n_units * rows * dv * 4, S_dst=S)
+    with pytest.raises(ValueError, match="active_out"):
+        hla.dasc_restore_int8(**dict(r8, active_out=act32[:-1]))
+    with pytest.raises(ValueError, match="GPU"):
+        hla.dasc_restore_int8(**r8)
+    cb = dict(scratch=active, scratch_layer_stride_bytes=stride, S_scratch=S, active=active,
+              layer_stride_bytes=stride, S_act=S, L=L, n_units=n_units, unit_bytes=ub,
+              offsets_local=offsets, unit_index_local=idx, R_local=4, src_slot=ids,
+              dst_slot=ids)
+    with pytest.raises(ValueError, match="scratch"):
+        hla.dasc_refresh_local(**dict(cb, scratch=active[:-1]))
+    with pytest.raises(ValueError, match="GPU"):
+        hla.dasc_refresh_local(**cb)
