@@ -30,6 +30,12 @@
  *     buffers must be 16-byte aligned.
  *   - All entry points are reentrant; the library keeps no mutable global
  *     state.  Concurrent calls that write the same buffers race.
+ *   - Within one call, the non-negative entries of a slot map that selects
+ *     state the call writes (slot of the state-updating entry points, dst_slot
+ *     of the checkpoint copies) must be distinct: two requests or pairs naming
+ *     the same slot would update it from two workgroups at once, and the
+ *     result is undefined.  Maps the call only reads through (src_slot, the
+ *     slot of verify_drafts) may repeat entries.
  */
 #ifndef HLA_H
 #define HLA_H
@@ -253,8 +259,8 @@ HLA_API int dasc_pack(const void *active, int64_t layer_stride_bytes, int S_act,
  * "Insertion and reuse"): for each pair n < N, write EVERY unit of every layer
  * of private slot dst_slot[n]: a retained unit receives its packed bytes from
  * checkpoint slot src_slot[n], an omitted unit is zero-filled.  The checkpoint
- * is only read ([K3]: restore copies the immutable checkpoint into the
- * request's private running state).
+ * is only read: a hit leaves the checkpoint as it is and gives the request a
+ * state of its own ([K3], the part on prefix caching).
  * unit_pos    device int32 [L * n_units] from dasc_plan.
  * active_out  device, layer l at active_out + l * layer_stride_bytes, each
  *             layer [S_dst, n_units, unit_bytes].
@@ -295,9 +301,9 @@ HLA_API int replay_accepted(float *state, int n_slots, const int32_t *slot, int 
 
 /* -------------------------------------------------------------------------
  * replay_accepted_bonus -- replay_accepted fused with the next ordinary step
- * ([K3] "Speculative decoding without state snapshots": after verification
- * one kernel replays the accepted projections on-chip, adds the target
- * model's bonus token and continues).  For request b: the first n_b draft
+ * ([K3] "Speculative decoding without state snapshots": the replay of the
+ * accepted drafts and the step of the token the target model itself emitted
+ * after them run in one kernel).  For request b: the first n_b draft
  * tokens as replay_accepted, then one gdn_step / kda_step update with the
  * bonus token's own projections, all on one read and one write of the state.
  * The bonus token is applied for every live request, also when n_b = 0.

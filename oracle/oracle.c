@@ -563,7 +563,7 @@ ORC_API void orc_dasc_pack(const uint8_t *active, long layer_stride_bytes, int S
 /* Load path, no refresh ([dasc] §4.2 dasc-nr; App. B.2 "Insertion and
    reuse"): the retained units are restored exactly and every omitted unit of
    the destination slot reads as zero; the checkpoint itself is only read
-   ([K3] "copy the immutable checkpoint before updating"). */
+   ([K3], the part on prefix caching: a hit gives the request its own copy). */
 ORC_API void orc_dasc_restore(const uint8_t *packed, int S_ckpt, int R_total,
                               const int32_t *offsets, const int32_t *unit_index, int L,
                               int n_units, long unit_bytes, const int32_t *src_slot,
