@@ -34,13 +34,20 @@ namespace hla {
 // The tile is read through a buffer resource over the head (scalar registers:
 // base, size) with one 32-bit per-lane byte offset and the row offset in the
 // scalar offset operand, so no 64-bit per-lane pointer is kept live across
-// the token (registers are what limits waves per SIMD here), and any read
-// outside the head's dk*dv*4 bytes would be dropped by the hardware range
-// check.  Word 3 of the descriptor is the raw-buffer format used on
-// gfx9-family GPUs; cache policy: nontemporal.  The tile is written back with
-// ordinary global nontemporal stores, whose addresses are formed only after
-// the token's arithmetic (the buffer form of the store gave wrong values in
-// part of the tile and is not used).
+// the token (registers are what limits waves per SIMD here).  Every read is
+// inside the head by construction: the lane offset (row0*dv + col0)*4 plus
+// the row offset m*dv*4 plus 16 bytes is at most dk*dv*4.  (The descriptor's
+// size is not a guard here: the scalar offset is not part of the hardware
+// range check.)  Word 3 of the descriptor is the raw-buffer format used on
+// gfx9-family GPUs; cache policy: nontemporal.
+// The tile is written back with ordinary global nontemporal stores, whose
+// addresses are formed only after the token's arithmetic.  Not the buffer
+// form of the store: with the row offset in a scalar register the compiler
+// lets the next VALU instruction overwrite the store's 16-byte data registers
+// with no wait state (it inserts one for a constant scalar offset and for
+// global stores), and that variant wrote wrong values in lanes 12-15 of each
+// 16-lane group of some waves, the pattern of a store reading its data after
+// it was overwritten.
 constexpr int kBufNt = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const float *head, uint32_t bytes)
