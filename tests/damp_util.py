@@ -77,3 +77,23 @@ def _assert_bars(w):
 
 def _perm(rng, H, dk):
     return np.stack([rng.permutation(dk) for _ in range(H)]).astype(np.int32)
+
+
+def state_bars_batch(g, o, perm, K_hi, dk, val_perm=None, val_scale=None):
+    """_state_bars over a whole batch, request range by request range on every host
+    thread; the code-disagreement fraction is taken over all INT8 values, every other
+    figure is the worst over the ranges."""
+    import oracle_par
+
+    n = o[2].shape[0]
+
+    def run(b0, b1):
+        w = _state_bars(tuple(a[b0:b1] for a in g), tuple(a[b0:b1] for a in o), perm, K_hi, dk,
+                        val_perm=val_perm, val_scale=val_scale)
+        return w, o[1][b0:b1].size
+
+    parts = oracle_par.pmap(run, n)
+    total = sum(c for _, c in parts)
+    w = {k: max(p[k] for p, _ in parts) for k in parts[0][0]}
+    w["frac"] = sum(p["frac"] * c for p, c in parts) / total if total else 0.0
+    return w

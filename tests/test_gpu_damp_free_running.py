@@ -1,0 +1,138 @@
+"""The mixed-precision step free-running for 100 steps at the serving shape, every head
+against the float64 oracle ([DAMP] §3.3 Eq. (7)-(13)).
+
+Three trajectories (and a fourth, below) start from the same point and take the same
+100 steps of the workload's inputs (batch 256 x 32 heads x 128 x 128, K_hi = 16, per-channel decay):
+
+* the GPU's quantised recurrence S^q_t = Q(A_t S^q_{t-1} + beta k v^T) (damp_step);
+* the oracle's quantised recurrence, same equation, float64 update with the stored
+  FP16 / INT8 / FP32-scale representation between steps;
+* the oracle's unquantised FP32-state recurrence (float64), from the FP32 state the
+  packed one was quantised from.
+
+Neither quantised side is re-synchronised with the other.  A code that rounds the other
+way at a half-integer (allowed: the FP32 update and the float64 update differ in the
+last bits) changes that row's next update, and rounding decisions keep cascading
+([DAMP] Eq. (8)-(12): each step's requantisation error R_t is new, A_t only damps the
+old ones), so two valid quantised trajectories drift apart while each stays as close to
+the unquantised recurrence as the other.  The size of that separation is measured, not
+assumed: a fourth trajectory runs the oracle's quantised recurrence with beta raised by
+one FP32 ulp at every step (a perturbation at the level of the GPU's FP32 rounding).
+
+Reported at steps 1, 32 and 100 for the whole batch: the fraction of INT8 codes that
+differ, the largest code difference, FP16 ulps, the dequantised state's distance from
+the oracle's quantised trajectory (worst head, relative Frobenius, and over the batch),
+the readout's distance from the oracle's quantised readout, each quantised
+trajectory's drift from the unquantised one (state and readout, relative Frobenius over
+the batch), and the same separation figures for the one-ulp trajectory.
+
+Gates: step 1 starts both sides from the same packed state, so it is the teacher-forced
+case and meets its bars; at every reported step the GPU's drift from the unquantised
+recurrence is of the oracle's size (<= 1.5 x the oracle's + 1e-4), and the GPU's
+separation from the oracle's quantised trajectory (code-disagreement fraction, state
+and readout over the batch) is at most 3 x + 1e-6 the separation one ulp of beta
+causes, with the largest code difference at most 2 above the one-ulp trajectory's."""
+import json
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_par
+import synth
+from damp_util import _assert_bars, _packed_dev, _packed_host, state_bars_batch
+from gpu_util import dev, dev_inputs, f64_inputs, host, need_gpu
+
+pytestmark = pytest.mark.gpu
+REPORT_AT = (1, 32, 100)
+
+
+def _nrm(a):
+    return float(np.linalg.norm(np.asarray(a).reshape(-1)))
+
+
+@pytest.mark.parametrize("name", ["damp_kda", "damp_kda_g32sr"])
+def test_mixed_precision_free_running_100_steps_every_head(name):
+    hla = need_gpu()
+    cfg = synth.CONFIGS[name]
+    group = synth.damp_group(cfg)
+    perm = synth.damp_key_perm(cfg)
+    vp = vs = None
+    if cfg.sr:
+        vp, vs = synth.damp_value_plan(cfg)
+    vp_d = None if vp is None else dev(vp)
+    vs_d = None if vs is None else dev(vs)
+    perm_d = dev(perm)
+    S_fp = synth.initial_state(cfg).astype(np.float64)
+    parts = oracle_par.pmap(lambda b0, b1: oracle.damp_quantize(
+        S_fp[b0:b1], perm, cfg.K_hi, group=group, val_perm=vp, val_scale=vs), cfg.B)
+    hi, lo, sc = (np.concatenate([p[i] for p in parts]) for i in range(3))
+    del parts
+    hi_d, lo_d, sc_d = _packed_dev(hi, lo, sc)
+    pert = tuple(a.copy() for a in (hi, lo, sc))  # the one-ulp-of-beta trajectory
+    report = {}
+    with ThreadPoolExecutor(1) as pre:  # the next step's inputs are drawn meanwhile
+        nxt = pre.submit(synth.step_inputs, cfg, 0)
+        for t in range(1, max(REPORT_AT) + 1):
+            x = nxt.result()
+            if t < max(REPORT_AT):
+                nxt = pre.submit(synth.step_inputs, cfg, t)
+            xd = dev_inputs(x, cfg.in_dtype)
+            o_g = hla.damp_step(hi_d, lo_d, sc_d, perm_d, cfg.K_hi, xd["q"], xd["k"], xd["v"],
+                                xd["alpha"], 1, xd["beta"], val_perm=vp_d, val_scale=vs_d)
+            x64 = f64_inputs(x, cfg.in_dtype)
+            o_q = oracle_par.damp_step(hi, lo, sc, perm, cfg.K_hi, x64, per_channel=True,
+                                       val_perm=vp, val_scale=vs)
+            o_f = oracle_par.delta_step(S_fp, x64, per_channel=True)
+            xp = dict(x64, beta=np.nextafter(x["beta"], np.float32(np.inf)).astype(np.float64))
+            o_p = oracle_par.damp_step(*pert, perm, cfg.K_hi, xp, per_channel=True,
+                                       val_perm=vp, val_scale=vs)
+            if t not in REPORT_AT:
+                continue
+            g = _packed_host(hi_d, lo_d, sc_d)
+            w = state_bars_batch(g, (hi, lo, sc), perm, cfg.K_hi, cfg.dk, val_perm=vp,
+                                 val_scale=vs)
+            o_gh = host(o_g)
+            w["out"] = oracle_par.rel_err_tiles(o_gh, o_q, 1)
+            deq_g = oracle_par.damp_dequantize(*g, perm, cfg.K_hi, cfg.dk, val_perm=vp,
+                                               val_scale=vs)
+            deq_o = oracle_par.damp_dequantize(hi, lo, sc, perm, cfg.K_hi, cfg.dk,
+                                               val_perm=vp, val_scale=vs)
+            nf, nof = _nrm(S_fp), _nrm(o_f)
+            r = dict(code_frac=w["frac"], code_max_diff=w["dmax"], fp16_ulps=w["fp16_ulps"],
+                     code_steps=w["code_steps"], scale_rel=w["scale_rel"],
+                     state_vs_oracle_worst_head=w["state"],
+                     state_vs_oracle=_nrm(deq_g - deq_o) / _nrm(deq_o),
+                     out_vs_oracle_worst_head=w["out"],
+                     drift_gpu=_nrm(deq_g - S_fp) / nf, drift_oracle=_nrm(deq_o - S_fp) / nf,
+                     out_drift_gpu=_nrm(o_gh - o_f) / nof, out_drift_oracle=_nrm(o_q - o_f) / nof)
+            wp = state_bars_batch(pert, (hi, lo, sc), perm, cfg.K_hi, cfg.dk, val_perm=vp,
+                                  val_scale=vs)
+            deq_p = oracle_par.damp_dequantize(*pert, perm, cfg.K_hi, cfg.dk, val_perm=vp,
+                                               val_scale=vs)
+            r.update(ulp_code_frac=wp["frac"], ulp_code_max_diff=wp["dmax"],
+                     ulp_state_vs_oracle=_nrm(deq_p - deq_o) / _nrm(deq_o),
+                     ulp_out_vs_oracle=_nrm(o_p - o_q) / _nrm(o_q),
+                     out_vs_oracle=_nrm(o_gh - o_q) / _nrm(o_q))
+            del deq_g, deq_o, deq_p, g
+            report[t] = r
+            print(f"{name} step {t}: " + ", ".join(
+                f"{k}={v:.3g}" if isinstance(v, float) else f"{k}={v}" for k, v in r.items()),
+                flush=True)
+            if t == 1:
+                _assert_bars(w)  # same packed start: one teacher-forced step
+    out_dir = os.environ.get("HLA_REPORT_DIR")
+    if out_dir:
+        os.makedirs(out_dir, exist_ok=True)
+        with open(os.path.join(out_dir, f"damp_free_running_{name}.json"), "w") as f:
+            json.dump(dict(workload=name, heads=cfg.B * cfg.H, steps=max(REPORT_AT),
+                           at=report), f, indent=1)
+    for t, r in report.items():
+        assert r["drift_gpu"] <= 1.5 * r["drift_oracle"] + 1e-4, (t, r)
+        assert r["out_drift_gpu"] <= 1.5 * r["out_drift_oracle"] + 1e-4, (t, r)
+        assert r["code_frac"] <= 3 * r["ulp_code_frac"] + 1e-6, (t, r)
+        assert r["code_max_diff"] <= r["ulp_code_max_diff"] + 2, (t, r)
+        assert r["state_vs_oracle"] <= 3 * r["ulp_state_vs_oracle"] + 1e-6, (t, r)
+        assert r["out_vs_oracle"] <= 3 * r["ulp_out_vs_oracle"] + 1e-6, (t, r)

@@ -191,6 +191,45 @@ def test_damp_trajectory_obeys_error_propagation_identity(orc):
         Sq_prev = Sq
 
 
+def test_quantised_trajectories_separate_under_one_ulp(orc):
+    """DAMP Eq. (8)-(12) have a new storage error R_t at every step: a perturbation at the
+    level of FP32 rounding (beta raised by one FP32 ulp at every step) flips codes at
+    rounding boundaries, and the flips cascade, so after 100 free-running steps the two
+    quantised trajectories disagree on many codes by several steps, while each stays as
+    close to the unquantised recurrence as the other.  This is why free-running code
+    agreement between two implementations that round differently in FP32 cannot be
+    gated at the teacher-forced bars; it is gated against this measured separation."""
+    import synth
+
+    cfg = synth.shrink(synth.CONFIGS["damp_kda"], B=4, H=8)
+    perm = synth.damp_key_perm(cfg)
+    S = synth.initial_state(cfg).astype(np.float64)
+    a = orc.damp_quantize(S, perm, cfg.K_hi)
+    p = tuple(x.copy() for x in a)
+
+    def f64(x):
+        return {n: (synth.stored_to_f64(v, cfg.in_dtype) if n in ("q", "k", "v")
+                    else v.astype(np.float64)) for n, v in x.items()}
+
+    for t in range(100):
+        x = synth.step_inputs(cfg, t)
+        xa = f64(x)
+        xp = dict(xa, beta=np.nextafter(x["beta"], np.float32(np.inf)).astype(np.float64))
+        orc.damp_step(*a, perm, cfg.K_hi, xa["q"], xa["k"], xa["v"], xa["alpha"], xa["beta"],
+                      per_channel=True)
+        orc.damp_step(*p, perm, cfg.K_hi, xp["q"], xp["k"], xp["v"], xp["alpha"], xp["beta"],
+                      per_channel=True)
+        orc.kda_step(S, xa["q"], xa["k"], xa["v"], xa["alpha"], xa["beta"])
+    d = np.abs(a[1].astype(np.int32) - p[1].astype(np.int32))
+    assert d.mean() > 0 and (d > 0).mean() > 0.01 and d.max() >= 2
+    da = orc.damp_dequantize(*a, perm, cfg.K_hi, cfg.dk)
+    dp = orc.damp_dequantize(*p, perm, cfg.K_hi, cfg.dk)
+    n = np.linalg.norm
+    drift_a, drift_p = n(da - S) / n(S), n(dp - S) / n(S)
+    assert abs(drift_a - drift_p) <= 0.05 * drift_a
+    assert n(dp - da) / n(da) > 1e-3  # the separation is a sizeable part of the drift
+
+
 def _bits_per_value(dk, dv, K_hi, group):
     """Storage bits per state value: FP16 rows, INT8 rows, FP32 scales per `group` values."""
     bits = K_hi * dv * 16 + (dk - K_hi) * (dv * 8 + (dv // group) * 32)
