@@ -66,3 +66,16 @@ def test_speculative_bytes_recounted():
 def test_traffic_only_for_the_profiled_source():
     assert bench.traffic_from_profile("gdn_step", ["bench.py"]) is None
     assert bench.traffic_from_profile("no_such_kernel", bench.STEP_SOURCES) is None
+
+
+def test_cpu_baseline_runs_the_oracle_on_the_gpu_inputs():
+    """The CPU baseline's fields, on the input sets the caller names (the benchmark passes
+    the ones its first timed GPU steps use); a short budget keeps this test quick."""
+    import synth
+
+    r = bench.cpu_baseline(synth, 0.4, (3, 4))
+    assert r["kind"] == "oracle" and r["cores"] == 1 and r["unit"] == "GB/s" and r["value"] > 0
+    assert "input sets [3, 4]" in r["sample"]
+    assert r["host_cpus"] >= 1 and r["cpu_model"]
+    if "all_cores" in r:
+        assert r["all_cores"]["cores"] == bench.host_threads() and r["all_cores"]["value"] > 0
