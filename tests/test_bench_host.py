@@ -79,3 +79,21 @@ def test_cpu_baseline_runs_the_oracle_on_the_gpu_inputs():
     assert r["host_cpus"] >= 1 and r["cpu_model"]
     if "all_cores" in r:
         assert r["all_cores"]["cores"] == bench.host_threads() and r["all_cores"]["value"] > 0
+
+
+def test_free_running_figures_only_for_the_recorded_source(tmp_path, monkeypatch):
+    """The benchmark quotes the recorded free-running figures only when they were taken on
+    the current mixed-precision kernel source."""
+    import json
+
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    assert bench.drift_vs_oracle("damp_kda") is None
+    rec = {"1": {"code_frac": 1e-6, "drift_gpu": 0.007, "drift_oracle": 0.007, "other": 1}}
+    for h, want in (("0" * 16, None), (bench.source_hash(bench.DAMP_SOURCES), "match")):
+        (tmp_path / "damp_free_running_damp_kda.json").write_text(
+            json.dumps({"source_hash": h, "at": rec}))
+        got = bench.drift_vs_oracle("damp_kda")
+        if want is None:
+            assert got is None
+        else:
+            assert got == {"1": {"code_frac": 1e-6, "drift_gpu": 0.007, "drift_oracle": 0.007}}

@@ -126,9 +126,12 @@ def test_mixed_precision_free_running_100_steps_every_head(name):
     out_dir = os.environ.get("HLA_REPORT_DIR")
     if out_dir:
         os.makedirs(out_dir, exist_ok=True)
+        import bench  # the kernel-source hash the benchmark checks before quoting these
+
         with open(os.path.join(out_dir, f"damp_free_running_{name}.json"), "w") as f:
             json.dump(dict(workload=name, heads=cfg.B * cfg.H, steps=max(REPORT_AT),
-                           at=report), f, indent=1)
+                           source_hash=bench.source_hash(bench.DAMP_SOURCES), at=report), f,
+                      indent=1)
     for t, r in report.items():
         assert r["drift_gpu"] <= 1.5 * r["drift_oracle"] + 1e-4, (t, r)
         assert r["out_drift_gpu"] <= 1.5 * r["out_drift_oracle"] + 1e-4, (t, r)
