@@ -180,3 +180,40 @@ def rel_err_tiles(got, ref, tile_dims: int = 2) -> float:
         return float((num / den).max())
 
     return max(pmap(run, n))
+
+
+def dasc_pack_int8_all(active, offsets, unit_index):
+    """oracle.dasc_pack_int8 of every slot of `active` (float32 [L, S, n_units, unit_rows,
+    dv]) into checkpoint slot of the same index, slot range by slot range on every host
+    thread.  Returns (codes int8 [S, R, unit_rows, dv], scales float32 [S, R, unit_rows])."""
+    L, S, n_units, unit_rows, dv = active.shape
+    R = int(offsets[-1])
+    codes = np.empty((S, R, unit_rows, dv), np.int8)
+    scales = np.empty((S, R, unit_rows), np.float32)
+
+    def run(b0, b1):
+        ids = np.arange(b1 - b0, dtype=np.int32)
+        c, s = oracle.dasc_pack_int8(np.ascontiguousarray(active[:, b0:b1]), offsets,
+                                     unit_index, ids, ids, b1 - b0)
+        codes[b0:b1] = c
+        scales[b0:b1] = s
+
+    pmap(run, S)
+    return codes, scales
+
+
+def dasc_restore_int8_all(codes, scales, offsets, unit_index, L, n_units, active_out):
+    """oracle.dasc_restore_int8 of checkpoint slot s into slot s of active_out (float32
+    [L, S, n_units, unit_rows, dv], in place) for every slot, by slot ranges."""
+    S = codes.shape[0]
+
+    def run(b0, b1):
+        ids = np.arange(b1 - b0, dtype=np.int32)
+        part = np.ascontiguousarray(active_out[:, b0:b1])
+        oracle.dasc_restore_int8(np.ascontiguousarray(codes[b0:b1]),
+                                 np.ascontiguousarray(scales[b0:b1]), offsets, unit_index, L,
+                                 n_units, ids, ids, part)
+        active_out[:, b0:b1] = part
+
+    pmap(run, S)
+    return active_out

@@ -67,13 +67,36 @@ def test_pack_and_restore_int8(unit_rows, dv, n_units, p_keep):
     assert int(err.item()) == 0
 
 
+def _every_pair_against_oracle(hla, act_h, codes, scales, offsets, unit_index, unit_pos, R):
+    """All 512 pairs of a full-size checkpoint workload: the GPU's pack against the oracle's
+    (scales bit-exact, codes within one step on at most 0.1%), then the oracle's checkpoint
+    restored on the GPU against the oracle's restore, every byte of the 4 GiB."""
+    import oracle_par
+
+    L, S_, nu, ur, dv = act_h.shape
+    c_o, s_o = oracle_par.dasc_pack_int8_all(act_h, offsets, unit_index)
+    assert np.array_equal(host(scales).reshape(s_o.shape), s_o)
+    c_g = codes.cpu().numpy().reshape(c_o.shape)
+    diff = np.abs(c_g.astype(np.int16) - c_o.astype(np.int16))
+    assert diff.max() <= 1 and (diff > 0).mean() <= CODE_FRAC, (diff.max(), (diff > 0).mean())
+    del c_g, diff
+    ids = dev(np.arange(S_, dtype=np.int32))
+    out = torch.full((L, S_, nu, ur, dv), float("nan"), device="cuda")
+    hla.dasc_restore_int8(dev(c_o), dev(s_o), S_, R, dev(unit_pos.reshape(-1)), L, nu, ur, dv,
+                          ids, ids, out, S_ * nu * ur * dv * 4, S_)
+    ref = np.full(act_h.shape, np.nan, np.float32)
+    oracle_par.dasc_restore_int8_all(c_o, s_o, offsets, unit_index, L, nu, ref)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
 def test_kda_checkpoint_workload_static_horizon_selection():
     """4 layers x 512 request states x 32 heads x 128 key channels, one unit per channel
     row (512 B), selected by static horizons (softplus gate, a_s = -0.3, W_max = 16) from
     the synthetic gate parameters: INT8 pack of all 512 states, restore into 512 private
     slots.  Over the whole 4 GiB state: every retained value within half a quantisation
     step of the original (plus the rounding slack of the GPU quantiser), every omitted
-    value zero; 4 sampled pairs against the oracle."""
+    value zero; every pair against the oracle (pack at the quantiser bars, restore of the
+    oracle's checkpoint bit for bit)."""
     hla = need_gpu()
     cfg = synth.CONFIGS["dasc_kda"]
     A, d = synth.gate_params(cfg)
@@ -99,14 +122,8 @@ def test_kda_checkpoint_workload_static_horizon_selection():
     bound = (0.5 + 5e-5) * step + act.abs() * 2.0 ** -23
     assert bool(((out - act).abs() <= bound)[keep.expand_as(act)].all())
     assert bool((out[~keep.expand_as(act)] == 0).all())
-    g = np.random.default_rng(3)
-    for s in g.choice(S_, size=4, replace=False):
-        a_s = act[:, s:s + 1].cpu().numpy().reshape(L, 1, nu, 1, dv)
-        c_o, s_o = oracle.dasc_pack_int8(a_s, offsets, unit_index, np.zeros(1, np.int32),
-                                         np.zeros(1, np.int32), 1)
-        assert np.array_equal(scales[s].cpu().numpy(), s_o[0])
-        diff = np.abs(codes[s].cpu().numpy().astype(int) - c_o[0].astype(int))
-        assert diff.max() <= 1 and (diff > 0).mean() <= CODE_FRAC
+    _every_pair_against_oracle(hla, act.cpu().numpy().reshape(L, S_, nu, 1, dv), codes, scales,
+                               offsets, unit_index, unit_pos, R)
 
 
 def test_refresh_local_bit_exact():
@@ -184,8 +201,8 @@ def test_gdn_checkpoint_workload_head_units():
     """4 layers x 512 request states x 32 heads of 128 x 128 FP32 (4 GiB), the seeded
     ragged head selection (64 of 128 heads): INT8 pack of all 512 states, restore into
     512 private slots.  Every retained value within half a quantisation step (plus the
-    GPU quantiser's rounding slack), every omitted head zero; 3 sampled pairs against the
-    oracle."""
+    GPU quantiser's rounding slack), every omitted head zero; every pair against the
+    oracle (pack at the quantiser bars, restore of the oracle's checkpoint bit for bit)."""
     hla = need_gpu()
     cfg = synth.CONFIGS["dasc_gdn"]
     mask = synth.dasc_masks(cfg)
@@ -207,14 +224,8 @@ def test_gdn_checkpoint_workload_head_units():
     bound = (0.5 + 5e-5) * step + act.abs() * 2.0 ** -23
     assert bool(((out - act).abs() <= bound)[keep].all())
     assert bool((out[~keep] == 0).all())
-    g = np.random.default_rng(4)
-    for s in g.choice(S_, size=3, replace=False):
-        a_s = act[:, s:s + 1].cpu().numpy()
-        c_o, s_o = oracle.dasc_pack_int8(a_s, offsets, unit_index, np.zeros(1, np.int32),
-                                         np.zeros(1, np.int32), 1)
-        assert np.array_equal(scales[s].cpu().numpy(), s_o[0])
-        diff = np.abs(codes[s].cpu().numpy().astype(int) - c_o[0].astype(int))
-        assert diff.max() <= 1 and (diff > 0).mean() <= CODE_FRAC
+    _every_pair_against_oracle(hla, act.cpu().numpy(), codes, scales, offsets, unit_index,
+                               unit_pos, R)
 
 
 def test_kda_refresh_local_workload():
