@@ -205,6 +205,60 @@ int check_dasc_tables(Range w0, Range w1, const int32_t *offsets, int L,
     return HLA_OK;
 }
 
+int check_restore_replay(const RestoreReplayArgs &a)
+{
+    if (a.N < 0 || a.L <= 0 || a.H <= 0 || a.S_ckpt < 0 || a.S_dst < 0 || a.R_total < 0 ||
+        a.layer_stride_bytes < 0)
+        return HLA_ERR_SHAPE;
+    if (a.K < 1 || a.K > 16) return HLA_ERR_SHAPE;
+    if (!dtype_ok(a.in_dtype) || !dtype_ok(a.out_dtype)) return HLA_ERR_DTYPE;
+    if (a.decay != HLA_DECAY_SCALAR && a.decay != HLA_DECAY_VECTOR) return HLA_ERR_DTYPE;
+    if (!head_dim_ok(a.dk) || !head_dim_ok(a.dv)) return HLA_ERR_UNSUPPORTED;
+    if ((int64_t)a.R_total > (int64_t)a.L * a.H) return HLA_ERR_PLAN;
+    if (a.N == 0) return HLA_OK;
+    if ((a.R_total > 0 && !a.packed) || !a.unit_pos || !a.src_slot || !a.dst_slot ||
+        !a.active_out || !a.q || !a.k || !a.v || !a.alpha || !a.beta || !a.n_accept)
+        return HLA_ERR_NULL;
+    const bool vec = a.decay == HLA_DECAY_VECTOR;
+    if ((a.packed && !aligned16(a.packed)) || !aligned16(a.active_out) || !aligned16(a.q) ||
+        !aligned16(a.k) || !aligned16(a.v) || (a.out && !aligned16(a.out)) ||
+        (vec && !aligned16(a.alpha)) || a.layer_stride_bytes % 16 != 0)
+        return HLA_ERR_ALIGN;
+    // sizes: workgroups (l, n, h) and (l, n, t, h) tokens must fit 32-bit indices; the
+    // byte spans must fit 64 bits
+    const int64_t head = (int64_t)a.dk * a.dv * 4;
+    int64_t groups, toks, layer_bytes, span, pk_bytes;
+    if (!mul3_ok(a.L, a.N, a.H, groups) || groups > (int64_t)INT_MAX ||
+        !mul_ok(groups, a.K, toks) || toks > (int64_t)INT_MAX)
+        return HLA_ERR_SHAPE;
+    if (!mul3_ok(a.S_dst, a.H, head, layer_bytes)) return HLA_ERR_SHAPE;
+    if (a.L > 1 && a.layer_stride_bytes < layer_bytes) return HLA_ERR_SHAPE;
+    if (!mul_ok(a.L - 1, a.layer_stride_bytes, span) ||
+        __builtin_add_overflow(span, layer_bytes, &span) ||
+        !mul3_ok(a.S_ckpt, a.R_total, head, pk_bytes))
+        return HLA_ERR_SHAPE;
+    const size_t es = dtype_bytes(a.in_dtype), os = dtype_bytes(a.out_dtype);
+    const size_t nt = (size_t)toks;
+    const Range act{a.active_out, (size_t)span};
+    const Range outr{a.out, nt * a.dv * os};
+    const Range ins[] = {
+        {a.packed, (size_t)pk_bytes},
+        {a.q, nt * a.dk * es},
+        {a.k, nt * a.dk * es},
+        {a.v, nt * a.dv * es},
+        {a.alpha, nt * (vec ? a.dk : 1) * sizeof(float)},
+        {a.beta, nt * sizeof(float)},
+        {a.unit_pos, (size_t)a.L * a.H * sizeof(int32_t)},
+        {a.src_slot, (size_t)a.N * sizeof(int32_t)},
+        {a.dst_slot, (size_t)a.N * sizeof(int32_t)},
+        {a.n_accept, (size_t)a.N * sizeof(int32_t)},
+    };
+    for (const Range &r : ins)
+        if (overlaps(act, r) || overlaps(outr, r)) return HLA_ERR_ALIAS;
+    if (overlaps(act, outr)) return HLA_ERR_ALIAS;
+    return HLA_OK;
+}
+
 int check_dasc_int8(const void *active, int64_t layer_stride_bytes, int S_act, int L,
                     int n_units, int unit_rows, int dv, const void *table_a,
                     const void *table_b, int R_total, const int32_t *src_slot,
@@ -257,7 +311,7 @@ const char *hla_status_str(int status)
     }
 }
 
-int hla_version(void) { return 101; }
+int hla_version(void) { return 102; }
 
 // Ragged plan ([dasc] App. B, Scheme 2): r_l retained units per layer,
 // o_0 = 0, o_{l+1} = o_l + r_l, retained units of layer l at flat positions

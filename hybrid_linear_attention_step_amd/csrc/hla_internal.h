@@ -137,6 +137,30 @@ int check_dasc_int8(const void *active, int64_t layer_stride_bytes, int S_act, i
                     const int32_t *dst_slot, int N, const void *codes, const void *scales,
                     int S_ckpt);
 
+// dasc_restore_replay: a checkpoint of whole-head units restored into private
+// slots with each request's accepted drafts replayed on the way.
+struct RestoreReplayArgs {
+    const float *packed;
+    int S_ckpt, R_total;
+    const int32_t *unit_pos;
+    int L;
+    const int32_t *src_slot, *dst_slot;
+    int N;
+    float *active_out;
+    int64_t layer_stride_bytes;
+    int S_dst, H, dk, dv, K;
+    const void *q, *k, *v;
+    int in_dtype;
+    const float *alpha;
+    int decay;
+    const float *beta;
+    const int32_t *n_accept;
+    void *out;
+    int out_dtype;
+};
+
+int check_restore_replay(const RestoreReplayArgs &a);
+
 // log2 of a power of two (checked by the caller).
 inline int log2_exact(int x)
 {

@@ -251,11 +251,96 @@ k_delta_step(float *__restrict__ state, int n_slots, const int32_t *__restrict__
     }
 }
 
+// Draft-token inputs staged in LDS.  A workgroup that replays n_b tokens copies all of
+// their inputs into LDS at once, with the direct global-to-LDS load (global_load_lds,
+// 16 bytes per lane; a wave's 64 lanes fill 1 KiB of LDS in lane order), issued together
+// with the state tile's loads; the token loop then reads each token from LDS.  So the
+// tokens cost one memory round trip per workgroup instead of one each, which matters
+// most for a head that starts from zero (no state read to hide the token loads behind).
+// Token t takes WG consecutive 16-byte words: q, k, v and (per-channel decay) alpha, as
+// stored; the scalar decay and beta sit in one float2 per token after the K tokens.
+template <int DK, int DV, typename TIn, bool VEC>
+struct TokenLds {
+    static constexpr int QB = DK * (int)sizeof(TIn) / 16;  // words of q (and of k)
+    static constexpr int VB = DV * (int)sizeof(TIn) / 16;  // words of v
+    static constexpr int AB = VEC ? DK * 4 / 16 : 0;        // words of a vector decay
+    static constexpr int WG = 2 * QB + VB + AB;            // words per token
+    static size_t bytes(int K) { return (size_t)K * (WG * 16 + sizeof(float2)); }
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Issue the staging copies of tokens [0, nb) of workgroup (ln, h); every wave of the
+// workgroup takes 64 words per pass.  The LDS address of a wave's copy is wave-uniform.
+template <int DK, int DV, typename TIn, bool VEC>
+__device__ __forceinline__ void stage_tokens(uint8_t *lds, int nb, size_t tok0, int H,
+                                             const TIn *q, const TIn *k, const TIn *v,
+                                             const float *alpha, const float *beta, int K)
+{
+    using T = TokenLds<DK, DV, TIn, VEC>;
+    constexpr int NW = 2 * DV / 64;  // waves per workgroup
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int total = nb * T::WG;
+    for (int w0 = wave * 64; w0 < total; w0 += NW * 64) {
+        const int f = w0 + lane;
+        if (f < total) {
+            const int t = f / T::WG, i = f - t * T::WG;
+            const size_t tok = tok0 + (size_t)t * H;
+            const uint8_t *src;
+            if (i < T::QB)
+                src = reinterpret_cast<const uint8_t *>(q + tok * DK) + i * 16;
+            else if (i < 2 * T::QB)
+                src = reinterpret_cast<const uint8_t *>(k + tok * DK) + (i - T::QB) * 16;
+            else if (i < 2 * T::QB + T::VB)
+                src = reinterpret_cast<const uint8_t *>(v + tok * DV) + (i - 2 * T::QB) * 16;
+            else
+                src = reinterpret_cast<const uint8_t *>(alpha + tok * DK) +
+                      (i - 2 * T::QB - T::VB) * 16;
+            __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(lds + (size_t)w0 * 16), 16, 0,
+                                             0);
+        }
+    }
+    float2 *ab = reinterpret_cast<float2 *>(lds + (size_t)K * T::WG * 16);
+    if ((int)threadIdx.x < nb) {
+        const size_t tok = tok0 + (size_t)threadIdx.x * H;
+        ab[threadIdx.x] = make_float2(VEC ? 0.0f : alpha[tok], beta[tok]);
+    }
+}
+
+// Token t's per-lane inputs from LDS, in the layout token_load gives.
+template <int DK, int DV, typename TIn, bool VEC>
+__device__ __forceinline__ void token_from_lds(const uint8_t *lds, int t, int K, int row0,
+                                               int col0, TokenRaw<DK, TIn, VEC> &R)
+{
+    using T = TokenLds<DK, DV, TIn, VEC>;
+    using TR = TokenRaw<DK, TIn, VEC>;
+    const u32x4 *w = reinterpret_cast<const u32x4 *>(lds) + (size_t)t * T::WG;
+    const int r = row0 * (int)sizeof(TIn) / 16;
+#pragma unroll
+    for (int i = 0; i < TR::QW; ++i) {
+        R.q[i] = w[r + i];
+        R.k[i] = w[T::QB + r + i];
+    }
+    if constexpr (VEC) {
+#pragma unroll
+        for (int i = 0; i < TR::RPL / 4; ++i) R.a[i] = w[2 * T::QB + T::VB + row0 / 4 + i];
+    }
+    if constexpr (sizeof(TIn) == 2)
+        R.v2 = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint8_t *>(w + 2 * T::QB) +
+                                                col0 * 2);
+    else
+        R.v4 = w[2 * T::QB + col0 / 4];
+    const float2 ab = reinterpret_cast<const float2 *>(lds + (size_t)K * T::WG * 16)[t];
+    R.a0 = ab.x;
+    R.b0 = ab.y;
+}
+
 // Several tokens per (request, head) with the tile held in registers
 // throughout ("Serving recurrent attention", part "Speculative decoding
 // without state snapshots"):
-//   MODE_REPLAY  the first n_b of K cached draft projections; the state is
-//                read once and written once, and not touched when n_b = 0;
+//   MODE_REPLAY  the first n_b of K cached draft projections (their inputs
+//                staged in LDS); the state is read once and written once, and
+//                not touched when n_b = 0;
 //   MODE_BONUS   the same, then the target model's bonus token ([B, H, .]
 //                inputs, applied also when n_b = 0), then one write.
 template <int DK, int DV, typename TIn, typename TOut, bool VEC, int MODE>
@@ -268,6 +353,7 @@ k_tokens(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
          const float *__restrict__ alpha_b, const float *__restrict__ beta_b,
          TOut *__restrict__ out_b, int32_t *__restrict__ err)
 {
+    extern __shared__ __attribute__((aligned(16))) uint8_t tok_lds[];
     constexpr int RPL = DK / 8;
     const int bh = blockIdx.x;
     const int b = bh / H, h = bh - b * H;
@@ -292,15 +378,20 @@ k_tokens(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
 
     float x[RPL][4];
     tile_load<RPL>(head, off, DV, x);
+    const size_t tok0 = (size_t)b * K * H + h;  // token t of (b, h) is tok0 + t * H
+    if (n > 0) {
+        stage_tokens<DK, DV, TIn, VEC>(tok_lds, n, tok0, H, q, k, v, alpha, beta, K);
+        __builtin_amdgcn_s_waitcnt(0);  // the copies into LDS (and the tile) have landed
+        __syncthreads();
+    }
     for (int t = 0; t < n; ++t) {
-        const size_t tok = ((size_t)b * K + t) * H + h;
         TokenRaw<DK, TIn, VEC> raw;
-        token_load<DK, DV, TIn, VEC>(q, k, v, alpha, beta, tok, row0, col0, raw);
+        token_from_lds<DK, DV, TIn, VEC>(tok_lds, t, K, row0, col0, raw);
         float vv[4];
         token_v<TIn>(raw.v2, raw.v4, vv);
         float o[4];
         tile_token_raw<DK, TIn, VEC>(x, raw, vv, raw.b0, o);
-        if (out && rg == 0) store_out4(out + tok * DV + col0, o);
+        if (out && rg == 0) store_out4(out + (tok0 + (size_t)t * H) * DV + col0, o);
     }
     if constexpr (MODE == MODE_BONUS) {
         TokenRaw<DK, TIn, VEC> raw;
@@ -314,13 +405,88 @@ k_tokens(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
     tile_store<RPL>(head_ptr, off, DV, x);
 }
 
+// A checkpoint of whole-head units restored into private slots with each request's
+// accepted drafts replayed on the way ("dasc: Decay-Aware State Compression for Hybrid
+// Linear-Attention Serving", §4.2 dasc-nr; "Serving recurrent attention", part
+// "Speculative decoding without state snapshots").  Workgroup (l, n, h): the head starts
+// as its packed copy from checkpoint slot src_slot[n] (or zero when head h of layer l is
+// not retained), takes the first n_b draft tokens of layer l in registers (their inputs
+// staged in LDS), and is written once into private slot dst_slot[n].  Same lane layout
+// and per-token function as the step, so the result is bitwise that of dasc_restore
+// followed by replay_accepted.
+template <int DK, int DV, typename TIn, typename TOut, bool VEC>
+__global__ void __launch_bounds__(2 * DV)
+k_restore_tokens(const float *__restrict__ packed, int S_ckpt, int R_total,
+                 const int32_t *__restrict__ unit_pos, int N,
+                 const int32_t *__restrict__ src_slot, const int32_t *__restrict__ dst_slot,
+                 float *__restrict__ active_out, int64_t layer_stride_floats, int S_dst, int H,
+                 int K, const TIn *__restrict__ q, const TIn *__restrict__ k,
+                 const TIn *__restrict__ v, const float *__restrict__ alpha,
+                 const float *__restrict__ beta, const int32_t *__restrict__ n_accept,
+                 TOut *__restrict__ out, int32_t *__restrict__ err)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t tok_lds[];
+    constexpr int RPL = DK / 8;
+    const int g = blockIdx.x;  // (l * N + n) * H + h
+    const int ln = g / H, h = g - ln * H;
+    const int l = ln / N, n = ln - l * N;
+    const int src = src_slot[n], dst = dst_slot[n];
+    if (src < 0 || src >= S_ckpt || dst < 0 || dst >= S_dst) {
+        if (err && threadIdx.x == 0) atomicOr(err, HLA_DEVERR_SLOT);
+        return;
+    }
+    int nb = n_accept[n];
+    if (nb < 0 || nb > K) {
+        if (err && threadIdx.x == 0 && h == 0 && l == 0) atomicOr(err, HLA_DEVERR_ACCEPT);
+        nb = nb < 0 ? 0 : K;
+    }
+    int pos = unit_pos[l * H + h];
+    if (pos >= R_total) {  // a bad plan entry: the head starts from zero, as a restore writes it
+        if (err && threadIdx.x == 0) atomicOr(err, HLA_DEVERR_PLAN);
+        pos = -1;
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int cg = lane & 7, rg = lane >> 3;
+    const int col0 = wave * 32 + cg * 4, row0 = rg * RPL;
+    const uint32_t off = (uint32_t)(row0 * DV + col0) * 4;
+
+    float x[RPL][4];
+    if (pos >= 0) {
+        const float *ck = packed + ((size_t)src * R_total + pos) * (DK * DV);
+        tile_load<RPL>(head_rsrc(ck, DK * DV * 4), off, DV, x);
+    } else {
+#pragma unroll
+        for (int m = 0; m < RPL; ++m)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) x[m][c] = 0.0f;
+    }
+    const size_t tok0 = (size_t)ln * K * H + h;  // token t of (l, n, h) is tok0 + t * H
+    if (nb > 0) {
+        stage_tokens<DK, DV, TIn, VEC>(tok_lds, nb, tok0, H, q, k, v, alpha, beta, K);
+        __builtin_amdgcn_s_waitcnt(0);  // the copies into LDS (and the tile) have landed
+        __syncthreads();
+    }
+    for (int t = 0; t < nb; ++t) {
+        TokenRaw<DK, TIn, VEC> raw;
+        token_from_lds<DK, DV, TIn, VEC>(tok_lds, t, K, row0, col0, raw);
+        float vv[4];
+        token_v<TIn>(raw.v2, raw.v4, vv);
+        float o[4];
+        tile_token_raw<DK, TIn, VEC>(x, raw, vv, raw.b0, o);
+        if (out && rg == 0) store_out4(out + (tok0 + (size_t)t * H) * DV + col0, o);
+    }
+    float *head_ptr = active_out + l * layer_stride_floats + ((size_t)dst * H + h) * (DK * DV);
+    tile_store<RPL>(head_ptr, off, DV, x);
+}
+
 // ----------------------------------------------------------------- dispatch
 
 template <int DK, int DV, typename TIn, typename TOut, bool VEC, int MODE>
 static void launch_tokens(const StepArgs &a, int32_t *err, hipStream_t st)
 {
     const dim3 grid((unsigned)((size_t)a.B * a.H)), block(2 * DV);
-    hipLaunchKernelGGL((k_tokens<DK, DV, TIn, TOut, VEC, MODE>), grid, block, 0, st, a.state,
+    const size_t lds = TokenLds<DK, DV, TIn, VEC>::bytes(a.K);
+    hipLaunchKernelGGL((k_tokens<DK, DV, TIn, TOut, VEC, MODE>), grid, block, lds, st, a.state,
                        a.n_slots, a.slot, a.H, a.K, (const TIn *)a.q, (const TIn *)a.k,
                        (const TIn *)a.v, a.alpha, a.beta, a.n_accept, (TOut *)a.out,
                        (const TIn *)a.qb, (const TIn *)a.kb, (const TIn *)a.vb, a.alpha_b,
@@ -363,6 +529,48 @@ static int launch_dtypes(const StepArgs &a, int32_t *err, hipStream_t st)
     if (a.in_dtype == HLA_F16) { HLA_STEP_OUT(f16_t) }
     HLA_STEP_OUT(float)
 #undef HLA_STEP_OUT
+}
+
+template <int DK, int DV, typename TIn, typename TOut, bool VEC>
+static void launch_restore_tokens(const RestoreReplayArgs &a, int32_t *err, hipStream_t st)
+{
+    const dim3 grid((unsigned)((size_t)a.L * a.N * a.H)), block(2 * DV);
+    const size_t lds = TokenLds<DK, DV, TIn, VEC>::bytes(a.K);
+    hipLaunchKernelGGL((k_restore_tokens<DK, DV, TIn, TOut, VEC>), grid, block, lds, st,
+                       a.packed, a.S_ckpt, a.R_total, a.unit_pos, a.N, a.src_slot, a.dst_slot,
+                       a.active_out, a.layer_stride_bytes / 4, a.S_dst, a.H, a.K,
+                       (const TIn *)a.q, (const TIn *)a.k, (const TIn *)a.v, a.alpha, a.beta,
+                       a.n_accept, (TOut *)a.out, err);
+}
+
+template <int DK, int DV>
+static void restore_tokens_dtypes(const RestoreReplayArgs &a, int32_t *err, hipStream_t st)
+{
+    const bool vec = a.decay == HLA_DECAY_VECTOR;
+#define HLA_RT_DECAY(TI_, TO_)                                                                \
+    if (vec) launch_restore_tokens<DK, DV, TI_, TO_, true>(a, err, st);                       \
+    else launch_restore_tokens<DK, DV, TI_, TO_, false>(a, err, st);
+#define HLA_RT_OUT(TI_)                                                                       \
+    if (a.out_dtype == HLA_BF16) { HLA_RT_DECAY(TI_, uint16_t) }                              \
+    else if (a.out_dtype == HLA_F16) { HLA_RT_DECAY(TI_, f16_t) }                             \
+    else { HLA_RT_DECAY(TI_, float) }
+    if (a.in_dtype == HLA_BF16) { HLA_RT_OUT(uint16_t) }
+    else if (a.in_dtype == HLA_F16) { HLA_RT_OUT(f16_t) }
+    else { HLA_RT_OUT(float) }
+#undef HLA_RT_OUT
+#undef HLA_RT_DECAY
+}
+
+static int run_restore_replay(const RestoreReplayArgs &a, int32_t *err, void *stream)
+{
+    int rc = check_restore_replay(a);
+    if (rc != HLA_OK || a.N == 0) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (a.dk == 128 && a.dv == 128) restore_tokens_dtypes<128, 128>(a, err, st);
+    else if (a.dk == 128 && a.dv == 64) restore_tokens_dtypes<128, 64>(a, err, st);
+    else if (a.dk == 64 && a.dv == 128) restore_tokens_dtypes<64, 128>(a, err, st);
+    else restore_tokens_dtypes<64, 64>(a, err, st);
+    return hipGetLastError() == hipSuccess ? HLA_OK : HLA_ERR_LAUNCH;
 }
 
 static int run_step(const StepArgs &a, int32_t *err, void *stream)
@@ -423,6 +631,22 @@ int replay_accepted_bonus(float *state, int n_slots, const int32_t *slot, int B,
                     beta,      n_accept, out,     out_dtype, hla::MODE_BONUS, q_bonus, k_bonus,
                     v_bonus,   alpha_bonus, beta_bonus, out_bonus};
     return hla::run_step(a, err_flag, stream);
+}
+
+int dasc_restore_replay(const float *packed, int S_ckpt, int R_total, const int32_t *unit_pos,
+                        int L, const int32_t *src_slot, const int32_t *dst_slot, int N,
+                        float *active_out, int64_t layer_stride_bytes, int S_dst, int H, int dk,
+                        int dv, int K, const void *q, const void *k, const void *v, int in_dtype,
+                        const float *alpha, int decay_kind, const float *beta,
+                        const int32_t *n_accept, void *out, int out_dtype, int32_t *err_flag,
+                        void *stream)
+{
+    hla::RestoreReplayArgs a{packed,     S_ckpt, R_total,   unit_pos,  L,    src_slot,
+                             dst_slot,   N,      active_out, layer_stride_bytes, S_dst, H,
+                             dk,         dv,     K,         q,         k,    v,
+                             in_dtype,   alpha,  decay_kind, beta,     n_accept, out,
+                             out_dtype};
+    return hla::run_restore_replay(a, err_flag, stream);
 }
 
 int verify_drafts(const float *state, int n_slots, const int32_t *slot, int B, int H, int dk,

@@ -85,7 +85,8 @@ enum hla_device_error {
 /* Static, NUL-terminated description of a status code.  Thread-safe. */
 HLA_API const char *hla_status_str(int status);
 
-/* Library ABI version (major * 100 + minor): 101 (1.01 added HLA_F16). */
+/* Library ABI version (major * 100 + minor): 102 (1.01 added HLA_F16, 1.02
+ * dasc_restore_replay). */
 HLA_API int hla_version(void);
 
 /* -------------------------------------------------------------------------
@@ -323,6 +324,52 @@ HLA_API int replay_accepted_bonus(float *state, int n_slots, const int32_t *slot
                           const void *k_bonus, const void *v_bonus, const float *alpha_bonus,
                           const float *beta_bonus, void *out_bonus, int out_dtype,
                           int32_t *err_flag, void *stream);
+
+/* -------------------------------------------------------------------------
+ * dasc_restore_replay -- dasc_restore of a checkpoint of whole-head units
+ * followed by replay_accepted, in one pass over each private state ([dasc]
+ * §4.2 dasc-nr restore, then [K3] "Speculative decoding without state
+ * snapshots": the accepted drafts are applied on-chip).  For each pair n < N,
+ * layer l < L and head h: the head of private slot dst_slot[n] in layer l
+ * starts as the packed head of checkpoint slot src_slot[n] when head h of
+ * layer l is retained, and as zero otherwise; the first n_b = n_accept[n]
+ * draft tokens of layer l are applied to it in order (clamped to [0, K]); it is
+ * written once.  The result equals dasc_restore followed by replay_accepted on
+ * each layer, bit for bit, with one state read (retained heads only) and one
+ * write instead of a read, two writes and a read.
+ *
+ * packed      device float32 [S_ckpt, R_total, dk, dv]: dasc_pack of head
+ *             units (unit_bytes = dk * dv * 4).  Only read.
+ * unit_pos    device int32 [L * H] from dasc_plan of the head mask; an entry
+ *             >= R_total sets HLA_DEVERR_PLAN and that head starts from zero.
+ * src_slot    device int32 [N] (< S_ckpt); dst_slot device int32 [N] (< S_dst,
+ *             distinct); a pair out of range is skipped (HLA_DEVERR_SLOT).
+ * active_out  device float32, layer l at active_out + l * layer_stride_bytes,
+ *             each layer [S_dst, H, dk, dv]; heads of slots no pair names are
+ *             left as they are.
+ * q, k        device [L, N, K, H, dk]; v device [L, N, K, H, dv] (in_dtype):
+ *             the draft projections of every layer.
+ * alpha       device float32 [L, N, K, H] (HLA_DECAY_SCALAR) or
+ *             [L, N, K, H, dk]; beta device float32 [L, N, K, H].
+ * n_accept    device int32 [N]: accepted drafts per request (every layer
+ *             replays the same count); values outside [0, K] are clamped and set
+ *             HLA_DEVERR_ACCEPT.
+ * out         device [L, N, K, H, dv] of out_dtype, or NULL: the readout after
+ *             each replayed token; rows t >= n_b are left untouched.
+ * 1 <= K <= 16; dk, dv in {64, 128}; layer_stride_bytes a multiple of 16 and
+ * >= S_dst * H * dk * dv * 4.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, UNSUPPORTED, PLAN (R_total > L * H), ALIAS
+ * (the private state overlapping the checkpoint, an input, a plan table or a
+ * slot map; the readout overlapping an input), LAUNCH.
+ * ---------------------------------------------------------------------- */
+HLA_API int dasc_restore_replay(const float *packed, int S_ckpt, int R_total,
+                                const int32_t *unit_pos, int L, const int32_t *src_slot,
+                                const int32_t *dst_slot, int N, float *active_out,
+                                int64_t layer_stride_bytes, int S_dst, int H, int dk, int dv,
+                                int K, const void *q, const void *k, const void *v,
+                                int in_dtype, const float *alpha, int decay_kind,
+                                const float *beta, const int32_t *n_accept, void *out,
+                                int out_dtype, int32_t *err_flag, void *stream);
 
 /* -------------------------------------------------------------------------
  * verify_drafts -- the recurrent layer's part of the target model's verify

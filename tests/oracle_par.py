@@ -162,6 +162,24 @@ def readout_scale(state64, q64, live=None):
     return out
 
 
+def replay_terms(state64, x64, n_accept, *, per_channel):
+    """The oracle's replay as n_b single steps per request (oracle.replay is exactly that),
+    in place on state64.  Returns the readouts [B, K, H, dv] (NaN for t >= n_b) and, for
+    each (b, t, h), the size of the readout's terms, max_j sum_i |S_t[i][j]| |q_t,i|: a
+    readout evaluated in FP32 has a rounding error relative to that size, not to its own,
+    which cancels whenever q and the state's columns are nearly orthogonal."""
+    B, K, H = x64["q"].shape[:3]
+    n_accept = np.clip(np.asarray(n_accept), 0, K)
+    out = np.full((B, K, H, state64.shape[-1]), np.nan)
+    scale = np.zeros((B, K, H))
+    for t in range(K):
+        live = n_accept > t
+        xt = {n: np.ascontiguousarray(a[:, t]) for n, a in x64.items()}
+        out[:, t] = delta_step(state64, xt, per_channel=per_channel, live=live)
+        scale[:, t] = readout_scale(state64, xt["q"], live)
+    return out, scale
+
+
 def rel_err_tiles(got, ref, tile_dims: int = 2) -> float:
     """max over tiles (the last `tile_dims` axes) of max|got - ref| / max|ref|, the
     denominator floored at 1e-30; NaN anywhere in got counts as an infinite error."""

@@ -47,7 +47,7 @@ def test_status_strings(L):
         assert len(hla.status_str(code)) > 0
     assert hla.status_str(0) == "ok"
     assert hla.status_str(99) == "unknown status"
-    assert L.hla_version() == 101
+    assert L.hla_version() == 102
 
 
 # Fake device addresses: never dereferenced, because every call below fails
@@ -212,6 +212,45 @@ def test_dasc_validation(L):
     for table in ("unit_pos", "src", "dst"):
         a = dict(rs, out=out, **{table: ctypes.c_void_p(out.value + 3 * 512 * 32 * 65536)})
         assert L.dasc_restore(*a.values()) == ALIAS, table
+
+
+def test_restore_replay_validation(L):
+    """The fused restore + replay: the checks of both halves, on the host."""
+    f = Fake()
+    ub = 128 * 128 * 4
+    base = dict(packed=f(), S_ckpt=512, R_total=64, unit_pos=f(), L=4, src=f(), dst=f(),
+                N=512, active_out=f(4 * 512 * 32 * ub), stride=512 * 32 * ub, S_dst=512, H=32,
+                dk=128, dv=128, K=8, q=f(), k=f(), v=f(), in_dtype=1, alpha=f(), decay=0,
+                beta=f(), n_accept=f(), out=None, out_dtype=0, err=None, stream=None)
+
+    def rr(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.dasc_restore_replay(*a.values())
+
+    assert rr(N=0) == OK
+    assert rr(K=0) == SHAPE and rr(K=17) == SHAPE and rr(L=0) == SHAPE
+    assert rr(R_total=129) == PLAN
+    assert rr(dk=96) == UNSUP and rr(in_dtype=7) == DTYPE and rr(decay=3) == DTYPE
+    for name in ("unit_pos", "src", "dst", "active_out", "q", "k", "v", "alpha", "beta",
+                 "n_accept"):
+        assert rr(**{name: None}) == NULL, name
+    assert rr(packed=None) == NULL
+    assert rr(stride=512 * 32 * ub - 16) == SHAPE     # layers would overlap
+    assert rr(stride=512 * 32 * ub + 4) == ALIGN
+    assert rr(v=ctypes.c_void_p(f().value + 8)) == ALIGN
+    assert rr(decay=1, alpha=ctypes.c_void_p(f().value + 4)) == ALIGN
+    assert rr(out=ctypes.c_void_p(f().value + 2), out_dtype=1) == ALIGN
+    assert rr(L=1 << 12, N=1 << 12, H=1 << 8) == SHAPE  # workgroups beyond 32-bit indices
+    # the private state over the checkpoint, an input or a table it reads while it writes;
+    # the readout over an input or the state
+    act = base["active_out"]
+    inside = ctypes.c_void_p(act.value + 3 * 512 * 32 * ub)
+    for name in ("packed", "unit_pos", "src", "dst", "q", "v", "alpha", "beta", "n_accept"):
+        assert rr(**{name: inside}) == ALIAS, name
+    o = f()
+    assert rr(out=o, q=ctypes.c_void_p(o.value + 64)) == ALIAS
+    assert rr(out=inside) == ALIAS
 
 
 def test_dasc_plan_matches_oracle(L, orc):
@@ -500,6 +539,30 @@ def test_binding_checks_checkpoint_buffer_sizes():
         hla.dasc_restore(**dict(rs, S_dst=S + 1))
     with pytest.raises(ValueError, match="GPU"):
         hla.dasc_restore(**rs)
+    # restore fused with the replay: shapes follow the private state [L, S, H, dk, dv]
+    z = torch.zeros
+    H, dk, N, K = 2, 64, 3, 4
+    pk64 = z(S, 4, dk * dk)
+    st = z(L, S, H, dk, dk)
+    rr = dict(packed=pk64, unit_pos=z(L, H, dtype=i32), src_slot=ids, dst_slot=ids,
+              active_out=st, q=z(L, N, K, H, dk), k=z(L, N, K, H, dk), v=z(L, N, K, H, dk),
+              alpha=z(L, N, K, H), beta=z(L, N, K, H), n_accept=z(N, dtype=i32), decay_kind=0)
+    with pytest.raises(ValueError, match="unit_pos"):
+        hla.dasc_restore_replay(**dict(rr, unit_pos=z(L * H + 1, dtype=i32)))
+    with pytest.raises(ValueError, match="packed"):
+        hla.dasc_restore_replay(**dict(rr, packed=z(S, 4, dk * dk - 1)))
+    with pytest.raises(ValueError, match="alpha"):
+        hla.dasc_restore_replay(**dict(rr, decay_kind=1))
+    with pytest.raises(ValueError, match="k"):
+        hla.dasc_restore_replay(**dict(rr, k=z(L, N, K + 1, H, dk)))
+    with pytest.raises(ValueError, match="n_accept"):
+        hla.dasc_restore_replay(**dict(rr, n_accept=z(N + 1, dtype=i32)))
+    with pytest.raises(ValueError, match="out"):
+        hla.dasc_restore_replay(**rr, out=z(L, N, K, H, dk + 1))
+    with pytest.raises(TypeError, match="q"):
+        hla.dasc_restore_replay(**dict(rr, q=z(L, N, K, H, dk, dtype=torch.float64)))
+    with pytest.raises(ValueError, match="GPU"):
+        hla.dasc_restore_replay(**rr)
     # INT8 checkpoints: codes and scales sized by rows, the FP32 state by the geometry
     rows, dv = 2, 4
     act32 = torch.zeros(L * S * n_units * rows * dv)

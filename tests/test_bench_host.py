@@ -63,6 +63,21 @@ def test_speculative_bytes_recounted():
                                                   + 4 * H * (tok_in + dv * 4))
 
 
+def test_fused_restore_replay_bytes_recounted():
+    n = np.array([0, 3, 8, 1], np.int32)
+    S, R, L, H, dk, dv = 4, 5, 3, 2, 64, 32
+    head = dk * dv * 4
+    tok_in = (2 * dk + dv) * 4 + 4 + 4
+    # retained checkpoint heads read once, every private head written once, each layer's
+    # accepted tokens' inputs read
+    want = S * R * head + L * S * H * head + L * 12 * H * tok_in
+    assert bench.restore_replay_bytes(n, S, R, L, H, dk, dv, 4) == want
+    # the separate calls move every live state (3 of 4 requests) once more per layer, in
+    # and out
+    two = (S * R * head + L * S * H * head) + L * bench.replay_bytes(n, H, dk, dv, 4, False)
+    assert two - want == L * 3 * H * 2 * head
+
+
 def test_traffic_only_for_the_profiled_source():
     assert bench.traffic_from_profile("gdn_step", ["bench.py"]) is None
     assert bench.traffic_from_profile("no_such_kernel", bench.STEP_SOURCES) is None

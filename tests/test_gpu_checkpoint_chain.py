@@ -81,8 +81,8 @@ def test_pack_restore_replay_chain_full_size():
         hla.replay_accepted(st, xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"],
                             dev(n_acc), 0, out=out)
         S64 = ref_rest[l].view(np.float32).reshape(S_, H, dk, dv).astype(np.float64)
-        o_ref, scale = _oracle_replay(S64, f64_inputs({n: x[n] for n in NAMES}, cfg.in_dtype),
-                                      n_acc)
+        o_ref, scale = oracle_par.replay_terms(
+            S64, f64_inputs({n: x[n] for n in NAMES}, cfg.in_dtype), n_acc, per_channel=False)
         got = host(st)
         err_s = oracle_par.rel_err_tiles(got, S64)
         idle = n_acc == 0
@@ -99,18 +99,3 @@ def test_pack_restore_replay_chain_full_size():
               f"requests replay {int(n_acc.sum())} tokens; state err {err_s:.2e}; readout err "
               f"{err_o:.2e} of its terms' size ({err_plain:.2e} of its own size)")
         assert err_s <= TOL and err_o <= TOL
-
-
-def _oracle_replay(S64, x64, n_acc):
-    """The oracle's replay as n_b single steps per request (the oracle's replay is exactly
-    that), in place on S64.  Returns the readouts [B, K, H, dv] (NaN for t >= n_b) and,
-    for each (b, t, h), the size of the readout's terms, max_j sum_i |S_t[i][j]| |q_t,i|."""
-    B, K, H = x64["q"].shape[:3]
-    out = np.full((B, K, H, S64.shape[-1]), np.nan)
-    scale = np.zeros((B, K, H))
-    for t in range(K):
-        live = n_acc > t
-        xt = {n: np.ascontiguousarray(a[:, t]) for n, a in x64.items()}
-        out[:, t] = oracle_par.delta_step(S64, xt, per_channel=False, live=live)
-        scale[:, t] = oracle_par.readout_scale(S64, xt["q"], live)
-    return out, scale

@@ -1,0 +1,294 @@
+"""GPU parity of dasc_restore_replay: a checkpoint of whole-head units restored into
+private slots with each request's accepted drafts replayed on the way ([dasc] §4.2
+dasc-nr; [K3] "Speculative decoding without state snapshots").
+
+Every case is checked twice:
+
+* against the oracle: its restore of the same packed bits (retained heads copied,
+  omitted heads zero), then its replay of the first n_b drafts of each layer in float64
+  (state within 1e-5 of max|oracle| per head tile, each accepted readout within 1e-5
+  of the size of its terms, max_j sum_i |S_t[i][j] q_t,i|, per head and token);
+* bit for bit against the library's two-call chain, dasc_restore followed by
+  replay_accepted on each layer, which the fused kernel must reproduce exactly (same
+  per-token arithmetic, the state held in registers in between).
+
+Small cases span GDN / KDA decay, FP32 / BF16 / FP16 inputs and readouts, all four
+head shapes, K = 1, 5 and 16, accepted counts from 0 to K with clamping, slot maps that
+permute, leave destination slots alone and name bad slots, a plan entry past the
+checkpoint, a checkpoint that retains nothing, and no pairs.  The full-size case is the
+checkpoint workload: 4 layers x 512 requests x 32 GDN heads x 128 x 128 with 64 of 128
+layer-heads retained and K = 8 drafts, one accepted count per request for every layer."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle_par
+import synth
+from gpu_util import dev, dev_inputs, f64_inputs, host, need_gpu, torch
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+NAMES = ("q", "k", "v", "alpha", "beta")
+TORCH_DT = {"f32": "float32", "bf16": "bfloat16", "f16": "float16"}
+
+
+def _cfg(kind, dk, dv, in_dtype, K, H=4, L=3, S=7, seed=0):
+    base = synth.CONFIGS["dasc_gdn"]
+    return synth.shrink(base, H=H, dk=dk, dv=dv, in_dtype=in_dtype, K=K, L=L, slots=S,
+                        decay="vector" if kind == "kda" else "scalar",
+                        seed=base.seed + 11 * dk + 5 * dv + K + seed
+                        + (3 if kind == "kda" else 0), plan_seed=base.plan_seed + seed)
+
+
+def _checkpoint(cfg, mask):
+    """The oracle's pack of every slot's retained heads (uint8 [S, R, dk*dv*4]) and the
+    plan tables."""
+    hla = need_gpu()
+    offsets, unit_index, unit_pos, R = hla.dasc_plan(mask)
+    ub = cfg.dk * cfg.dv * 4
+    act = np.stack([synth.initial_state(cfg, S=cfg.slots, layer=l) for l in range(cfg.L)])
+    ids = np.arange(cfg.slots, dtype=np.int32)
+    packed = oracle.dasc_pack(act.view(np.uint8).reshape(cfg.L, cfg.slots, cfg.H, ub),
+                              offsets, unit_index, ids, ids, cfg.slots)
+    return packed, offsets, unit_index, unit_pos, R
+
+
+def _drafts(cfg, N):
+    """Each layer's draft projections for N requests, stacked [L, N, K, H, ...]."""
+    xs = [synth.replay_inputs(cfg, l, B=N) for l in range(cfg.L)]
+    return {n: np.stack([x[n] for x in xs]) for n in NAMES}
+
+
+def _fused(hla, cfg, packed_d, unit_pos, src, dst, S_dst, xd, n_acc, out_dtype, init):
+    L, H = cfg.L, cfg.H
+    st = torch.full((L, S_dst, H, cfg.dk, cfg.dv), init, device="cuda")
+    out = torch.full((L, len(src), cfg.K, H, cfg.dv), 5.0, device="cuda",
+                     dtype=getattr(torch, TORCH_DT[out_dtype]))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pos = dev(np.ascontiguousarray(unit_pos, np.int32).reshape(-1))
+    hla.dasc_restore_replay(packed_d, pos, dev(src), dev(dst), st, xd["q"], xd["k"], xd["v"],
+                            xd["alpha"], xd["beta"], dev(n_acc),
+                            1 if cfg.decay == "vector" else 0, out=out, err_flag=err)
+    return st, out, int(err.item())
+
+
+def _chain(hla, cfg, packed_d, unit_pos, src, dst, S_dst, xd, n_acc, out_dtype, init):
+    """dasc_restore, then replay_accepted layer by layer into the restored slots."""
+    L, H = cfg.L, cfg.H
+    ub = cfg.dk * cfg.dv * 4
+    st = torch.full((L, S_dst, H, cfg.dk, cfg.dv), init, device="cuda")
+    out = torch.full((L, len(src), cfg.K, H, cfg.dv), 5.0, device="cuda",
+                     dtype=getattr(torch, TORCH_DT[out_dtype]))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    S_ck, R = packed_d.shape[:2]
+    src_d, dst_d, n_d = dev(src), dev(dst), dev(n_acc)
+    pos = dev(np.ascontiguousarray(unit_pos, np.int32).reshape(-1))
+    hla.dasc_restore(packed_d, S_ck, R, pos, L, H, ub, src_d, dst_d, st, S_dst * H * ub, S_dst,
+                     err_flag=err)
+    for l in range(L):
+        hla.replay_accepted(st[l], xd["q"][l], xd["k"][l], xd["v"][l], xd["alpha"][l],
+                            xd["beta"][l], n_d, 1 if cfg.decay == "vector" else 0, out=out[l],
+                            slot=dst_d, err_flag=err)
+    return st, out, int(err.item())
+
+
+def _oracle(cfg, packed, offsets, unit_index, src, dst, S_dst, x64, n_acc, init,
+            zero_heads=()):
+    """The oracle's restore into a state filled with `init` (the heads (l, h) listed in
+    zero_heads then zero-filled in the restored slots), then its replay per layer.
+    Returns the state [L, S_dst, H, dk, dv] (float64), readouts [L, N, K, H, dv] and the
+    readouts' term sizes [L, N, K, H]."""
+    L, H, dk, dv = cfg.L, cfg.H, cfg.dk, cfg.dv
+    rest = np.full((L, S_dst, H, dk, dv), init, np.float32)
+    oracle.dasc_restore(packed, offsets, unit_index, L, H, src, dst,
+                        rest.view(np.uint8).reshape(L, S_dst, H, dk * dv * 4))
+    for l, h in zero_heads:
+        rest[l, dst, h] = 0.0
+    S64 = rest.astype(np.float64)
+    outs, scales = [], []
+    for l in range(L):
+        Sl = np.ascontiguousarray(S64[l][dst])
+        o, sc = oracle_par.replay_terms(Sl, {n: x64[n][l] for n in NAMES}, n_acc,
+                                        per_channel=(cfg.decay == "vector"))
+        S64[l][dst] = Sl
+        outs.append(o)
+        scales.append(sc)
+    return S64, np.stack(outs), np.stack(scales)
+
+
+def _check_vs_oracle(st, out, ref_st, ref_out, scale, n_acc, K):
+    got = host(st)
+    assert oracle_par.rel_err_tiles(got.reshape(-1, *got.shape[-2:]),
+                                    ref_st.reshape(-1, *ref_st.shape[-2:])) <= TOL
+    o = host(out)
+    rows = np.arange(K)[None, :] < np.clip(n_acc, 0, K)[:, None]       # [N, K]
+    rows = np.broadcast_to(rows[None], o.shape[:3])
+    assert (o[~rows] == 5.0).all()                                      # rows t >= n_b
+    err = np.where(rows[..., None, None], np.abs(o - ref_out), 0.0).max(axis=-1)
+    return float((err / np.maximum(scale, 1e-30)).max())
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("in_dtype,out_dtype", [("f32", "f32"), ("bf16", "f32"),
+                                                ("f16", "f16"), ("bf16", "bf16")])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (128, 64), (64, 128)])
+def test_restore_replay_matches_oracle_and_chain(kind, in_dtype, out_dtype, dk, dv):
+    hla = need_gpu()
+    cfg = _cfg(kind, dk, dv, in_dtype, K=5)
+    mask = synth.dasc_masks(cfg)
+    packed, offsets, unit_index, unit_pos, R = _checkpoint(cfg, mask)
+    assert 0 < R < cfg.L * cfg.H
+    src = np.array([3, 0, 6, 2, 5], np.int32)                # checkpoint slots, permuted
+    dst = np.array([1, 7, 4, 0, 2], np.int32)                # slots 3, 5, 6 are left alone
+    n_acc = np.array([0, 5, 2, 7, -1], np.int32)             # 7 and -1 clamp to 5 and 0
+    S_dst = 8
+    x = _drafts(cfg, len(src))
+    xd = dev_inputs(x, in_dtype)
+    packed_d = dev(packed.view(np.float32).reshape(cfg.slots, R, dk * dv))
+    st, out, err = _fused(hla, cfg, packed_d, unit_pos, src, dst, S_dst, xd, n_acc,
+                          out_dtype, 7.0)
+    assert err == hla.DEVERR_ACCEPT
+    st2, out2, err2 = _chain(hla, cfg, packed_d, unit_pos, src, dst, S_dst, xd, n_acc,
+                             out_dtype, 7.0)
+    assert err2 == hla.DEVERR_ACCEPT
+    assert torch.equal(st, st2) and torch.equal(out, out2)
+    ref_st, ref_out, scale = _oracle(cfg, packed, offsets, unit_index, src, dst, S_dst,
+                                     f64_inputs(x, in_dtype), n_acc, 7.0)
+    err_o = _check_vs_oracle(st, out, ref_st, ref_out, scale, n_acc, cfg.K)
+    tol_o = TOL if out_dtype == "f32" else (2.0 ** -8 if out_dtype == "bf16" else 2.0 ** -10)
+    assert err_o <= tol_o
+    # requests with nothing accepted hold the restored bits exactly; slots no pair names
+    # keep what they held
+    got = host(st)
+    assert np.array_equal(got[:, [1, 2]], ref_st[:, [1, 2]].astype(np.float32))
+    assert (got[:, [3, 5, 6]] == 7.0).all()
+
+
+@pytest.mark.parametrize("K", [1, 16])
+def test_restore_replay_draft_counts_at_the_limits(K):
+    hla = need_gpu()
+    cfg = _cfg("gdn", 128, 128, "bf16", K=K, L=2, S=4, seed=1)
+    packed, offsets, unit_index, unit_pos, R = _checkpoint(cfg, synth.dasc_masks(cfg))
+    src = np.array([0, 1, 2, 3], np.int32)
+    dst = np.array([3, 2, 1, 0], np.int32)
+    n_acc = np.array([K, 0, K // 2, 1], np.int32)
+    x = _drafts(cfg, 4)
+    xd = dev_inputs(x, "bf16")
+    packed_d = dev(packed.view(np.float32).reshape(cfg.slots, R, -1))
+    st, out, err = _fused(hla, cfg, packed_d, unit_pos, src, dst, 4, xd, n_acc, "f32", 0.0)
+    st2, out2, _ = _chain(hla, cfg, packed_d, unit_pos, src, dst, 4, xd, n_acc, "f32", 0.0)
+    assert err == 0 and torch.equal(st, st2) and torch.equal(out, out2)
+    ref_st, ref_out, scale = _oracle(cfg, packed, offsets, unit_index, src, dst, 4,
+                                     f64_inputs(x, "bf16"), n_acc, 0.0)
+    assert _check_vs_oracle(st, out, ref_st, ref_out, scale, n_acc, K) <= TOL
+
+
+def test_restore_replay_device_errors_and_degenerate_plans():
+    """Bad slots are skipped, a plan entry past the checkpoint starts its head from zero;
+    both are reported.  A checkpoint that retains nothing starts every head from zero;
+    no pairs touches nothing."""
+    hla = need_gpu()
+    cfg = _cfg("kda", 64, 64, "f32", K=4, L=2, S=5, seed=2)
+    mask = synth.dasc_masks(cfg)
+    packed, offsets, unit_index, unit_pos, R = _checkpoint(cfg, mask)
+    packed_d = dev(packed.view(np.float32).reshape(cfg.slots, R, -1))
+    src = np.array([0, 5, 2, -1, 4], np.int32)   # 5 and -1: not checkpoint slots
+    dst = np.array([0, 1, 6, 3, 2], np.int32)    # 6: not a private slot
+    n_acc = np.array([4, 2, 3, 1, 2], np.int32)
+    x = _drafts(cfg, len(src))
+    xd = dev_inputs(x, "f32")
+    pos = unit_pos.copy()
+    h_bad = int(np.flatnonzero(pos[1] >= 0)[0])
+    pos[1, h_bad] = R + 3                        # a bad plan entry: that head starts at zero
+    st, out, err = _fused(hla, cfg, packed_d, pos, src, dst, 6, xd, n_acc, "f32", 7.0)
+    assert err == hla.DEVERR_SLOT | hla.DEVERR_PLAN
+    good = np.array([0, 4])
+    xg = {n: a[:, good] for n, a in x.items()}
+    st2, out2, err2 = _chain(hla, cfg, packed_d, pos, src[good], dst[good], 6,
+                             dev_inputs(xg, "f32"), n_acc[good], "f32", 7.0)
+    assert err2 == hla.DEVERR_PLAN
+    assert torch.equal(st, st2) and torch.equal(out[:, good], out2)
+    assert (host(out)[:, [1, 2, 3]] == 5.0).all()         # skipped pairs: no readout
+    assert (host(st)[:, [1, 3, 4, 5]] == 7.0).all()       # and no state written
+    # the oracle's restore with the bad entry's head zero-filled, as an omitted head
+    ref_st, ref_out, scale = _oracle(cfg, packed, offsets, unit_index, src[good], dst[good], 6,
+                                     f64_inputs(xg, "f32"), n_acc[good], 7.0,
+                                     zero_heads=[(1, h_bad)])
+    assert _check_vs_oracle(st2, out2, ref_st, ref_out, scale, n_acc[good], cfg.K) <= TOL
+
+    # nothing retained: every head starts from zero
+    none = np.zeros_like(mask)
+    _, _, pos0, R0 = hla.dasc_plan(none)
+    assert R0 == 0 and (pos0 < 0).all()
+    empty = torch.empty((cfg.slots, 0, cfg.dk * cfg.dv), device="cuda")
+    src0, dst0 = np.array([1, 0], np.int32), np.array([0, 1], np.int32)
+    x0 = {n: a[:, :2] for n, a in x.items()}
+    st0, out0, err0 = _fused(hla, cfg, empty, pos0, src0, dst0, 2, dev_inputs(x0, "f32"),
+                             n_acc[:2], "f32", 7.0)
+    assert err0 == 0
+    for l in range(cfg.L):
+        Z = np.zeros((2, cfg.H, cfg.dk, cfg.dv))
+        o, sc = oracle_par.replay_terms(Z, {n: f64_inputs(x0, "f32")[n][l] for n in NAMES},
+                                        n_acc[:2], per_channel=True)
+        assert oracle_par.rel_err_tiles(host(st0)[l], Z) <= TOL
+        e = np.nan_to_num(np.abs(host(out0)[l] - o)).max(axis=-1) / np.maximum(sc, 1e-30)
+        assert float(e.max()) <= TOL
+
+    # no pairs: nothing is launched and nothing changes
+    stn, outn, errn = _fused(hla, cfg, packed_d, unit_pos, np.zeros(0, np.int32),
+                             np.zeros(0, np.int32), 2,
+                             {n: t[:, :0].contiguous() for n, t in xd.items()},
+                             np.zeros(0, np.int32), "f32", 7.0)
+    assert errn == 0 and (host(stn) == 7.0).all()
+
+
+def test_restore_replay_full_size():
+    """The checkpoint workload at full size: bitwise against the two-call chain over the
+    whole 4 GiB of private state and every readout, and against the oracle on sampled
+    requests (every layer and head of each)."""
+    hla = need_gpu()
+    cfg = synth.CONFIGS["dasc_gdn"]
+    L, S_, H, dk, dv, K = cfg.L, cfg.slots, cfg.H, cfg.dk, cfg.dv, cfg.K
+    mask = synth.dasc_masks(cfg)
+    offsets, unit_index, unit_pos, R = hla.dasc_plan(mask)
+    assert R == 64
+    # the checkpoint's heads are drawn as the active state's are
+    packed = synth.initial_state(synth.shrink(cfg, H=R), S=S_).reshape(S_, R, dk * dv)
+    g = synth.rng(cfg.seed, 99)
+    src = g.permutation(S_).astype(np.int32)
+    dst = g.permutation(S_).astype(np.int32)
+    n_acc = synth.replay_inputs(cfg, 0)["n_accept"]
+    x = _drafts(cfg, S_)
+    xd = dev_inputs(x, cfg.in_dtype)
+    packed_d = dev(packed)
+    print(f"full size: {L} layers x {S_} requests x {H} heads, {R} heads retained, "
+          f"{int(n_acc.sum())} accepted tokens per layer", flush=True)
+    st, out, err = _fused(hla, cfg, packed_d, unit_pos, src, dst, S_, xd, n_acc, "f32", 7.0)
+    assert err == 0
+    st2, out2, err2 = _chain(hla, cfg, packed_d, unit_pos, src, dst, S_, xd, n_acc, "f32", 7.0)
+    assert err2 == 0
+    assert torch.equal(st, st2)
+    del st2
+    assert torch.equal(out, out2)
+    del out2
+    # the oracle on sampled requests: their heads start from the packed bits (or zero)
+    pick = np.sort(g.choice(S_, size=24, replace=False))
+    n_p = n_acc[pick]
+    x64 = f64_inputs({n: a[:, pick] for n, a in x.items()}, cfg.in_dtype)
+    st_h = st[:, torch.from_numpy(dst[pick]).long().cuda()].cpu().numpy()
+    out_h = out[:, torch.from_numpy(pick).long().cuda()].cpu().numpy()
+    for l in range(L):
+        S64 = np.zeros((len(pick), H, dk, dv))
+        for h in range(H):
+            if unit_pos[l, h] >= 0:
+                S64[:, h] = packed[src[pick], unit_pos[l, h]].reshape(-1, dk, dv)
+        o, sc = oracle_par.replay_terms(S64, {n: x64[n][l] for n in NAMES}, n_p,
+                                        per_channel=False)
+        err_s = oracle_par.rel_err_tiles(st_h[l], S64)
+        rows = np.arange(K)[None, :] < n_p[:, None]
+        e = np.where(rows[:, :, None, None], np.abs(out_h[l] - o), 0.0).max(axis=-1)
+        err_o = float((e / np.maximum(sc, 1e-30)).max())
+        print(f"layer {l}: sampled requests' state err {err_s:.2e}, readout err {err_o:.2e} "
+              f"of its terms' size", flush=True)
+        assert err_s <= TOL and err_o <= TOL
+        assert (out_h[l][~rows] == 5.0).all()
