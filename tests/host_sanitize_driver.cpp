@@ -165,6 +165,27 @@ static void checks()
                                                   fake(3), R, (const int32_t *)fake(4),
                                                   (const int32_t *)fake(5), 1, fake(6),
                                                   fake(7), S);
+    // the fused restore + replay: both halves' sizes at once
+    for (int S : big)
+        for (int L : {1, 4, 1 << 16, INT_MAX})
+            for (int N : {0, 1, 512, INT_MAX})
+                for (int H : {1, 32, INT_MAX})
+                    for (int R : {0, 64, INT_MAX})
+                        for (int64_t st : strides) {
+                            RestoreReplayArgs rr{};
+                            rr.packed = (const float *)fake(1), rr.S_ckpt = S, rr.R_total = R;
+                            rr.unit_pos = (const int32_t *)fake(2), rr.L = L;
+                            rr.src_slot = (const int32_t *)fake(3);
+                            rr.dst_slot = (const int32_t *)fake(4), rr.N = N;
+                            rr.active_out = (float *)fake(5), rr.layer_stride_bytes = st;
+                            rr.S_dst = S, rr.H = H, rr.dk = 128, rr.dv = 128, rr.K = 16;
+                            rr.q = fake(6), rr.k = fake(7), rr.v = fake(8);
+                            rr.in_dtype = rr.out_dtype = HLA_F32;
+                            rr.alpha = (const float *)fake(9), rr.decay = HLA_DECAY_VECTOR;
+                            rr.beta = (const float *)fake(10);
+                            rr.n_accept = (const int32_t *)fake(11), rr.out = (void *)fake(12);
+                            (void)check_restore_replay(rr);
+                        }
     for (int s = -3; s < 16; ++s) EXPECT(hla_status_str(s) != nullptr);
 }
 

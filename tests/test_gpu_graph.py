@@ -134,3 +134,28 @@ def test_dasc_int8_graph_replays():
                               stride, S_)
 
     _check_replays(launch, bufs["e"], bufs["g"])
+
+
+def test_restore_replay_graph_replays():
+    hla = need_gpu()
+    cfg = synth.shrink(synth.CONFIGS["dasc_gdn"], H=3, dk=64, dv=64, K=4, L=2, slots=4)
+    mask = synth.dasc_masks(cfg)
+    _, _, unit_pos, R = hla.dasc_plan(mask)
+    g = np.random.default_rng(7)
+    packed = dev((g.standard_normal((cfg.slots, R, cfg.dk * cfg.dv)) * 0.05).astype(np.float32))
+    pos = dev(unit_pos.reshape(-1))
+    src = dev(np.array([2, 0, 3], np.int32))
+    dst = dev(np.array([1, 3, 0], np.int32))
+    xs = [synth.replay_inputs(cfg, l, B=3) for l in range(cfg.L)]
+    x = {k: dev(np.stack([xl[k] for xl in xs])) for k in ("q", "k", "v", "alpha", "beta")}
+    n_acc = dev(np.array([4, 0, 2], np.int32))
+    bufs = {}
+    for side in ("e", "g"):
+        bufs[side] = [torch.full((cfg.L, cfg.slots, cfg.H, cfg.dk, cfg.dv), 7.0, device="cuda"),
+                      torch.zeros((cfg.L, 3, cfg.K, cfg.H, cfg.dv), device="cuda")]
+
+    def launch(state, i):
+        hla.dasc_restore_replay(packed, pos, src, dst, state[0], x["q"], x["k"], x["v"],
+                                x["alpha"], x["beta"], n_acc, 0, out=state[1])
+
+    _check_replays(launch, bufs["e"], bufs["g"])
