@@ -259,6 +259,12 @@ k_delta_step(float *__restrict__ state, int n_slots, const int32_t *__restrict__
 // most for a head that starts from zero (no state read to hide the token loads behind).
 // Token t takes WG consecutive 16-byte words: q, k, v and (per-channel decay) alpha, as
 // stored; the scalar decay and beta sit in one float2 per token after the K tokens.
+// The staging costs a workgroup barrier, which ties the head's waves together (each
+// otherwise streams its column slice on its own): with a state read to hide the token
+// loads behind, it pays from about 7 accepted tokens on (measured over 1-8), so fewer
+// are loaded token by token as in the step.
+constexpr int kStageMinTokens = 7;
+
 template <int DK, int DV, typename TIn, bool VEC>
 struct TokenLds {
     static constexpr int QB = DK * (int)sizeof(TIn) / 16;  // words of q (and of k)
@@ -338,9 +344,9 @@ __device__ __forceinline__ void token_from_lds(const uint8_t *lds, int t, int K,
 // Several tokens per (request, head) with the tile held in registers
 // throughout ("Serving recurrent attention", part "Speculative decoding
 // without state snapshots"):
-//   MODE_REPLAY  the first n_b of K cached draft projections (their inputs
-//                staged in LDS); the state is read once and written once, and
-//                not touched when n_b = 0;
+//   MODE_REPLAY  the first n_b of K cached draft projections (inputs staged
+//                in LDS from kStageMinTokens tokens on); the state is read once
+//                and written once, and not touched when n_b = 0;
 //   MODE_BONUS   the same, then the target model's bonus token ([B, H, .]
 //                inputs, applied also when n_b = 0), then one write.
 template <int DK, int DV, typename TIn, typename TOut, bool VEC, int MODE>
@@ -379,14 +385,19 @@ k_tokens(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
     float x[RPL][4];
     tile_load<RPL>(head, off, DV, x);
     const size_t tok0 = (size_t)b * K * H + h;  // token t of (b, h) is tok0 + t * H
-    if (n > 0) {
+    const bool staged = n >= kStageMinTokens;  // uniform over the workgroup
+    if (staged) {
         stage_tokens<DK, DV, TIn, VEC>(tok_lds, n, tok0, H, q, k, v, alpha, beta, K);
         __builtin_amdgcn_s_waitcnt(0);  // the copies into LDS (and the tile) have landed
         __syncthreads();
     }
     for (int t = 0; t < n; ++t) {
         TokenRaw<DK, TIn, VEC> raw;
-        token_from_lds<DK, DV, TIn, VEC>(tok_lds, t, K, row0, col0, raw);
+        if (staged)
+            token_from_lds<DK, DV, TIn, VEC>(tok_lds, t, K, row0, col0, raw);
+        else
+            token_load<DK, DV, TIn, VEC>(q, k, v, alpha, beta, tok0 + (size_t)t * H, row0, col0,
+                                         raw);
         float vv[4];
         token_v<TIn>(raw.v2, raw.v4, vv);
         float o[4];
@@ -411,7 +422,9 @@ k_tokens(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
 // "Speculative decoding without state snapshots").  Workgroup (l, n, h): the head starts
 // as its packed copy from checkpoint slot src_slot[n] (or zero when head h of layer l is
 // not retained), takes the first n_b draft tokens of layer l in registers (their inputs
-// staged in LDS), and is written once into private slot dst_slot[n].  Same lane layout
+// staged in LDS: half the heads start from zero, with no state read to hide token loads
+// behind, and measured over the whole workload staging every head's tokens was fastest),
+// and is written once into private slot dst_slot[n].  Same lane layout
 // and per-token function as the step, so the result is bitwise that of dasc_restore
 // followed by replay_accepted.
 template <int DK, int DV, typename TIn, typename TOut, bool VEC>
@@ -461,7 +474,7 @@ k_restore_tokens(const float *__restrict__ packed, int S_ckpt, int R_total,
             for (int c = 0; c < 4; ++c) x[m][c] = 0.0f;
     }
     const size_t tok0 = (size_t)ln * K * H + h;  // token t of (l, n, h) is tok0 + t * H
-    if (nb > 0) {
+    if (nb > 0) {  // uniform over the workgroup
         stage_tokens<DK, DV, TIn, VEC>(tok_lds, nb, tok0, H, q, k, v, alpha, beta, K);
         __builtin_amdgcn_s_waitcnt(0);  // the copies into LDS (and the tile) have landed
         __syncthreads();
