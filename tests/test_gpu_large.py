@@ -104,3 +104,49 @@ def test_damp_step_beyond_4gib():
     w = _state_bars(g, (hi_s, lo_s, sc_s), perm, K_hi, dk)
     w["out"] = rel_err_tiles(host(o), o_ref, 1)
     _assert_bars(w)
+
+
+def test_restore_replay_beyond_4gib():
+    """The fused restore + replay into a private state of 2 layers x 2,080 slots (8.7 GB):
+    pairs land on both sides of the 4 GiB boundary of each layer, and the second layer
+    starts past it."""
+    import oracle_par
+
+    hla = need_gpu()
+    base = synth.CONFIGS["dasc_gdn"]
+    H, dk, dv = base.H, base.dk, base.dv
+    slot_bytes = H * dk * dv * 4
+    n_slots = GIB4 // slot_bytes + 32
+    cfg = synth.shrink(base, L=2, slots=3, seed=base.seed + 41)
+    mask = synth.dasc_masks(cfg)
+    _, _, unit_pos, R = hla.dasc_plan(mask)
+    packed = synth.initial_state(synth.shrink(cfg, H=R), S=cfg.slots).reshape(cfg.slots, R, -1)
+    dst = _slots_across(n_slots, slot_bytes)
+    N = len(dst)
+    src = (np.arange(N) % cfg.slots).astype(np.int32)
+    xs = [synth.replay_inputs(cfg, l, B=N) for l in range(cfg.L)]
+    x = {n: np.stack([xl[n] for xl in xs]) for n in NAMES}
+    n_acc = xs[0]["n_accept"]
+    st = torch.full((cfg.L, n_slots, H, dk, dv), 7.0, device="cuda")
+    out = hla.dasc_restore_replay(dev(packed), dev(unit_pos.reshape(-1)), dev(src), dev(dst), st,
+                                  *(dev(x[n]) for n in NAMES), dev(n_acc), 0,
+                                  out=torch.full((cfg.L, N, cfg.K, H, dv), 5.0, device="cuda"))
+    got = host(st[:, torch.from_numpy(dst).long().cuda()])
+    o = host(out)
+    x64 = {n: a.astype(np.float64) for n, a in x.items()}
+    for l in range(cfg.L):
+        S64 = np.zeros((N, H, dk, dv))
+        for h in range(H):
+            if unit_pos[l, h] >= 0:
+                S64[:, h] = packed[src, unit_pos[l, h]].reshape(N, dk, dv)
+        o_ref, scale = oracle_par.replay_terms(S64, {n: x64[n][l] for n in NAMES}, n_acc,
+                                               per_channel=False)
+        assert rel_err_tiles(got[l], S64) <= TOL
+        rows = np.arange(cfg.K)[None, :] < n_acc[:, None]
+        e = np.where(rows[:, :, None, None], np.abs(o[l] - o_ref), 0.0).max(axis=-1)
+        assert float((e / np.maximum(scale, 1e-30)).max()) <= TOL
+        assert (o[l][~rows] == 5.0).all()
+    # slots no pair names keep their contents, on both sides of the boundary
+    others = [s for s in range(int(dst[1]) - 2, int(dst[-1]) + 3)
+              if s not in set(dst.tolist()) and 0 <= s < n_slots]
+    assert (host(st[:, others]) == 7.0).all()
