@@ -2,7 +2,9 @@
 count, units per layer, unit size, keep probability (empty and full masks included),
 checkpoint / private slot maps.  FP32 pack / restore bit-exact; INT8 pack: scales
 bit-exact, codes off by at most 1 on at most 0.1% of values; INT8 restore of the oracle's
-checkpoint bit-exact.  Slots no pair names keep their sentinel bytes."""
+checkpoint bit-exact; the fused restore + replay against the oracle's restore then replay
+and bit for bit against the library's two calls.  Slots no pair names keep their sentinel
+bytes."""
 import numpy as np
 import pytest
 
@@ -165,3 +167,85 @@ def test_refresh_local_device_errors():
     ref2 = ref.copy()
     ref2[1, 2, 0] = active[1, 2, 0]            # not copied
     assert np.array_equal(host(act2).reshape(active.shape), ref2)
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_restore_replay(i):
+    """The fused restore + replay on random geometry (layers, heads, head shape, draft
+    count, input and readout types, decay kind, masks from empty to full, slot maps,
+    accepted counts with out-of-range values): against the oracle's restore then replay,
+    and bit for bit against the library's restore followed by replay_accepted per layer."""
+    import oracle_par
+
+    hla = need_gpu()
+    g = np.random.default_rng(7300 + i)
+    L = int(g.integers(1, 5))
+    H = int(g.integers(1, 7))
+    dk, dv = (int(g.choice([64, 128])) for _ in range(2))
+    K = int(g.integers(1, 17))
+    vec = bool(g.integers(0, 2))
+    in_dt = str(g.choice(["f32", "bf16", "f16"]))
+    out_dt = str(g.choice(["f32", "bf16", "f16"]))
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+    mask = (g.random((L, H)) < _keep(g)).astype(np.uint8)
+    _, _, unit_pos, R = hla.dasc_plan(mask)
+    S_ckpt, S_dst = int(g.integers(1, 6)), int(g.integers(1, 8))
+    src, dst = _maps(g, S_ckpt, S_dst)
+    N = len(src)
+    packed = (g.standard_normal((S_ckpt, R, dk * dv)) * 0.05).astype(np.float32)
+    # inputs: q, k unit vectors, stored in the input type; values the kernel reads exactly
+    qk = g.standard_normal((2, L, N, K, H, dk))
+    qk /= np.linalg.norm(qk, axis=-1, keepdims=True)
+    v = g.standard_normal((L, N, K, H, dv)) * 0.5
+    x_t = {n: torch.from_numpy(a).to(tdt[in_dt])
+           for n, a in (("q", qk[0]), ("k", qk[1]), ("v", v))}
+    alpha = g.uniform(0.9, 0.9999, size=(L, N, K, H) + ((dk,) if vec else ())).astype(np.float32)
+    beta = g.uniform(0.05, 0.95, size=(L, N, K, H)).astype(np.float32)
+    n_acc = g.integers(-2, K + 3, size=N).astype(np.int32)
+    n_eff = np.clip(n_acc, 0, K)
+    xd = {n: t.cuda() for n, t in x_t.items()}
+    xd.update(alpha=dev(alpha), beta=dev(beta))
+    pk = dev(packed)
+    pos = dev(unit_pos.reshape(-1))
+
+    def fused():
+        st = torch.full((L, S_dst, H, dk, dv), 3.0, device="cuda")
+        out = torch.full((L, N, K, H, dv), 5.0, device="cuda", dtype=tdt[out_dt])
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        hla.dasc_restore_replay(pk, pos, dev(src), dev(dst), st, xd["q"], xd["k"], xd["v"],
+                                xd["alpha"], xd["beta"], dev(n_acc), int(vec), out=out,
+                                err_flag=err)
+        return st, out, int(err.item())
+
+    st, out, err = fused()
+    assert err == (hla.DEVERR_ACCEPT if (n_acc != n_eff).any() else 0)
+    # the two-call chain
+    st2 = torch.full((L, S_dst, H, dk, dv), 3.0, device="cuda")
+    out2 = torch.full((L, N, K, H, dv), 5.0, device="cuda", dtype=tdt[out_dt])
+    ub = dk * dv * 4
+    hla.dasc_restore(pk if R else dev(np.zeros(4, np.float32)), S_ckpt, R, pos, L, H, ub,
+                     dev(src), dev(dst), st2, S_dst * H * ub, S_dst)
+    for l in range(L):
+        hla.replay_accepted(st2[l], xd["q"][l], xd["k"][l], xd["v"][l], xd["alpha"][l],
+                            xd["beta"][l], dev(n_acc), int(vec), out=out2[l], slot=dev(dst))
+    assert torch.equal(st, st2) and torch.equal(out, out2)
+    # the oracle
+    got, o = host(st), host(out)
+    x64 = {"q": x_t["q"].double().numpy(), "k": x_t["k"].double().numpy(),
+           "v": x_t["v"].double().numpy(), "alpha": alpha.astype(np.float64),
+           "beta": beta.astype(np.float64)}
+    tol_o = 1e-5 if out_dt == "f32" else (2.0 ** -8 if out_dt == "bf16" else 2.0 ** -10)
+    for l in range(L):
+        S64 = np.zeros((N, H, dk, dv))
+        for h in range(H):
+            if unit_pos[l, h] >= 0:
+                S64[:, h] = packed[src, unit_pos[l, h]].reshape(N, dk, dv)
+        o_ref, scale = oracle_par.replay_terms(S64, {n: x64[n][l] for n in x64}, n_acc,
+                                               per_channel=vec)
+        assert oracle_par.rel_err_tiles(got[l][dst], S64) <= 1e-5
+        rows = np.arange(K)[None, :] < n_eff[:, None]
+        e = np.where(rows[:, :, None, None], np.abs(o[l] - o_ref), 0.0).max(axis=-1)
+        assert float((e / np.maximum(scale, 1e-30)).max()) <= tol_o
+        assert (o[l][~rows] == 5.0).all()
+    others = sorted(set(range(S_dst)) - set(dst.tolist()))
+    assert (got[:, others] == 3.0).all()
