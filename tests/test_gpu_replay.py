@@ -22,11 +22,14 @@ def _cfg(kind, dk, dv, in_dtype, B, K, H=3):
 @pytest.mark.parametrize("kind", ["gdn", "kda"])
 @pytest.mark.parametrize("in_dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (128, 64)])
-def test_replay_matches_oracle_with_clamping(kind, in_dtype, dk, dv):
+@pytest.mark.parametrize("K", [4, 12])
+def test_replay_matches_oracle_with_clamping(kind, in_dtype, dk, dv, K):
+    """K = 12 takes requests with 7 or more accepted tokens through the path that stages
+    their inputs in LDS; K = 4 through the token-by-token loads."""
     hla = need_gpu()
-    cfg = _cfg(kind, dk, dv, in_dtype, B=6, K=4)
+    cfg = _cfg(kind, dk, dv, in_dtype, B=6, K=K)
     x = synth.replay_inputs(cfg, 0)
-    n_acc = np.array([0, 1, 4, 2, 9, -3], np.int32)  # 9 and -3 are clamped to 4 and 0
+    n_acc = np.array([0, 1, K, K // 2 + 1, K + 5, -3], np.int32)  # K + 5, -3 clamp to K, 0
     S0 = synth.initial_state(cfg)
     S64 = S0.astype(np.float64)
     st = dev(S0)

@@ -164,22 +164,25 @@ def test_restore_replay_matches_oracle_and_chain(kind, in_dtype, out_dtype, dk, 
     assert (got[:, [3, 5, 6]] == 7.0).all()
 
 
+@pytest.mark.parametrize("kind,in_dtype", [("gdn", "bf16"), ("kda", "f32")])
 @pytest.mark.parametrize("K", [1, 16])
-def test_restore_replay_draft_counts_at_the_limits(K):
+def test_restore_replay_draft_counts_at_the_limits(K, kind, in_dtype):
+    """K = 16 with FP32 inputs and a per-channel decay stages the most bytes per token in
+    LDS (2 KiB per token at 128 x 128)."""
     hla = need_gpu()
-    cfg = _cfg("gdn", 128, 128, "bf16", K=K, L=2, S=4, seed=1)
+    cfg = _cfg(kind, 128, 128, in_dtype, K=K, L=2, S=4, seed=1)
     packed, offsets, unit_index, unit_pos, R = _checkpoint(cfg, synth.dasc_masks(cfg))
     src = np.array([0, 1, 2, 3], np.int32)
     dst = np.array([3, 2, 1, 0], np.int32)
     n_acc = np.array([K, 0, K // 2, 1], np.int32)
     x = _drafts(cfg, 4)
-    xd = dev_inputs(x, "bf16")
+    xd = dev_inputs(x, in_dtype)
     packed_d = dev(packed.view(np.float32).reshape(cfg.slots, R, -1))
     st, out, err = _fused(hla, cfg, packed_d, unit_pos, src, dst, 4, xd, n_acc, "f32", 0.0)
     st2, out2, _ = _chain(hla, cfg, packed_d, unit_pos, src, dst, 4, xd, n_acc, "f32", 0.0)
     assert err == 0 and torch.equal(st, st2) and torch.equal(out, out2)
     ref_st, ref_out, scale = _oracle(cfg, packed, offsets, unit_index, src, dst, 4,
-                                     f64_inputs(x, "bf16"), n_acc, 0.0)
+                                     f64_inputs(x, in_dtype), n_acc, 0.0)
     assert _check_vs_oracle(st, out, ref_st, ref_out, scale, n_acc, K) <= TOL
 
 
