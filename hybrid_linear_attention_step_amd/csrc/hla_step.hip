@@ -498,7 +498,8 @@ template <int DK, int DV, typename TIn, typename TOut, bool VEC, int MODE>
 static void launch_tokens(const StepArgs &a, int32_t *err, hipStream_t st)
 {
     const dim3 grid((unsigned)((size_t)a.B * a.H)), block(2 * DV);
-    const size_t lds = TokenLds<DK, DV, TIn, VEC>::bytes(a.K);
+    // no request can reach the staging threshold when K is below it: no LDS then
+    const size_t lds = a.K >= kStageMinTokens ? TokenLds<DK, DV, TIn, VEC>::bytes(a.K) : 0;
     hipLaunchKernelGGL((k_tokens<DK, DV, TIn, TOut, VEC, MODE>), grid, block, lds, st, a.state,
                        a.n_slots, a.slot, a.H, a.K, (const TIn *)a.q, (const TIn *)a.k,
                        (const TIn *)a.v, a.alpha, a.beta, a.n_accept, (TOut *)a.out,
