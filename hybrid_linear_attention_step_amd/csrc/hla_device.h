@@ -103,9 +103,6 @@ enum : int {
     DPP_ROW_HALF_MIRROR = 0x141 // lane i <- lane 7-i within each 8-lane half row
 };
 
-// An LDS address as the direct global-to-LDS load takes it.
-typedef __attribute__((address_space(3))) void lds_void_t;
-
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x)
 {

@@ -274,6 +274,9 @@ struct TokenLds {
     static size_t bytes(int K) { return (size_t)K * (WG * 16 + sizeof(float2)); }
 };
 
+// An LDS address as the direct global-to-LDS load takes it.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
 // Issue the staging copies of tokens [0, nb) of workgroup (ln, h); every wave of the
 // workgroup takes 64 words per pass.  The LDS address of a wave's copy is wave-uniform.
 template <int DK, int DV, typename TIn, bool VEC>
