@@ -33,8 +33,8 @@ SIGNATURES = {
     "dasc_plan": ([_P, _I, _I, _P, _P, _I, _P, _P], _I),
     "dasc_pack": ([_P, _L, _I, _I, _I, _L, _P, _P, _I, _P, _P, _I, _P, _I, _P, _P], _I),
     "dasc_restore": ([_P, _I, _I, _P, _I, _I, _L, _P, _P, _I, _P, _L, _I, _P, _P], _I),
-    "dasc_restore_replay": ([_P, _I, _I, _P, _I, _P, _P, _I, _P, _L, _I, _I, _I, _I, _I, _P,
-                             _P, _P, _I, _P, _I, _P, _P, _P, _I, _P, _P], _I),
+    "dasc_restore_replay": ([_P, _I, _I, _P, _I, _I, _P, _P, _I, _P, _L, _I, _I, _I, _I, _I,
+                             _P, _P, _P, _I, _P, _I, _P, _P, _P, _I, _P, _P], _I),
     "dasc_pack_int8": ([_P, _L, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P],
                        _I),
     "dasc_restore_int8": ([_P, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P, _I, _P, _L, _I, _P, _P],
@@ -528,22 +528,35 @@ def dasc_restore(packed, S_ckpt, R_total, unit_pos, L, n_units, unit_bytes, src_
 
 def dasc_restore_replay(packed, unit_pos, src_slot, dst_slot, active_out, q, k, v, alpha, beta,
                         n_accept, decay_kind, out=None, err_flag=None, stream=None):
-    """Restore a checkpoint of whole-head units into private slots and replay each request's
-    accepted drafts, layer by layer, in one pass.
+    """Restore a checkpoint into private slots and replay each request's accepted drafts,
+    layer by layer, in one pass.
 
-    packed [S_ckpt, R_total, dk * dv] fp32; unit_pos [L, H] or [L * H] int32 (dasc_plan of
-    the head mask); active_out [L, S_dst, H, dk, dv] fp32; q, k [L, N, K, H, dk], v
-    [L, N, K, H, dv]; alpha [L, N, K, H] (scalar decay) or [L, N, K, H, dk]; beta
-    [L, N, K, H]; n_accept [N] int32; out [L, N, K, H, dv] or None (no readout)."""
+    packed [S_ckpt, R_total, unit_rows * dv] (or [S_ckpt, R_total, unit_rows, dv]) fp32:
+    units of unit_rows key channels (dk: whole heads; 1: single channels); unit_pos
+    [L, H * dk / unit_rows] (or flat) int32 from dasc_plan of the unit mask; active_out
+    [L, S_dst, H, dk, dv] fp32; q, k [L, N, K, H, dk], v [L, N, K, H, dv]; alpha
+    [L, N, K, H] (scalar decay) or [L, N, K, H, dk]; beta [L, N, K, H]; n_accept [N]
+    int32; out [L, N, K, H, dv] or None (no readout)."""
     a = _Args("dasc_restore_replay")
     a.t(active_out, "active_out", _f32(), ndim=5)
     L, S_dst, H, dk, dv = active_out.shape
-    a.t(packed, "packed", _f32(), shape=(None, None, dk * dv))
+    a.t(packed, "packed", _f32())
+    if packed.dim() == 4 and packed.shape[3] == dv:
+        unit_rows = int(packed.shape[2])
+    elif packed.dim() == 3 and packed.shape[2] % dv == 0:
+        unit_rows = int(packed.shape[2]) // dv
+    else:
+        raise ValueError(f"dasc_restore_replay: packed: expected [S_ckpt, R_total, unit_rows * "
+                         f"{dv}] or [S_ckpt, R_total, unit_rows, {dv}], got {tuple(packed.shape)}")
+    if unit_rows < 1 or unit_rows > dk or unit_rows & (unit_rows - 1):
+        raise ValueError(f"dasc_restore_replay: packed: {unit_rows} rows per unit is not a "
+                         f"power of two in [1, {dk}]")
     S_ckpt, R_total = packed.shape[:2]
     a.t(unit_pos, "unit_pos", _i32())
-    if unit_pos.numel() != L * H:
+    n_units = H * dk // unit_rows
+    if unit_pos.numel() != L * n_units:
         raise ValueError(f"dasc_restore_replay: unit_pos has {unit_pos.numel()} entries, the "
-                         f"state has L * H = {L * H} heads")
+                         f"state has L * H * dk / unit_rows = {L * n_units} units")
     N = _pairs(a, src_slot, dst_slot)
     a.t(q, "q", _in_dtypes(), shape=(L, N, None, H, dk))
     K = q.shape[2]
@@ -554,7 +567,7 @@ def dasc_restore_replay(packed, unit_pos, src_slot, dst_slot, active_out, q, k, 
     a.t(n_accept, "n_accept", _i32(), shape=(N,))
     a.t(out, "out", _in_dtypes(), shape=(L, N, K, H, dv), optional=True)
     a.flag(err_flag)
-    _call("dasc_restore_replay", _ptr(packed), S_ckpt, R_total, _ptr(unit_pos), L,
+    _call("dasc_restore_replay", _ptr(packed), S_ckpt, R_total, _ptr(unit_pos), L, unit_rows,
           _ptr(src_slot), _ptr(dst_slot), N, _ptr(active_out), S_dst * H * dk * dv * 4, S_dst,
           H, dk, dv, K, _ptr(q), _ptr(k), _ptr(v), _code(q.dtype), _ptr(alpha), int(decay_kind),
           _ptr(beta), _ptr(n_accept), _ptr(out), _code(out.dtype) if out is not None else HLA_F32,

@@ -214,7 +214,12 @@ int check_restore_replay(const RestoreReplayArgs &a)
     if (!dtype_ok(a.in_dtype) || !dtype_ok(a.out_dtype)) return HLA_ERR_DTYPE;
     if (a.decay != HLA_DECAY_SCALAR && a.decay != HLA_DECAY_VECTOR) return HLA_ERR_DTYPE;
     if (!head_dim_ok(a.dk) || !head_dim_ok(a.dv)) return HLA_ERR_UNSUPPORTED;
-    if ((int64_t)a.R_total > (int64_t)a.L * a.H) return HLA_ERR_PLAN;
+    if (a.unit_rows < 1 || a.unit_rows > a.dk || (a.unit_rows & (a.unit_rows - 1)) != 0)
+        return HLA_ERR_SHAPE;
+    int64_t units;  // in the plan; the kernel indexes unit_pos in 32 bits
+    if (!mul3_ok(a.L, a.H, a.dk / a.unit_rows, units) || units > (int64_t)INT_MAX)
+        return HLA_ERR_SHAPE;
+    if ((int64_t)a.R_total > units) return HLA_ERR_PLAN;
     if (a.N == 0) return HLA_OK;
     if ((a.R_total > 0 && !a.packed) || !a.unit_pos || !a.src_slot || !a.dst_slot ||
         !a.active_out || !a.q || !a.k || !a.v || !a.alpha || !a.beta || !a.n_accept)
@@ -235,7 +240,7 @@ int check_restore_replay(const RestoreReplayArgs &a)
     if (a.L > 1 && a.layer_stride_bytes < layer_bytes) return HLA_ERR_SHAPE;
     if (!mul_ok(a.L - 1, a.layer_stride_bytes, span) ||
         __builtin_add_overflow(span, layer_bytes, &span) ||
-        !mul3_ok(a.S_ckpt, a.R_total, head, pk_bytes))
+        !mul3_ok(a.S_ckpt, a.R_total, (int64_t)a.unit_rows * a.dv * 4, pk_bytes))
         return HLA_ERR_SHAPE;
     const size_t es = dtype_bytes(a.in_dtype), os = dtype_bytes(a.out_dtype);
     const size_t nt = (size_t)toks;
@@ -248,7 +253,7 @@ int check_restore_replay(const RestoreReplayArgs &a)
         {a.v, nt * a.dv * es},
         {a.alpha, nt * (vec ? a.dk : 1) * sizeof(float)},
         {a.beta, nt * sizeof(float)},
-        {a.unit_pos, (size_t)a.L * a.H * sizeof(int32_t)},
+        {a.unit_pos, (size_t)units * sizeof(int32_t)},
         {a.src_slot, (size_t)a.N * sizeof(int32_t)},
         {a.dst_slot, (size_t)a.N * sizeof(int32_t)},
         {a.n_accept, (size_t)a.N * sizeof(int32_t)},

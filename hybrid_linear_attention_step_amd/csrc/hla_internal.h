@@ -144,6 +144,7 @@ struct RestoreReplayArgs {
     int S_ckpt, R_total;
     const int32_t *unit_pos;
     int L;
+    int unit_rows;  // key channels per unit: dk (whole heads) down to 1
     const int32_t *src_slot, *dst_slot;
     int N;
     float *active_out;

@@ -417,21 +417,23 @@ k_tokens(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
     tile_store<RPL>(head_ptr, off, DV, x);
 }
 
-// A checkpoint of whole-head units restored into private slots with each request's
-// accepted drafts replayed on the way ("dasc: Decay-Aware State Compression for Hybrid
-// Linear-Attention Serving", §4.2 dasc-nr; "Serving recurrent attention", part
-// "Speculative decoding without state snapshots").  Workgroup (l, n, h): the head starts
-// as its packed copy from checkpoint slot src_slot[n] (or zero when head h of layer l is
-// not retained), takes the first n_b draft tokens of layer l in registers (their inputs
+// A checkpoint restored into private slots with each request's accepted drafts replayed
+// on the way ("dasc: Decay-Aware State Compression for Hybrid Linear-Attention Serving",
+// §4.2 dasc-nr; "Serving recurrent attention", part "Speculative decoding without state
+// snapshots").  Workgroup (l, n, h): each unit of the head (HU: the whole head, one
+// buffer descriptor; otherwise 2^log2_ur rows, each lane looking up the unit of each of
+// its rows) starts as its packed copy from checkpoint slot src_slot[n], or as zero when
+// it is not retained; the head takes the first n_b draft tokens of layer l in registers
+// (their inputs
 // staged in LDS: half the heads start from zero, with no state read to hide token loads
 // behind, and measured over the whole workload staging every head's tokens was fastest),
 // and is written once into private slot dst_slot[n].  Same lane layout
 // and per-token function as the step, so the result is bitwise that of dasc_restore
 // followed by replay_accepted.
-template <int DK, int DV, typename TIn, typename TOut, bool VEC>
+template <int DK, int DV, typename TIn, typename TOut, bool VEC, bool HU>
 __global__ void __launch_bounds__(2 * DV)
 k_restore_tokens(const float *__restrict__ packed, int S_ckpt, int R_total,
-                 const int32_t *__restrict__ unit_pos, int N,
+                 const int32_t *__restrict__ unit_pos, int log2_ur, int N,
                  const int32_t *__restrict__ src_slot, const int32_t *__restrict__ dst_slot,
                  float *__restrict__ active_out, int64_t layer_stride_floats, int S_dst, int H,
                  int K, const TIn *__restrict__ q, const TIn *__restrict__ k,
@@ -454,25 +456,52 @@ k_restore_tokens(const float *__restrict__ packed, int S_ckpt, int R_total,
         if (err && threadIdx.x == 0 && h == 0 && l == 0) atomicOr(err, HLA_DEVERR_ACCEPT);
         nb = nb < 0 ? 0 : K;
     }
-    int pos = unit_pos[l * H + h];
-    if (pos >= R_total) {  // a bad plan entry: the head starts from zero, as a restore writes it
-        if (err && threadIdx.x == 0) atomicOr(err, HLA_DEVERR_PLAN);
-        pos = -1;
-    }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int cg = lane & 7, rg = lane >> 3;
     const int col0 = wave * 32 + cg * 4, row0 = rg * RPL;
     const uint32_t off = (uint32_t)(row0 * DV + col0) * 4;
 
     float x[RPL][4];
-    if (pos >= 0) {
-        const float *ck = packed + ((size_t)src * R_total + pos) * (DK * DV);
-        tile_load<RPL>(head_rsrc(ck, DK * DV * 4), off, DV, x);
+    if constexpr (HU) {
+        int pos = unit_pos[l * H + h];
+        if (pos >= R_total) {  // a bad plan entry: the head starts from zero, as restored
+            if (err && threadIdx.x == 0) atomicOr(err, HLA_DEVERR_PLAN);
+            pos = -1;
+        }
+        if (pos >= 0) {
+            const float *ck = packed + ((size_t)src * R_total + pos) * (DK * DV);
+            tile_load<RPL>(head_rsrc(ck, DK * DV * 4), off, DV, x);
+        } else {
+#pragma unroll
+            for (int m = 0; m < RPL; ++m)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) x[m][c] = 0.0f;
+        }
     } else {
+        // units of 2^log2_ur rows: every lookup first, then every retained row's load
+        const int upt = DK >> log2_ur;  // units per head
+        const int32_t *up = unit_pos + ((size_t)l * H + h) * upt;
+        const uint32_t rmask = (1u << log2_ur) - 1u;
+        int pr[RPL];
 #pragma unroll
-        for (int m = 0; m < RPL; ++m)
+        for (int m = 0; m < RPL; ++m) {
+            int p = up[(row0 + m) >> log2_ur];
+            if (p >= R_total) {  // a bad plan entry: that unit starts from zero
+                if (err) atomicOr(err, HLA_DEVERR_PLAN);
+                p = -1;
+            }
+            pr[m] = p;
+        }
+        const size_t unit0 = (size_t)src * R_total;  // the source slot's first unit
 #pragma unroll
-            for (int c = 0; c < 4; ++c) x[m][c] = 0.0f;
+        for (int m = 0; m < RPL; ++m) {
+            f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (pr[m] >= 0) {
+                const size_t row = ((unit0 + pr[m]) << log2_ur) + ((row0 + m) & rmask);
+                t = ld_nt(reinterpret_cast<const f32x4 *>(packed + row * DV + col0));
+            }
+            x[m][0] = t.x; x[m][1] = t.y; x[m][2] = t.z; x[m][3] = t.w;
+        }
     }
     const size_t tok0 = (size_t)ln * K * H + h;  // token t of (l, n, h) is tok0 + t * H
     if (nb > 0) {  // uniform over the workgroup
@@ -551,11 +580,19 @@ static void launch_restore_tokens(const RestoreReplayArgs &a, int32_t *err, hipS
 {
     const dim3 grid((unsigned)((size_t)a.L * a.N * a.H)), block(2 * DV);
     const size_t lds = TokenLds<DK, DV, TIn, VEC>::bytes(a.K);
-    hipLaunchKernelGGL((k_restore_tokens<DK, DV, TIn, TOut, VEC>), grid, block, lds, st,
-                       a.packed, a.S_ckpt, a.R_total, a.unit_pos, a.N, a.src_slot, a.dst_slot,
-                       a.active_out, a.layer_stride_bytes / 4, a.S_dst, a.H, a.K,
-                       (const TIn *)a.q, (const TIn *)a.k, (const TIn *)a.v, a.alpha, a.beta,
-                       a.n_accept, (TOut *)a.out, err);
+    const int lr = log2_exact(a.unit_rows);
+    if (a.unit_rows == DK)
+        hipLaunchKernelGGL((k_restore_tokens<DK, DV, TIn, TOut, VEC, true>), grid, block, lds, st,
+                           a.packed, a.S_ckpt, a.R_total, a.unit_pos, lr, a.N, a.src_slot,
+                           a.dst_slot, a.active_out, a.layer_stride_bytes / 4, a.S_dst, a.H, a.K,
+                           (const TIn *)a.q, (const TIn *)a.k, (const TIn *)a.v, a.alpha,
+                           a.beta, a.n_accept, (TOut *)a.out, err);
+    else
+        hipLaunchKernelGGL((k_restore_tokens<DK, DV, TIn, TOut, VEC, false>), grid, block, lds,
+                           st, a.packed, a.S_ckpt, a.R_total, a.unit_pos, lr, a.N, a.src_slot,
+                           a.dst_slot, a.active_out, a.layer_stride_bytes / 4, a.S_dst, a.H, a.K,
+                           (const TIn *)a.q, (const TIn *)a.k, (const TIn *)a.v, a.alpha,
+                           a.beta, a.n_accept, (TOut *)a.out, err);
 }
 
 template <int DK, int DV>
@@ -649,18 +686,18 @@ int replay_accepted_bonus(float *state, int n_slots, const int32_t *slot, int B,
 }
 
 int dasc_restore_replay(const float *packed, int S_ckpt, int R_total, const int32_t *unit_pos,
-                        int L, const int32_t *src_slot, const int32_t *dst_slot, int N,
-                        float *active_out, int64_t layer_stride_bytes, int S_dst, int H, int dk,
-                        int dv, int K, const void *q, const void *k, const void *v, int in_dtype,
-                        const float *alpha, int decay_kind, const float *beta,
+                        int L, int unit_rows, const int32_t *src_slot, const int32_t *dst_slot,
+                        int N, float *active_out, int64_t layer_stride_bytes, int S_dst, int H,
+                        int dk, int dv, int K, const void *q, const void *k, const void *v,
+                        int in_dtype, const float *alpha, int decay_kind, const float *beta,
                         const int32_t *n_accept, void *out, int out_dtype, int32_t *err_flag,
                         void *stream)
 {
-    hla::RestoreReplayArgs a{packed,     S_ckpt, R_total,   unit_pos,  L,    src_slot,
-                             dst_slot,   N,      active_out, layer_stride_bytes, S_dst, H,
-                             dk,         dv,     K,         q,         k,    v,
-                             in_dtype,   alpha,  decay_kind, beta,     n_accept, out,
-                             out_dtype};
+    hla::RestoreReplayArgs a{packed,   S_ckpt,     R_total,    unit_pos, L,     unit_rows,
+                             src_slot, dst_slot,   N,          active_out,
+                             layer_stride_bytes,   S_dst,      H,        dk,    dv,
+                             K,        q,          k,          v,        in_dtype,
+                             alpha,    decay_kind, beta,       n_accept, out,   out_dtype};
     return hla::run_restore_replay(a, err_flag, stream);
 }
 

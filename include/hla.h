@@ -326,22 +326,28 @@ HLA_API int replay_accepted_bonus(float *state, int n_slots, const int32_t *slot
                           int32_t *err_flag, void *stream);
 
 /* -------------------------------------------------------------------------
- * dasc_restore_replay -- dasc_restore of a checkpoint of whole-head units
- * followed by replay_accepted, in one pass over each private state ([dasc]
- * §4.2 dasc-nr restore, then [K3] "Speculative decoding without state
- * snapshots": the accepted drafts are applied on-chip).  For each pair n < N,
- * layer l < L and head h: the head of private slot dst_slot[n] in layer l
- * starts as the packed head of checkpoint slot src_slot[n] when head h of
- * layer l is retained, and as zero otherwise; the first n_b = n_accept[n]
- * draft tokens of layer l are applied to it in order (clamped to [0, K]); it is
- * written once.  The result equals dasc_restore followed by replay_accepted on
- * each layer, bit for bit, with one state read (retained heads only) and one
- * write instead of a read, two writes and a read.
+ * dasc_restore_replay -- dasc_restore of a checkpoint followed by
+ * replay_accepted, in one pass over each private head ([dasc] §4.2 dasc-nr
+ * restore, then [K3] "Speculative decoding without state snapshots": the
+ * accepted drafts are applied on-chip).  A unit is unit_rows consecutive key
+ * channels (rows) of one head: unit_rows = dk for whole-head units (GDN, [dasc]
+ * §4.1), 1 for single key channels (KDA, [dasc] §3.3 / §4.1); head h, rows
+ * [j * unit_rows, (j + 1) * unit_rows) is unit h * (dk / unit_rows) + j of its
+ * layer.  For each pair n < N, layer l < L and head h: each unit of the head
+ * of private slot dst_slot[n] in layer l starts as its packed copy from
+ * checkpoint slot src_slot[n] when retained, and as zero otherwise; the first
+ * n_b = n_accept[n] draft tokens of layer l are applied to the head in order
+ * (clamped to [0, K]); it is written once.  The result equals dasc_restore
+ * (unit_bytes = unit_rows * dv * 4) followed by replay_accepted on each layer,
+ * bit for bit, with one read of the retained units and one write of each head
+ * instead of a read, two writes and a read.
  *
- * packed      device float32 [S_ckpt, R_total, dk, dv]: dasc_pack of head
- *             units (unit_bytes = dk * dv * 4).  Only read.
- * unit_pos    device int32 [L * H] from dasc_plan of the head mask; an entry
- *             >= R_total sets HLA_DEVERR_PLAN and that head starts from zero.
+ * packed      device float32 [S_ckpt, R_total, unit_rows, dv]: dasc_pack of
+ *             the units.  Only read.
+ * unit_pos    device int32 [L, H * dk / unit_rows] from dasc_plan of the unit
+ *             mask; an entry >= R_total sets HLA_DEVERR_PLAN and that unit
+ *             starts from zero.
+ * unit_rows   a power of two, 1 <= unit_rows <= dk.
  * src_slot    device int32 [N] (< S_ckpt); dst_slot device int32 [N] (< S_dst,
  *             distinct); a pair out of range is skipped (HLA_DEVERR_SLOT).
  * active_out  device float32, layer l at active_out + l * layer_stride_bytes,
@@ -358,16 +364,17 @@ HLA_API int replay_accepted_bonus(float *state, int n_slots, const int32_t *slot
  *             each replayed token; rows t >= n_b are left untouched.
  * 1 <= K <= 16; dk, dv in {64, 128}; layer_stride_bytes a multiple of 16 and
  * >= S_dst * H * dk * dv * 4.
- * Errors: NULL, SHAPE, ALIGN, DTYPE, UNSUPPORTED, PLAN (R_total > L * H), ALIAS
- * (the private state overlapping the checkpoint, an input, a plan table or a
- * slot map; the readout overlapping an input), LAUNCH.
+ * Errors: NULL, SHAPE (including unit_rows), ALIGN, DTYPE, UNSUPPORTED, PLAN
+ * (R_total above the unit count L * H * dk / unit_rows), ALIAS (the private
+ * state overlapping the checkpoint, an input, a plan table or a slot map; the
+ * readout overlapping an input), LAUNCH.
  * ---------------------------------------------------------------------- */
 HLA_API int dasc_restore_replay(const float *packed, int S_ckpt, int R_total,
-                                const int32_t *unit_pos, int L, const int32_t *src_slot,
-                                const int32_t *dst_slot, int N, float *active_out,
-                                int64_t layer_stride_bytes, int S_dst, int H, int dk, int dv,
-                                int K, const void *q, const void *k, const void *v,
-                                int in_dtype, const float *alpha, int decay_kind,
+                                const int32_t *unit_pos, int L, int unit_rows,
+                                const int32_t *src_slot, const int32_t *dst_slot, int N,
+                                float *active_out, int64_t layer_stride_bytes, int S_dst, int H,
+                                int dk, int dv, int K, const void *q, const void *k,
+                                const void *v, int in_dtype, const float *alpha, int decay_kind,
                                 const float *beta, const int32_t *n_accept, void *out,
                                 int out_dtype, int32_t *err_flag, void *stream);
 

@@ -171,8 +171,10 @@ static void checks()
             for (int N : {0, 1, 512, INT_MAX})
                 for (int H : {1, 32, INT_MAX})
                     for (int R : {0, 64, INT_MAX})
-                        for (int64_t st : strides) {
+                        for (int64_t st : strides)
+                        for (int ur : {1, 16, 128}) {
                             RestoreReplayArgs rr{};
+                            rr.unit_rows = ur;
                             rr.packed = (const float *)fake(1), rr.S_ckpt = S, rr.R_total = R;
                             rr.unit_pos = (const int32_t *)fake(2), rr.L = L;
                             rr.src_slot = (const int32_t *)fake(3);

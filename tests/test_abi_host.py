@@ -218,8 +218,9 @@ def test_restore_replay_validation(L):
     """The fused restore + replay: the checks of both halves, on the host."""
     f = Fake()
     ub = 128 * 128 * 4
-    base = dict(packed=f(), S_ckpt=512, R_total=64, unit_pos=f(), L=4, src=f(), dst=f(),
-                N=512, active_out=f(4 * 512 * 32 * ub), stride=512 * 32 * ub, S_dst=512, H=32,
+    base = dict(packed=f(), S_ckpt=512, R_total=64, unit_pos=f(), L=4, unit_rows=128,
+                src=f(), dst=f(), N=512, active_out=f(4 * 512 * 32 * ub), stride=512 * 32 * ub,
+                S_dst=512, H=32,
                 dk=128, dv=128, K=8, q=f(), k=f(), v=f(), in_dtype=1, alpha=f(), decay=0,
                 beta=f(), n_accept=f(), out=None, out_dtype=0, err=None, stream=None)
 
@@ -231,6 +232,12 @@ def test_restore_replay_validation(L):
     assert rr(N=0) == OK
     assert rr(K=0) == SHAPE and rr(K=17) == SHAPE and rr(L=0) == SHAPE
     assert rr(R_total=129) == PLAN
+    # the unit count follows unit_rows (N = 0: the checks run, nothing is launched)
+    assert rr(R_total=129, unit_rows=64, N=0) == OK
+    assert rr(R_total=4 * 32 * 128, unit_rows=1, N=0) == OK
+    assert rr(R_total=4 * 32 * 128 + 1, unit_rows=1, N=0) == PLAN
+    for bad in (0, 3, 256, -1):
+        assert rr(unit_rows=bad) == SHAPE, bad
     assert rr(dk=96) == UNSUP and rr(in_dtype=7) == DTYPE and rr(decay=3) == DTYPE
     for name in ("unit_pos", "src", "dst", "active_out", "q", "k", "v", "alpha", "beta",
                  "n_accept"):

@@ -76,6 +76,13 @@ def test_fused_restore_replay_bytes_recounted():
     # and out
     two = (S * R * head + L * S * H * head) + L * bench.replay_bytes(n, H, dk, dv, 4, False)
     assert two - want == L * 3 * H * 2 * head
+    # units of single key channels (R of them), per-channel decay read with each token
+    tok_kda = (2 * dk + dv) * 4 + dk * 4 + 4
+    assert bench.restore_replay_bytes(n, S, R, L, H, dk, dv, 4, unit_rows=1,
+                                      vector_decay=True) == (S * R * dv * 4 + L * S * H * head
+                                                             + L * 12 * H * tok_kda)
+    assert bench.replay_bytes(n, H, dk, dv, 4, False, vector_decay=True) == (
+        3 * H * 2 * head + 12 * H * tok_kda)
 
 
 def test_traffic_only_for_the_profiled_source():

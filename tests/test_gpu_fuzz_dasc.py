@@ -171,10 +171,11 @@ def test_refresh_local_device_errors():
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_restore_replay(i):
-    """The fused restore + replay on random geometry (layers, heads, head shape, draft
-    count, input and readout types, decay kind, masks from empty to full, slot maps,
-    accepted counts with out-of-range values): against the oracle's restore then replay,
-    and bit for bit against the library's restore followed by replay_accepted per layer."""
+    """The fused restore + replay on random geometry (layers, heads, head shape, unit size
+    from one key channel to a whole head, draft count, input and readout types, decay kind,
+    masks from empty to full, slot maps, accepted counts with out-of-range values): against
+    the oracle's restore then replay, and bit for bit against the library's restore
+    followed by replay_accepted per layer."""
     import oracle_par
 
     hla = need_gpu()
@@ -187,12 +188,14 @@ def test_random_restore_replay(i):
     in_dt = str(g.choice(["f32", "bf16", "f16"]))
     out_dt = str(g.choice(["f32", "bf16", "f16"]))
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
-    mask = (g.random((L, H)) < _keep(g)).astype(np.uint8)
+    ur = int(g.choice([1, 2, 8, dk]))  # key channels per unit
+    n_units = H * dk // ur
+    mask = (g.random((L, n_units)) < _keep(g)).astype(np.uint8)
     _, _, unit_pos, R = hla.dasc_plan(mask)
     S_ckpt, S_dst = int(g.integers(1, 6)), int(g.integers(1, 8))
     src, dst = _maps(g, S_ckpt, S_dst)
     N = len(src)
-    packed = (g.standard_normal((S_ckpt, R, dk * dv)) * 0.05).astype(np.float32)
+    packed = (g.standard_normal((S_ckpt, R, ur * dv)) * 0.05).astype(np.float32)
     # inputs: q, k unit vectors, stored in the input type; values the kernel reads exactly
     qk = g.standard_normal((2, L, N, K, H, dk))
     qk /= np.linalg.norm(qk, axis=-1, keepdims=True)
@@ -222,9 +225,9 @@ def test_random_restore_replay(i):
     # the two-call chain
     st2 = torch.full((L, S_dst, H, dk, dv), 3.0, device="cuda")
     out2 = torch.full((L, N, K, H, dv), 5.0, device="cuda", dtype=tdt[out_dt])
-    ub = dk * dv * 4
-    hla.dasc_restore(pk if R else dev(np.zeros(4, np.float32)), S_ckpt, R, pos, L, H, ub,
-                     dev(src), dev(dst), st2, S_dst * H * ub, S_dst)
+    ub = ur * dv * 4
+    hla.dasc_restore(pk if R else dev(np.zeros(4, np.float32)), S_ckpt, R, pos, L, n_units, ub,
+                     dev(src), dev(dst), st2, S_dst * n_units * ub, S_dst)
     for l in range(L):
         hla.replay_accepted(st2[l], xd["q"][l], xd["k"][l], xd["v"][l], xd["alpha"][l],
                             xd["beta"][l], dev(n_acc), int(vec), out=out2[l], slot=dev(dst))
@@ -236,10 +239,11 @@ def test_random_restore_replay(i):
            "beta": beta.astype(np.float64)}
     tol_o = 1e-5 if out_dt == "f32" else (2.0 ** -8 if out_dt == "bf16" else 2.0 ** -10)
     for l in range(L):
-        S64 = np.zeros((N, H, dk, dv))
-        for h in range(H):
-            if unit_pos[l, h] >= 0:
-                S64[:, h] = packed[src, unit_pos[l, h]].reshape(N, dk, dv)
+        S64 = np.zeros((N, H * dk // ur, ur, dv))
+        for u in range(n_units):
+            if unit_pos[l, u] >= 0:
+                S64[:, u] = packed[src, unit_pos[l, u]].reshape(N, ur, dv)
+        S64 = S64.reshape(N, H, dk, dv)
         o_ref, scale = oracle_par.replay_terms(S64, {n: x64[n][l] for n in x64}, n_acc,
                                                per_channel=vec)
         assert oracle_par.rel_err_tiles(got[l][dst], S64) <= 1e-5

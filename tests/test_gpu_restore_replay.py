@@ -15,9 +15,11 @@ Every case is checked twice:
 Small cases span GDN / KDA decay, FP32 / BF16 / FP16 inputs and readouts, all four
 head shapes, K = 1, 5 and 16, accepted counts from 0 to K with clamping, slot maps that
 permute, leave destination slots alone and name bad slots, a plan entry past the
-checkpoint, a checkpoint that retains nothing, and no pairs.  The full-size case is the
-checkpoint workload: 4 layers x 512 requests x 32 GDN heads x 128 x 128 with 64 of 128
-layer-heads retained and K = 8 drafts, one accepted count per request for every layer."""
+checkpoint, a checkpoint that retains nothing, no pairs, and units smaller than a head
+(1 to 32 key channels).  The full-size cases are the two checkpoint workloads: 4 layers x
+512 requests x 32 heads x 128 x 128, K = 8 drafts, one accepted count per request for
+every layer; GDN heads with 64 of 128 layer-heads retained, and KDA single key channels
+selected by static horizons."""
 import numpy as np
 import pytest
 
@@ -72,10 +74,13 @@ def _fused(hla, cfg, packed_d, unit_pos, src, dst, S_dst, xd, n_acc, out_dtype, 
     return st, out, int(err.item())
 
 
-def _chain(hla, cfg, packed_d, unit_pos, src, dst, S_dst, xd, n_acc, out_dtype, init):
+def _chain(hla, cfg, packed_d, unit_pos, src, dst, S_dst, xd, n_acc, out_dtype, init,
+           unit_rows=None):
     """dasc_restore, then replay_accepted layer by layer into the restored slots."""
     L, H = cfg.L, cfg.H
-    ub = cfg.dk * cfg.dv * 4
+    ur = cfg.dk if unit_rows is None else unit_rows
+    ub = ur * cfg.dv * 4
+    n_units = H * cfg.dk // ur
     st = torch.full((L, S_dst, H, cfg.dk, cfg.dv), init, device="cuda")
     out = torch.full((L, len(src), cfg.K, H, cfg.dv), 5.0, device="cuda",
                      dtype=getattr(torch, TORCH_DT[out_dtype]))
@@ -83,8 +88,8 @@ def _chain(hla, cfg, packed_d, unit_pos, src, dst, S_dst, xd, n_acc, out_dtype, 
     S_ck, R = packed_d.shape[:2]
     src_d, dst_d, n_d = dev(src), dev(dst), dev(n_acc)
     pos = dev(np.ascontiguousarray(unit_pos, np.int32).reshape(-1))
-    hla.dasc_restore(packed_d, S_ck, R, pos, L, H, ub, src_d, dst_d, st, S_dst * H * ub, S_dst,
-                     err_flag=err)
+    hla.dasc_restore(packed_d, S_ck, R, pos, L, n_units, ub, src_d, dst_d, st,
+                     S_dst * n_units * ub, S_dst, err_flag=err)
     for l in range(L):
         hla.replay_accepted(st[l], xd["q"][l], xd["k"][l], xd["v"][l], xd["alpha"][l],
                             xd["beta"][l], n_d, 1 if cfg.decay == "vector" else 0, out=out[l],
@@ -93,17 +98,20 @@ def _chain(hla, cfg, packed_d, unit_pos, src, dst, S_dst, xd, n_acc, out_dtype, 
 
 
 def _oracle(cfg, packed, offsets, unit_index, src, dst, S_dst, x64, n_acc, init,
-            zero_heads=()):
+            zero_heads=(), unit_rows=None, zero_rows=()):
     """The oracle's restore into a state filled with `init` (the heads (l, h) listed in
     zero_heads then zero-filled in the restored slots), then its replay per layer.
     Returns the state [L, S_dst, H, dk, dv] (float64), readouts [L, N, K, H, dv] and the
     readouts' term sizes [L, N, K, H]."""
     L, H, dk, dv = cfg.L, cfg.H, cfg.dk, cfg.dv
+    ur = dk if unit_rows is None else unit_rows
     rest = np.full((L, S_dst, H, dk, dv), init, np.float32)
-    oracle.dasc_restore(packed, offsets, unit_index, L, H, src, dst,
-                        rest.view(np.uint8).reshape(L, S_dst, H, dk * dv * 4))
+    oracle.dasc_restore(packed, offsets, unit_index, L, H * dk // ur, src, dst,
+                        rest.view(np.uint8).reshape(L, S_dst, H * dk // ur, ur * dv * 4))
     for l, h in zero_heads:
         rest[l, dst, h] = 0.0
+    for l, h, r0, r1 in zero_rows:
+        rest[l, dst, h, r0:r1] = 0.0
     S64 = rest.astype(np.float64)
     outs, scales = [], []
     for l in range(L):
@@ -295,3 +303,129 @@ def test_restore_replay_full_size():
               f"of its terms' size", flush=True)
         assert err_s <= TOL and err_o <= TOL
         assert (out_h[l][~rows] == 5.0).all()
+
+
+def _row_checkpoint(cfg, unit_rows, keep, seed):
+    """Every slot's state, a seeded random mask over units of unit_rows key channels
+    ([L, H * dk / unit_rows]) and the oracle's pack of the retained units."""
+    hla = need_gpu()
+    n_units = cfg.H * cfg.dk // unit_rows
+    g = np.random.default_rng(seed)
+    mask = (g.random((cfg.L, n_units)) < keep).astype(np.uint8)
+    offsets, unit_index, unit_pos, R = hla.dasc_plan(mask)
+    act = np.stack([synth.initial_state(cfg, S=cfg.slots, layer=l) for l in range(cfg.L)])
+    ids = np.arange(cfg.slots, dtype=np.int32)
+    packed = oracle.dasc_pack(act.view(np.uint8).reshape(cfg.L, cfg.slots, n_units,
+                                                         unit_rows * cfg.dv * 4),
+                              offsets, unit_index, ids, ids, cfg.slots)
+    return packed, offsets, unit_index, unit_pos, R
+
+
+@pytest.mark.parametrize("kind,dk,dv", [("kda", 128, 128), ("gdn", 128, 64), ("kda", 64, 128)])
+@pytest.mark.parametrize("unit_rows", [1, 4, 16, 32])
+def test_restore_replay_row_units(kind, dk, dv, unit_rows):
+    """Units of unit_rows key channels (1: the KDA checkpoints' single channels): each
+    lane looks up the unit of every row it holds."""
+    hla = need_gpu()
+    cfg = _cfg(kind, dk, dv, "f32", K=8, L=2, S=5, seed=3 + unit_rows)
+    packed, offsets, unit_index, unit_pos, R = _row_checkpoint(cfg, unit_rows, 0.35,
+                                                               70 + unit_rows + dk)
+    src = np.array([4, 0, 2, 1], np.int32)
+    dst = np.array([2, 5, 0, 3], np.int32)       # slots 1 and 4 are left alone
+    n_acc = np.array([8, 0, 3, 11], np.int32)    # 11 clamps to 8
+    S_dst = 6
+    x = _drafts(cfg, len(src))
+    xd = dev_inputs(x, "f32")
+    packed_d = dev(packed.view(np.float32).reshape(cfg.slots, R, unit_rows * dv))
+    st, out, err = _fused(hla, cfg, packed_d, unit_pos, src, dst, S_dst, xd, n_acc, "f32", 7.0)
+    assert err == hla.DEVERR_ACCEPT
+    st2, out2, err2 = _chain(hla, cfg, packed_d, unit_pos, src, dst, S_dst, xd, n_acc, "f32",
+                             7.0, unit_rows=unit_rows)
+    assert err2 == hla.DEVERR_ACCEPT
+    assert torch.equal(st, st2) and torch.equal(out, out2)
+    ref_st, ref_out, scale = _oracle(cfg, packed, offsets, unit_index, src, dst, S_dst,
+                                     f64_inputs(x, "f32"), n_acc, 7.0, unit_rows=unit_rows)
+    assert _check_vs_oracle(st, out, ref_st, ref_out, scale, n_acc, cfg.K) <= TOL
+    assert (host(st)[:, [1, 4]] == 7.0).all()
+
+
+def test_restore_replay_row_units_bad_plan_entry():
+    """A single-channel unit whose plan entry is past the checkpoint starts from zero and
+    is reported, as the restore writes it."""
+    hla = need_gpu()
+    cfg = _cfg("kda", 128, 128, "f32", K=4, L=2, S=3, seed=9)
+    packed, offsets, unit_index, unit_pos, R = _row_checkpoint(cfg, 1, 0.3, 90)
+    pos = unit_pos.copy()
+    u_bad = int(np.flatnonzero(pos[1] >= 0)[3])
+    pos[1, u_bad] = R + 5
+    src = np.array([2, 0], np.int32)
+    dst = np.array([0, 1], np.int32)
+    n_acc = np.array([4, 2], np.int32)
+    x = _drafts(cfg, 2)
+    xd = dev_inputs(x, "f32")
+    packed_d = dev(packed.view(np.float32).reshape(cfg.slots, R, cfg.dv))
+    st, out, err = _fused(hla, cfg, packed_d, pos, src, dst, 2, xd, n_acc, "f32", 7.0)
+    assert err == hla.DEVERR_PLAN
+    st2, out2, err2 = _chain(hla, cfg, packed_d, pos, src, dst, 2, xd, n_acc, "f32", 7.0,
+                             unit_rows=1)
+    assert err2 == hla.DEVERR_PLAN
+    assert torch.equal(st, st2) and torch.equal(out, out2)
+    h, r = divmod(u_bad, cfg.dk)
+    ref_st, ref_out, scale = _oracle(cfg, packed, offsets, unit_index, src, dst, 2,
+                                     f64_inputs(x, "f32"), n_acc, 7.0, unit_rows=1,
+                                     zero_rows=[(1, h, r, r + 1)])
+    assert _check_vs_oracle(st, out, ref_st, ref_out, scale, n_acc, cfg.K) <= TOL
+
+
+def test_restore_replay_full_size_kda_channel_rows():
+    """The KDA checkpoint workload: 4 layers x 512 requests x 32 heads x 128 x 128 with
+    units of single key channels selected by static horizons (4,124 of 16,384), per-channel
+    decay, K = 8 drafts.  Bit for bit against the two calls over the whole 4 GiB state and
+    every readout; against the oracle on sampled requests."""
+    hla = need_gpu()
+    cfg = synth.CONFIGS["dasc_kda"]
+    L, S_, H, dk, dv, K = cfg.L, cfg.slots, cfg.H, cfg.dk, cfg.dv, cfg.K
+    A, d = synth.gate_params(cfg)
+    _, mask3 = hla.dasc_static_horizon(A, d, hla.GATE_SOFTPLUS, cfg.a_s, cfg.W_max)
+    mask = mask3.reshape(L, H * dk)
+    _, _, unit_pos, R = hla.dasc_plan(mask)
+    # the checkpoint's rows are drawn as the active state's are
+    packed = synth.initial_state(synth.shrink(cfg, H=R, dk=1), S=S_).reshape(S_, R, dv)
+    g = synth.rng(cfg.seed, 98)
+    src = g.permutation(S_).astype(np.int32)
+    dst = g.permutation(S_).astype(np.int32)
+    n_acc = synth.replay_inputs(cfg, 0)["n_accept"]
+    x = _drafts(cfg, S_)
+    xd = dev_inputs(x, cfg.in_dtype)
+    packed_d = dev(packed)
+    print(f"full size: {L} layers x {S_} requests x {H} heads, {R} of {L * H * dk} channel "
+          f"rows retained, {int(n_acc.sum())} accepted tokens per layer", flush=True)
+    st, out, err = _fused(hla, cfg, packed_d, unit_pos, src, dst, S_, xd, n_acc, "f32", 7.0)
+    assert err == 0
+    st2, out2, err2 = _chain(hla, cfg, packed_d, unit_pos, src, dst, S_, xd, n_acc, "f32", 7.0,
+                             unit_rows=1)
+    assert err2 == 0
+    assert torch.equal(st, st2)
+    del st2
+    assert torch.equal(out, out2)
+    del out2
+    pick = np.sort(g.choice(S_, size=16, replace=False))
+    n_p = n_acc[pick]
+    x64 = f64_inputs({n: a[:, pick] for n, a in x.items()}, cfg.in_dtype)
+    st_h = st[:, torch.from_numpy(dst[pick]).long().cuda()].cpu().numpy()
+    out_h = out[:, torch.from_numpy(pick).long().cuda()].cpu().numpy()
+    for l in range(L):
+        S64 = np.zeros((len(pick), H, dk, dv))
+        pl = unit_pos[l].reshape(H, dk)
+        for h in range(H):
+            kept = np.flatnonzero(pl[h] >= 0)
+            S64[:, h, kept] = packed[src[pick]][:, pl[h][kept]]
+        o, sc = oracle_par.replay_terms(S64, {n: x64[n][l] for n in NAMES}, n_p,
+                                        per_channel=True)
+        err_s = oracle_par.rel_err_tiles(st_h[l], S64)
+        rows = np.arange(K)[None, :] < n_p[:, None]
+        e = np.where(rows[:, :, None, None], np.abs(out_h[l] - o), 0.0).max(axis=-1)
+        err_o = float((e / np.maximum(sc, 1e-30)).max())
+        print(f"layer {l}: {int((pl >= 0).sum())} rows retained; sampled requests' state err "
+              f"{err_s:.2e}, readout err {err_o:.2e} of its terms' size", flush=True)
+        assert err_s <= TOL and err_o <= TOL
