@@ -227,7 +227,7 @@ int check_restore_replay(const RestoreReplayArgs &a)
     const bool vec = a.decay == HLA_DECAY_VECTOR;
     if ((a.packed && !aligned16(a.packed)) || !aligned16(a.active_out) || !aligned16(a.q) ||
         !aligned16(a.k) || !aligned16(a.v) || (a.out && !aligned16(a.out)) ||
-        (vec && !aligned16(a.alpha)) || a.layer_stride_bytes % 16 != 0)
+        (vec && !aligned16(a.alpha)) || !aligned16(a.unit_pos) || a.layer_stride_bytes % 16 != 0)
         return HLA_ERR_ALIGN;
     // sizes: workgroups (l, n, h) and (l, n, t, h) tokens must fit 32-bit indices; the
     // byte spans must fit 64 bits

@@ -483,14 +483,23 @@ k_restore_tokens(const float *__restrict__ packed, int S_ckpt, int R_total,
         const int32_t *up = unit_pos + ((size_t)l * H + h) * upt;
         const uint32_t rmask = (1u << log2_ur) - 1u;
         int pr[RPL];
+        if (log2_ur == 0) {  // one unit per row: the lane's RPL entries are contiguous
+#pragma unroll
+            for (int i = 0; i < RPL / 4; ++i) {
+                const u32x4 w = *reinterpret_cast<const u32x4 *>(up + row0 + 4 * i);
+                pr[4 * i] = (int)w.x; pr[4 * i + 1] = (int)w.y;
+                pr[4 * i + 2] = (int)w.z; pr[4 * i + 3] = (int)w.w;
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < RPL; ++m) pr[m] = up[(row0 + m) >> log2_ur];
+        }
 #pragma unroll
         for (int m = 0; m < RPL; ++m) {
-            int p = up[(row0 + m) >> log2_ur];
-            if (p >= R_total) {  // a bad plan entry: that unit starts from zero
+            if (pr[m] >= R_total) {  // a bad plan entry: that unit starts from zero
                 if (err) atomicOr(err, HLA_DEVERR_PLAN);
-                p = -1;
+                pr[m] = -1;
             }
-            pr[m] = p;
         }
         const size_t unit0 = (size_t)src * R_total;  // the source slot's first unit
 #pragma unroll

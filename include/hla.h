@@ -344,9 +344,9 @@ HLA_API int replay_accepted_bonus(float *state, int n_slots, const int32_t *slot
  *
  * packed      device float32 [S_ckpt, R_total, unit_rows, dv]: dasc_pack of
  *             the units.  Only read.
- * unit_pos    device int32 [L, H * dk / unit_rows] from dasc_plan of the unit
- *             mask; an entry >= R_total sets HLA_DEVERR_PLAN and that unit
- *             starts from zero.
+ * unit_pos    device int32 [L, H * dk / unit_rows] (16-byte aligned) from
+ *             dasc_plan of the unit mask; an entry >= R_total sets
+ *             HLA_DEVERR_PLAN and that unit starts from zero.
  * unit_rows   a power of two, 1 <= unit_rows <= dk.
  * src_slot    device int32 [N] (< S_ckpt); dst_slot device int32 [N] (< S_dst,
  *             distinct); a pair out of range is skipped (HLA_DEVERR_SLOT).

@@ -246,6 +246,7 @@ def test_restore_replay_validation(L):
     assert rr(stride=512 * 32 * ub - 16) == SHAPE     # layers would overlap
     assert rr(stride=512 * 32 * ub + 4) == ALIGN
     assert rr(v=ctypes.c_void_p(f().value + 8)) == ALIGN
+    assert rr(unit_pos=ctypes.c_void_p(f().value + 4)) == ALIGN
     assert rr(decay=1, alpha=ctypes.c_void_p(f().value + 4)) == ALIGN
     assert rr(out=ctypes.c_void_p(f().value + 2), out_dtype=1) == ALIGN
     assert rr(L=1 << 12, N=1 << 12, H=1 << 8) == SHAPE  # workgroups beyond 32-bit indices
