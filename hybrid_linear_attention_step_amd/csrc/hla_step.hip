@@ -1,7 +1,8 @@
 // gfx950 kernels for the FP32 gated delta-rule step (GDN scalar decay, KDA
 // per-key-channel decay) and for several tokens per launch: the replay of
-// accepted draft tokens (optionally followed by the bonus token).  The verify
-// pass over all drafts has its own kernel (hla_verify.hip).
+// accepted draft tokens (optionally followed by the bonus token, or preceded by
+// the restore of a checkpoint into the state).  The verify pass over all drafts
+// has its own kernel (hla_verify.hip).
 //
 // Operation ("DAMP: Decay-Aware Mixed-Precision Recurrent-State
 // Quantization", §3.1 Eq. (1)-(2)), per (request, head), state S in dk x dv:
@@ -424,12 +425,11 @@ k_tokens(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
 // buffer descriptor; otherwise 2^log2_ur rows, each lane looking up the unit of each of
 // its rows) starts as its packed copy from checkpoint slot src_slot[n], or as zero when
 // it is not retained; the head takes the first n_b draft tokens of layer l in registers
-// (their inputs
-// staged in LDS: half the heads start from zero, with no state read to hide token loads
-// behind, and measured over the whole workload staging every head's tokens was fastest),
-// and is written once into private slot dst_slot[n].  Same lane layout
-// and per-token function as the step, so the result is bitwise that of dasc_restore
-// followed by replay_accepted.
+// and is written once into private slot dst_slot[n].  The tokens' inputs are staged in
+// LDS for every head with n_b > 0: many heads start from zero, with no state read to hide
+// token loads behind, and over the whole workload staging all of them measured fastest.
+// Same lane layout and per-token function as the step, so the result is bitwise that of
+// dasc_restore followed by replay_accepted.
 template <int DK, int DV, typename TIn, typename TOut, bool VEC, bool HU>
 __global__ void __launch_bounds__(2 * DV)
 k_restore_tokens(const float *__restrict__ packed, int S_ckpt, int R_total,
