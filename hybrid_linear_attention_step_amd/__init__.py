@@ -35,6 +35,8 @@ SIGNATURES = {
     "dasc_restore": ([_P, _I, _I, _P, _I, _I, _L, _P, _P, _I, _P, _L, _I, _P, _P], _I),
     "dasc_restore_replay": ([_P, _I, _I, _P, _I, _I, _P, _P, _I, _P, _L, _I, _I, _I, _I, _I,
                              _P, _P, _P, _I, _P, _I, _P, _P, _P, _I, _P, _P], _I),
+    "dasc_restore_int8_replay": ([_P, _P, _I, _I, _P, _I, _I, _P, _P, _I, _P, _L, _I, _I, _I, _I,
+                                  _I, _P, _P, _P, _I, _P, _I, _P, _P, _P, _I, _P, _P], _I),
     "dasc_pack_int8": ([_P, _L, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P],
                        _I),
     "dasc_restore_int8": ([_P, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P, _I, _P, _L, _I, _P, _P],
@@ -526,6 +528,61 @@ def dasc_restore(packed, S_ckpt, R_total, unit_pos, L, n_units, unit_bytes, src_
           int(layer_stride_bytes), S_dst, _ptr(err_flag), a.stream(stream))
 
 
+def _restore_replay_units(a, units, name, dtypes, dv, dk):
+    """Rows per checkpoint unit from the unit buffer's shape: [S_ckpt, R_total, unit_rows *
+    dv] or [S_ckpt, R_total, unit_rows, dv]."""
+    a.t(units, name, dtypes)
+    if units.dim() == 4 and units.shape[3] == dv:
+        unit_rows = int(units.shape[2])
+    elif units.dim() == 3 and units.shape[2] % dv == 0:
+        unit_rows = int(units.shape[2]) // dv
+    else:
+        raise ValueError(f"{a.fn}: {name}: expected [S_ckpt, R_total, unit_rows * {dv}] or "
+                         f"[S_ckpt, R_total, unit_rows, {dv}], got {tuple(units.shape)}")
+    if unit_rows < 1 or unit_rows > dk or unit_rows & (unit_rows - 1):
+        raise ValueError(f"{a.fn}: {name}: {unit_rows} rows per unit is not a power of two in "
+                         f"[1, {dk}]")
+    return unit_rows
+
+
+def _restore_replay(fn, units, scales, unit_pos, src_slot, dst_slot, active_out, q, k, v, alpha,
+                    beta, n_accept, decay_kind, out, err_flag, stream):
+    a = _Args(fn)
+    a.t(active_out, "active_out", _f32(), ndim=5)
+    L, S_dst, H, dk, dv = active_out.shape
+    q8 = scales is not None
+    unit_rows = _restore_replay_units(a, units, "codes" if q8 else "packed",
+                                      (_torch().int8,) if q8 else _f32(), dv, dk)
+    S_ckpt, R_total = units.shape[:2]
+    if q8:
+        a.nbytes(scales, "scales", S_ckpt * R_total * unit_rows * 4, _f32())
+        if scales.numel() != S_ckpt * R_total * unit_rows:
+            raise ValueError(f"{fn}: scales has {scales.numel()} entries, the checkpoint has "
+                             f"{S_ckpt * R_total * unit_rows} rows")
+    a.t(unit_pos, "unit_pos", _i32())
+    n_units = H * dk // unit_rows
+    if unit_pos.numel() != L * n_units:
+        raise ValueError(f"{fn}: unit_pos has {unit_pos.numel()} entries, the state has "
+                         f"L * H * dk / unit_rows = {L * n_units} units")
+    N = _pairs(a, src_slot, dst_slot)
+    a.t(q, "q", _in_dtypes(), shape=(L, N, None, H, dk))
+    K = q.shape[2]
+    a.t(k, "k", (q.dtype,), shape=(L, N, K, H, dk))
+    a.t(v, "v", (q.dtype,), shape=(L, N, K, H, dv))
+    _decay_arg(a, alpha, "alpha", (L, N, K, H), decay_kind, dk)
+    a.t(beta, "beta", _f32(), shape=(L, N, K, H))
+    a.t(n_accept, "n_accept", _i32(), shape=(N,))
+    a.t(out, "out", _in_dtypes(), shape=(L, N, K, H, dv), optional=True)
+    a.flag(err_flag)
+    head = ([_ptr(units), _ptr(scales)] if q8 else [_ptr(units)])
+    _call(fn, *head, S_ckpt, R_total, _ptr(unit_pos), L, unit_rows, _ptr(src_slot),
+          _ptr(dst_slot), N, _ptr(active_out), S_dst * H * dk * dv * 4, S_dst, H, dk, dv, K,
+          _ptr(q), _ptr(k), _ptr(v), _code(q.dtype), _ptr(alpha), int(decay_kind), _ptr(beta),
+          _ptr(n_accept), _ptr(out), _code(out.dtype) if out is not None else HLA_F32,
+          _ptr(err_flag), a.stream(stream))
+    return out
+
+
 def dasc_restore_replay(packed, unit_pos, src_slot, dst_slot, active_out, q, k, v, alpha, beta,
                         n_accept, decay_kind, out=None, err_flag=None, stream=None):
     """Restore a checkpoint into private slots and replay each request's accepted drafts,
@@ -537,42 +594,20 @@ def dasc_restore_replay(packed, unit_pos, src_slot, dst_slot, active_out, q, k, 
     [L, S_dst, H, dk, dv] fp32; q, k [L, N, K, H, dk], v [L, N, K, H, dv]; alpha
     [L, N, K, H] (scalar decay) or [L, N, K, H, dk]; beta [L, N, K, H]; n_accept [N]
     int32; out [L, N, K, H, dv] or None (no readout)."""
-    a = _Args("dasc_restore_replay")
-    a.t(active_out, "active_out", _f32(), ndim=5)
-    L, S_dst, H, dk, dv = active_out.shape
-    a.t(packed, "packed", _f32())
-    if packed.dim() == 4 and packed.shape[3] == dv:
-        unit_rows = int(packed.shape[2])
-    elif packed.dim() == 3 and packed.shape[2] % dv == 0:
-        unit_rows = int(packed.shape[2]) // dv
-    else:
-        raise ValueError(f"dasc_restore_replay: packed: expected [S_ckpt, R_total, unit_rows * "
-                         f"{dv}] or [S_ckpt, R_total, unit_rows, {dv}], got {tuple(packed.shape)}")
-    if unit_rows < 1 or unit_rows > dk or unit_rows & (unit_rows - 1):
-        raise ValueError(f"dasc_restore_replay: packed: {unit_rows} rows per unit is not a "
-                         f"power of two in [1, {dk}]")
-    S_ckpt, R_total = packed.shape[:2]
-    a.t(unit_pos, "unit_pos", _i32())
-    n_units = H * dk // unit_rows
-    if unit_pos.numel() != L * n_units:
-        raise ValueError(f"dasc_restore_replay: unit_pos has {unit_pos.numel()} entries, the "
-                         f"state has L * H * dk / unit_rows = {L * n_units} units")
-    N = _pairs(a, src_slot, dst_slot)
-    a.t(q, "q", _in_dtypes(), shape=(L, N, None, H, dk))
-    K = q.shape[2]
-    a.t(k, "k", (q.dtype,), shape=(L, N, K, H, dk))
-    a.t(v, "v", (q.dtype,), shape=(L, N, K, H, dv))
-    _decay_arg(a, alpha, "alpha", (L, N, K, H), decay_kind, dk)
-    a.t(beta, "beta", _f32(), shape=(L, N, K, H))
-    a.t(n_accept, "n_accept", _i32(), shape=(N,))
-    a.t(out, "out", _in_dtypes(), shape=(L, N, K, H, dv), optional=True)
-    a.flag(err_flag)
-    _call("dasc_restore_replay", _ptr(packed), S_ckpt, R_total, _ptr(unit_pos), L, unit_rows,
-          _ptr(src_slot), _ptr(dst_slot), N, _ptr(active_out), S_dst * H * dk * dv * 4, S_dst,
-          H, dk, dv, K, _ptr(q), _ptr(k), _ptr(v), _code(q.dtype), _ptr(alpha), int(decay_kind),
-          _ptr(beta), _ptr(n_accept), _ptr(out), _code(out.dtype) if out is not None else HLA_F32,
-          _ptr(err_flag), a.stream(stream))
-    return out
+    return _restore_replay("dasc_restore_replay", packed, None, unit_pos, src_slot, dst_slot,
+                           active_out, q, k, v, alpha, beta, n_accept, decay_kind, out,
+                           err_flag, stream)
+
+
+def dasc_restore_int8_replay(codes, scales, unit_pos, src_slot, dst_slot, active_out, q, k, v,
+                             alpha, beta, n_accept, decay_kind, out=None, err_flag=None,
+                             stream=None):
+    """As dasc_restore_replay, from an INT8 checkpoint: codes int8 [S_ckpt, R_total,
+    unit_rows, dv] (or [S_ckpt, R_total, unit_rows * dv]) and scales fp32 with one entry
+    per checkpoint row (S_ckpt * R_total * unit_rows), as dasc_pack_int8 writes them."""
+    return _restore_replay("dasc_restore_int8_replay", codes, scales, unit_pos, src_slot,
+                           dst_slot, active_out, q, k, v, alpha, beta, n_accept, decay_kind,
+                           out, err_flag, stream)
 
 
 def dasc_pack_int8(active, layer_stride_bytes, S_act, L, n_units, unit_rows, dv, offsets,

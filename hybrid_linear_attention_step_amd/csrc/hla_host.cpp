@@ -221,13 +221,16 @@ int check_restore_replay(const RestoreReplayArgs &a)
         return HLA_ERR_SHAPE;
     if ((int64_t)a.R_total > units) return HLA_ERR_PLAN;
     if (a.N == 0) return HLA_OK;
-    if ((a.R_total > 0 && !a.packed) || !a.unit_pos || !a.src_slot || !a.dst_slot ||
-        !a.active_out || !a.q || !a.k || !a.v || !a.alpha || !a.beta || !a.n_accept)
+    const bool q8 = a.q8;
+    if ((a.R_total > 0 && (!a.packed || (q8 && !a.scales))) || !a.unit_pos || !a.src_slot ||
+        !a.dst_slot || !a.active_out || !a.q || !a.k || !a.v || !a.alpha || !a.beta ||
+        !a.n_accept)
         return HLA_ERR_NULL;
     const bool vec = a.decay == HLA_DECAY_VECTOR;
     if ((a.packed && !aligned16(a.packed)) || !aligned16(a.active_out) || !aligned16(a.q) ||
         !aligned16(a.k) || !aligned16(a.v) || (a.out && !aligned16(a.out)) ||
-        (vec && !aligned16(a.alpha)) || !aligned16(a.unit_pos) || a.layer_stride_bytes % 16 != 0)
+        (vec && !aligned16(a.alpha)) || !aligned16(a.unit_pos) ||
+        (q8 && a.scales && !aligned16(a.scales)) || a.layer_stride_bytes % 16 != 0)
         return HLA_ERR_ALIGN;
     // sizes: workgroups (l, n, h) and (l, n, t, h) tokens must fit 32-bit indices; the
     // byte spans must fit 64 bits
@@ -240,7 +243,10 @@ int check_restore_replay(const RestoreReplayArgs &a)
     if (a.L > 1 && a.layer_stride_bytes < layer_bytes) return HLA_ERR_SHAPE;
     if (!mul_ok(a.L - 1, a.layer_stride_bytes, span) ||
         __builtin_add_overflow(span, layer_bytes, &span) ||
-        !mul3_ok(a.S_ckpt, a.R_total, (int64_t)a.unit_rows * a.dv * 4, pk_bytes))
+        !mul3_ok(a.S_ckpt, a.R_total, (int64_t)a.unit_rows * a.dv * (q8 ? 1 : 4), pk_bytes))
+        return HLA_ERR_SHAPE;
+    int64_t sc_bytes = 0;  // INT8: one FP32 scale per checkpoint row
+    if (q8 && !mul3_ok(a.S_ckpt, a.R_total, (int64_t)a.unit_rows * 4, sc_bytes))
         return HLA_ERR_SHAPE;
     const size_t es = dtype_bytes(a.in_dtype), os = dtype_bytes(a.out_dtype);
     const size_t nt = (size_t)toks;
@@ -248,6 +254,7 @@ int check_restore_replay(const RestoreReplayArgs &a)
     const Range outr{a.out, nt * a.dv * os};
     const Range ins[] = {
         {a.packed, (size_t)pk_bytes},
+        {a.scales, (size_t)sc_bytes},
         {a.q, nt * a.dk * es},
         {a.k, nt * a.dk * es},
         {a.v, nt * a.dv * es},

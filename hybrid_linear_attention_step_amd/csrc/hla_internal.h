@@ -140,7 +140,9 @@ int check_dasc_int8(const void *active, int64_t layer_stride_bytes, int S_act, i
 // dasc_restore_replay: a checkpoint of whole-head units restored into private
 // slots with each request's accepted drafts replayed on the way.
 struct RestoreReplayArgs {
-    const float *packed;
+    bool q8;               // an INT8 checkpoint (codes + one FP32 scale per row)
+    const void *packed;    // FP32 units, or the INT8 codes
+    const float *scales;   // INT8: the scales; unused for FP32
     int S_ckpt, R_total;
     const int32_t *unit_pos;
     int L;
@@ -161,6 +163,15 @@ struct RestoreReplayArgs {
 };
 
 int check_restore_replay(const RestoreReplayArgs &a);
+
+// The INT8 checkpoint restore (arguments validated as dasc_restore_int8's) by blocks of
+// 128 rows through the fused restore + replay kernel with no tokens.  Returns false, with
+// nothing launched, when the geometry or alignment does not fit that kernel.
+bool restore_int8_by_blocks(const int8_t *codes, const float *scales, int S_ckpt, int R_total,
+                            const int32_t *unit_pos, int L, int n_units, int unit_rows, int dv,
+                            const int32_t *src_slot, const int32_t *dst_slot, int N,
+                            float *active_out, int64_t layer_stride_bytes, int S_dst,
+                            int32_t *err, void *stream);
 
 // log2 of a power of two (checked by the caller).
 inline int log2_exact(int x)

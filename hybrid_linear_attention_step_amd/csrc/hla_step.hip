@@ -430,10 +430,10 @@ k_tokens(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
 // token loads behind, and over the whole workload staging all of them measured fastest.
 // Same lane layout and per-token function as the step, so the result is bitwise that of
 // dasc_restore followed by replay_accepted.
-template <int DK, int DV, typename TIn, typename TOut, bool VEC, bool HU>
+template <int DK, int DV, typename TIn, typename TOut, bool VEC, bool HU, bool Q8>
 __global__ void __launch_bounds__(2 * DV)
-k_restore_tokens(const float *__restrict__ packed, int S_ckpt, int R_total,
-                 const int32_t *__restrict__ unit_pos, int log2_ur, int N,
+k_restore_tokens(const void *__restrict__ packed, const float *__restrict__ scales, int S_ckpt,
+                 int R_total, const int32_t *__restrict__ unit_pos, int log2_ur, int N,
                  const int32_t *__restrict__ src_slot, const int32_t *__restrict__ dst_slot,
                  float *__restrict__ active_out, int64_t layer_stride_floats, int S_dst, int H,
                  int K, const TIn *__restrict__ q, const TIn *__restrict__ k,
@@ -451,7 +451,7 @@ k_restore_tokens(const float *__restrict__ packed, int S_ckpt, int R_total,
         if (err && threadIdx.x == 0) atomicOr(err, HLA_DEVERR_SLOT);
         return;
     }
-    int nb = n_accept[n];
+    int nb = n_accept ? n_accept[n] : 0;  // no accepted counts: a restore only
     if (nb < 0 || nb > K) {
         if (err && threadIdx.x == 0 && h == 0 && l == 0) atomicOr(err, HLA_DEVERR_ACCEPT);
         nb = nb < 0 ? 0 : K;
@@ -468,8 +468,29 @@ k_restore_tokens(const float *__restrict__ packed, int S_ckpt, int R_total,
             if (err && threadIdx.x == 0) atomicOr(err, HLA_DEVERR_PLAN);
             pos = -1;
         }
-        if (pos >= 0) {
-            const float *ck = packed + ((size_t)src * R_total + pos) * (DK * DV);
+        if (pos >= 0 && Q8) {  // codes of the head's rows, then their scales
+            const size_t u0 = (size_t)src * R_total + pos;
+            const int8_t *cb = static_cast<const int8_t *>(packed) + u0 * (DK * DV) + col0;
+            // cached loads: a row's 128 code bytes are read 32 at a time by the head's four
+            // waves, which must find the line in L2 (nontemporal loads fetched it 4 times)
+            uint32_t w[RPL];
+#pragma unroll
+            for (int m = 0; m < RPL; ++m)
+                w[m] = *reinterpret_cast<const uint32_t *>(cb + (size_t)(row0 + m) * DV);
+            float sc[RPL];
+#pragma unroll
+            for (int i = 0; i < RPL / 4; ++i) {
+                const f32x4 t = *reinterpret_cast<const f32x4 *>(scales + u0 * DK + row0 + 4 * i);
+                sc[4 * i] = t.x; sc[4 * i + 1] = t.y; sc[4 * i + 2] = t.z; sc[4 * i + 3] = t.w;
+            }
+#pragma unroll
+            for (int m = 0; m < RPL; ++m)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    x[m][c] = (float)(int)(int8_t)(w[m] >> (8 * c)) * sc[m];  // code * scale
+        } else if (pos >= 0) {
+            const float *ck =
+                static_cast<const float *>(packed) + ((size_t)src * R_total + pos) * (DK * DV);
             tile_load<RPL>(head_rsrc(ck, DK * DV * 4), off, DV, x);
         } else {
 #pragma unroll
@@ -502,14 +523,40 @@ k_restore_tokens(const float *__restrict__ packed, int S_ckpt, int R_total,
             }
         }
         const size_t unit0 = (size_t)src * R_total;  // the source slot's first unit
+        if constexpr (Q8) {  // every retained row's codes, then its scale
+            uint32_t w[RPL];
+            float sc[RPL];
 #pragma unroll
-        for (int m = 0; m < RPL; ++m) {
-            f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (pr[m] >= 0) {
-                const size_t row = ((unit0 + pr[m]) << log2_ur) + ((row0 + m) & rmask);
-                t = ld_nt(reinterpret_cast<const f32x4 *>(packed + row * DV + col0));
+            for (int m = 0; m < RPL; ++m) {
+                w[m] = 0u;
+                if (pr[m] >= 0) {
+                    const size_t row = ((unit0 + pr[m]) << log2_ur) + ((row0 + m) & rmask);
+                    w[m] = *reinterpret_cast<const uint32_t *>(  // cached, as above
+                        static_cast<const int8_t *>(packed) + row * DV + col0);
+                }
             }
-            x[m][0] = t.x; x[m][1] = t.y; x[m][2] = t.z; x[m][3] = t.w;
+#pragma unroll
+            for (int m = 0; m < RPL; ++m) {
+                sc[m] = 0.0f;
+                if (pr[m] >= 0)
+                    sc[m] = scales[((unit0 + pr[m]) << log2_ur) + ((row0 + m) & rmask)];
+            }
+#pragma unroll
+            for (int m = 0; m < RPL; ++m)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    x[m][c] = (float)(int)(int8_t)(w[m] >> (8 * c)) * sc[m];  // 0 when omitted
+        } else {
+#pragma unroll
+            for (int m = 0; m < RPL; ++m) {
+                f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (pr[m] >= 0) {
+                    const size_t row = ((unit0 + pr[m]) << log2_ur) + ((row0 + m) & rmask);
+                    t = ld_nt(reinterpret_cast<const f32x4 *>(
+                        static_cast<const float *>(packed) + row * DV + col0));
+                }
+                x[m][0] = t.x; x[m][1] = t.y; x[m][2] = t.z; x[m][3] = t.w;
+            }
         }
     }
     const size_t tok0 = (size_t)ln * K * H + h;  // token t of (l, n, h) is tok0 + t * H
@@ -590,18 +637,51 @@ static void launch_restore_tokens(const RestoreReplayArgs &a, int32_t *err, hipS
     const dim3 grid((unsigned)((size_t)a.L * a.N * a.H)), block(2 * DV);
     const size_t lds = TokenLds<DK, DV, TIn, VEC>::bytes(a.K);
     const int lr = log2_exact(a.unit_rows);
-    if (a.unit_rows == DK)
-        hipLaunchKernelGGL((k_restore_tokens<DK, DV, TIn, TOut, VEC, true>), grid, block, lds, st,
-                           a.packed, a.S_ckpt, a.R_total, a.unit_pos, lr, a.N, a.src_slot,
-                           a.dst_slot, a.active_out, a.layer_stride_bytes / 4, a.S_dst, a.H, a.K,
-                           (const TIn *)a.q, (const TIn *)a.k, (const TIn *)a.v, a.alpha,
-                           a.beta, a.n_accept, (TOut *)a.out, err);
-    else
-        hipLaunchKernelGGL((k_restore_tokens<DK, DV, TIn, TOut, VEC, false>), grid, block, lds,
-                           st, a.packed, a.S_ckpt, a.R_total, a.unit_pos, lr, a.N, a.src_slot,
-                           a.dst_slot, a.active_out, a.layer_stride_bytes / 4, a.S_dst, a.H, a.K,
-                           (const TIn *)a.q, (const TIn *)a.k, (const TIn *)a.v, a.alpha,
-                           a.beta, a.n_accept, (TOut *)a.out, err);
+#define HLA_RT_LAUNCH(HU_, Q8_)                                                               \
+    hipLaunchKernelGGL((k_restore_tokens<DK, DV, TIn, TOut, VEC, HU_, Q8_>), grid, block, lds, \
+                       st, a.packed, a.scales, a.S_ckpt, a.R_total, a.unit_pos, lr, a.N,        \
+                       a.src_slot, a.dst_slot, a.active_out, a.layer_stride_bytes / 4, a.S_dst, \
+                       a.H, a.K, (const TIn *)a.q, (const TIn *)a.k, (const TIn *)a.v, a.alpha, \
+                       a.beta, a.n_accept, (TOut *)a.out, err)
+    const bool hu = a.unit_rows == DK;
+    if (a.q8) {
+        if (hu) HLA_RT_LAUNCH(true, true);
+        else HLA_RT_LAUNCH(false, true);
+    } else {
+        if (hu) HLA_RT_LAUNCH(true, false);
+        else HLA_RT_LAUNCH(false, false);
+    }
+#undef HLA_RT_LAUNCH
+}
+
+// The INT8 checkpoint restore by blocks of 128 rows (the fused kernel with no tokens): a
+// lane holds 16 consecutive rows of its block, so its plan entries are one contiguous
+// read and its stores cover whole 128-byte lines.  For sparse checkpoints of small units
+// it beats the row-per-lane restore kernel; see dasc_restore_int8.
+bool restore_int8_by_blocks(const int8_t *codes, const float *scales, int S_ckpt, int R_total,
+                            const int32_t *unit_pos, int L, int n_units, int unit_rows, int dv,
+                            const int32_t *src_slot, const int32_t *dst_slot, int N,
+                            float *active_out, int64_t layer_stride_bytes, int S_dst,
+                            int32_t *err, void *stream)
+{
+    constexpr int DK = 128;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t rows = (int64_t)n_units * unit_rows;  // per slot and layer
+    if ((dv != 64 && dv != 128) || unit_rows > DK || rows % DK != 0) return false;
+    const auto a16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    if (!a16(codes) || !a16(scales) || !a16(unit_pos) || !a16(active_out) ||
+        layer_stride_bytes % 16 != 0)
+        return false;
+    const int64_t blocks = rows / DK;
+    if ((int64_t)L * N * blocks > (int64_t)INT_MAX) return false;
+    RestoreReplayArgs a{true,     codes,     scales,   S_ckpt,  R_total, unit_pos,
+                        L,        unit_rows, src_slot, dst_slot, N,      active_out,
+                        layer_stride_bytes,  S_dst,    (int)blocks, DK,  dv,
+                        1,        nullptr,   nullptr,  nullptr, HLA_F32, nullptr,
+                        HLA_DECAY_SCALAR,    nullptr,  nullptr, nullptr, HLA_F32};
+    if (dv == 128) launch_restore_tokens<DK, 128, float, float, false>(a, err, st);
+    else launch_restore_tokens<DK, 64, float, float, false>(a, err, st);
+    return true;
 }
 
 template <int DK, int DV>
@@ -702,11 +782,28 @@ int dasc_restore_replay(const float *packed, int S_ckpt, int R_total, const int3
                         const int32_t *n_accept, void *out, int out_dtype, int32_t *err_flag,
                         void *stream)
 {
-    hla::RestoreReplayArgs a{packed,   S_ckpt,     R_total,    unit_pos, L,     unit_rows,
-                             src_slot, dst_slot,   N,          active_out,
-                             layer_stride_bytes,   S_dst,      H,        dk,    dv,
+    hla::RestoreReplayArgs a{false,    packed,     nullptr,    S_ckpt,   R_total, unit_pos,
+                             L,        unit_rows,  src_slot,   dst_slot, N,       active_out,
+                             layer_stride_bytes,   S_dst,      H,        dk,      dv,
                              K,        q,          k,          v,        in_dtype,
-                             alpha,    decay_kind, beta,       n_accept, out,   out_dtype};
+                             alpha,    decay_kind, beta,       n_accept, out,     out_dtype};
+    return hla::run_restore_replay(a, err_flag, stream);
+}
+
+int dasc_restore_int8_replay(const int8_t *codes, const float *scales, int S_ckpt, int R_total,
+                             const int32_t *unit_pos, int L, int unit_rows,
+                             const int32_t *src_slot, const int32_t *dst_slot, int N,
+                             float *active_out, int64_t layer_stride_bytes, int S_dst, int H,
+                             int dk, int dv, int K, const void *q, const void *k, const void *v,
+                             int in_dtype, const float *alpha, int decay_kind, const float *beta,
+                             const int32_t *n_accept, void *out, int out_dtype,
+                             int32_t *err_flag, void *stream)
+{
+    hla::RestoreReplayArgs a{true,     codes,      scales,     S_ckpt,   R_total, unit_pos,
+                             L,        unit_rows,  src_slot,   dst_slot, N,       active_out,
+                             layer_stride_bytes,   S_dst,      H,        dk,      dv,
+                             K,        q,          k,          v,        in_dtype,
+                             alpha,    decay_kind, beta,       n_accept, out,     out_dtype};
     return hla::run_restore_replay(a, err_flag, stream);
 }
 

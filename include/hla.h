@@ -86,7 +86,7 @@ enum hla_device_error {
 HLA_API const char *hla_status_str(int status);
 
 /* Library ABI version (major * 100 + minor): 102 (1.01 added HLA_F16, 1.02
- * dasc_restore_replay). */
+ * dasc_restore_replay and dasc_restore_int8_replay). */
 HLA_API int hla_version(void);
 
 /* -------------------------------------------------------------------------
@@ -429,6 +429,31 @@ HLA_API int dasc_restore_int8(const int8_t *codes, const float *scales, int S_ck
                       int dv, const int32_t *src_slot, const int32_t *dst_slot, int N,
                       float *active_out, int64_t layer_stride_bytes, int S_dst,
                       int32_t *err_flag, void *stream);
+
+/* -------------------------------------------------------------------------
+ * dasc_restore_int8_replay -- dasc_restore_int8 followed by replay_accepted in
+ * one pass over each private head, as dasc_restore_replay does for an FP32
+ * checkpoint ([dasc] App. E.1 Eq. (8): a hit dequantises each retained row
+ * once, value = code * scale in FP32; [dasc] §4.2 dasc-nr; [K3] "Speculative
+ * decoding without state snapshots").  The result equals dasc_restore_int8
+ * (n_units = H * dk / unit_rows) followed by replay_accepted on each layer, bit
+ * for bit.
+ *
+ * codes       device int8 [S_ckpt, R_total, unit_rows, dv] (16-byte aligned)
+ * scales      device float32 [S_ckpt, R_total, unit_rows] (16-byte aligned):
+ *             dasc_pack_int8 of the units.  Only read.
+ * Every other argument, the unit geometry, the device errors and the status
+ * codes are those of dasc_restore_replay (ALIAS also when the private state or
+ * the readout overlaps the codes or the scales).
+ * ---------------------------------------------------------------------- */
+HLA_API int dasc_restore_int8_replay(const int8_t *codes, const float *scales, int S_ckpt,
+                                     int R_total, const int32_t *unit_pos, int L, int unit_rows,
+                                     const int32_t *src_slot, const int32_t *dst_slot, int N,
+                                     float *active_out, int64_t layer_stride_bytes, int S_dst,
+                                     int H, int dk, int dv, int K, const void *q, const void *k,
+                                     const void *v, int in_dtype, const float *alpha,
+                                     int decay_kind, const float *beta, const int32_t *n_accept,
+                                     void *out, int out_dtype, int32_t *err_flag, void *stream);
 
 /* -------------------------------------------------------------------------
  * Static selection ([dasc] §3.3 Eq. (2)-(3), §4.1).  Host-only, float64.

@@ -261,6 +261,30 @@ def test_restore_replay_validation(L):
     assert rr(out=inside) == ALIAS
 
 
+def test_restore_int8_replay_validation(L):
+    """The INT8-checkpoint form: the codes and scales join the checks of the FP32 form."""
+    f = Fake()
+    ub = 128 * 128 * 4
+    act = f(4 * 512 * 32 * ub)
+    base = dict(codes=f(), scales=f(), S_ckpt=512, R_total=4124, unit_pos=f(), L=4,
+                unit_rows=1, src=f(), dst=f(), N=512, active_out=act, stride=512 * 32 * ub,
+                S_dst=512, H=32, dk=128, dv=128, K=8, q=f(), k=f(), v=f(), in_dtype=0,
+                alpha=f(), decay=1, beta=f(), n_accept=f(), out=None, out_dtype=0, err=None,
+                stream=None)
+
+    def rr(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.dasc_restore_int8_replay(*a.values())
+
+    assert rr(N=0) == OK
+    assert rr(scales=None) == NULL and rr(codes=None) == NULL
+    assert rr(scales=ctypes.c_void_p(f().value + 4)) == ALIGN
+    assert rr(unit_rows=5) == SHAPE and rr(R_total=4 * 32 * 128 + 1, N=0) == PLAN
+    inside = ctypes.c_void_p(act.value + 2 * 512 * 32 * ub)
+    assert rr(codes=inside) == ALIAS and rr(scales=inside) == ALIAS
+
+
 def test_dasc_plan_matches_oracle(L, orc):
     g = np.random.default_rng(40)
     for trial in range(20):
@@ -571,6 +595,19 @@ def test_binding_checks_checkpoint_buffer_sizes():
         hla.dasc_restore_replay(**dict(rr, q=z(L, N, K, H, dk, dtype=torch.float64)))
     with pytest.raises(ValueError, match="GPU"):
         hla.dasc_restore_replay(**rr)
+    # the INT8 form: codes int8, one scale per checkpoint row
+    r8 = dict(rr)
+    del r8["packed"]
+    codes = torch.zeros((S, 4, 8, dk), dtype=torch.int8)      # units of 8 channels
+    pos8 = z(L, H * dk // 8, dtype=i32)
+    with pytest.raises(TypeError, match="codes"):
+        hla.dasc_restore_int8_replay(codes.float(), z(S * 4 * 8), **dict(r8, unit_pos=pos8))
+    with pytest.raises(ValueError, match="scales"):
+        hla.dasc_restore_int8_replay(codes, z(S * 4 * 8 - 1), **dict(r8, unit_pos=pos8))
+    with pytest.raises(ValueError, match="unit_pos"):
+        hla.dasc_restore_int8_replay(codes, z(S * 4 * 8), **r8)
+    with pytest.raises(ValueError, match="GPU"):
+        hla.dasc_restore_int8_replay(codes, z(S * 4 * 8), **dict(r8, unit_pos=pos8))
     # INT8 checkpoints: codes and scales sized by rows, the FP32 state by the geometry
     rows, dv = 2, 4
     act32 = torch.zeros(L * S * n_units * rows * dv)

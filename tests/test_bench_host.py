@@ -81,6 +81,10 @@ def test_fused_restore_replay_bytes_recounted():
     assert bench.restore_replay_bytes(n, S, R, L, H, dk, dv, 4, unit_rows=1,
                                       vector_decay=True) == (S * R * dv * 4 + L * S * H * head
                                                              + L * 12 * H * tok_kda)
+    # an INT8 checkpoint: each retained row's dv codes and its FP32 scale
+    assert bench.restore_replay_bytes(n, S, R, L, H, dk, dv, 4, unit_rows=1, vector_decay=True,
+                                      int8=True) == (S * R * (dv + 4) + L * S * H * head
+                                                     + L * 12 * H * tok_kda)
     assert bench.replay_bytes(n, H, dk, dv, 4, False, vector_decay=True) == (
         3 * H * 2 * head + 12 * H * tok_kda)
 

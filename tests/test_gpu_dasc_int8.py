@@ -67,6 +67,72 @@ def test_pack_and_restore_int8(unit_rows, dv, n_units, p_keep):
     assert int(err.item()) == 0
 
 
+@pytest.mark.parametrize("unit_rows,dv,n_units", [
+    (1, 128, 384),   # channel rows, three heads per layer
+    (2, 64, 192),
+    (8, 128, 48),
+    (32, 64, 12),
+    (128, 128, 3),   # whole heads
+    (1, 64, 200),    # 200 rows per layer: not whole blocks of 128
+])
+def test_restore_int8_sparse_checkpoints(unit_rows, dv, n_units):
+    """Checkpoints that retain at most 3/8 of their units, where the restore goes by blocks
+    of 128 rows whenever a layer's rows are whole blocks and the tables 16-byte aligned:
+    bit-exact against the oracle's restore into sentinel-filled slots, with a plan entry
+    past the packed rows (that unit zero, HLA_DEVERR_PLAN) and a pair whose destination is
+    past S_dst (skipped, HLA_DEVERR_SLOT); the same restore with unit_pos and scales at
+    4-byte but not 16-byte alignment gives the same bits; an empty checkpoint restores
+    zeros."""
+    hla = need_gpu()
+    g = np.random.default_rng(7100 + unit_rows * 10 + dv)
+    L, S_ = 3, 5
+    act = (g.standard_normal((L, S_, n_units, unit_rows, dv)) * 0.05).astype(np.float32)
+    mask = (g.random((L, n_units)) < 0.25).astype(np.uint8)
+    mask[0, 0] = 1
+    offsets, unit_index, unit_pos, R = hla.dasc_plan(mask)
+    assert 0 < 8 * R <= 3 * L * n_units
+    S_ckpt, S_dst = S_, S_ + 2
+    c_o, s_o = oracle.dasc_pack_int8(act, offsets, unit_index, np.arange(S_, dtype=np.int32),
+                                     np.arange(S_, dtype=np.int32), S_ckpt)
+    bad_pos = unit_pos.reshape(-1).copy()
+    bad_pos[0] = R + 3                          # layer 0, unit 0: retained
+    src = np.array([3, 0, 4, 1], np.int32)
+    dst = np.array([6, 1, S_dst + 2, 0], np.int32)
+    out0 = np.full((L, S_dst, n_units, unit_rows, dv), 3.5, np.float32)
+    stride = _stride(S_dst, n_units, unit_rows, dv)
+    ok = dst < S_dst
+    ref = oracle.dasc_restore_int8(c_o, s_o, offsets, unit_index, L, n_units, src[ok], dst[ok],
+                                   out0.copy())
+    ref[0, dst[ok], 0] = 0.0                    # the unit with the bad position reads as zeros
+
+    def restore(pos_t, scales_t):
+        out = dev(out0)
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        hla.dasc_restore_int8(dev(c_o), scales_t, S_ckpt, R, pos_t, L, n_units, unit_rows, dv,
+                              dev(src), dev(dst), out, stride, S_dst, err_flag=err)
+        assert int(err.item()) == hla.DEVERR_PLAN | hla.DEVERR_SLOT
+        return host(out)
+
+    def shifted(x):  # the same values, 4 bytes past a 16-byte boundary
+        buf = torch.zeros(x.size + 4, dtype=torch.from_numpy(x[:0]).dtype, device="cuda")
+        view = buf[1:1 + x.size]
+        view.copy_(dev(x.reshape(-1)))
+        assert view.data_ptr() % 16 == 4
+        return view
+
+    assert np.array_equal(restore(dev(bad_pos), dev(s_o)), ref)
+    assert np.array_equal(restore(shifted(bad_pos), shifted(s_o)), ref)
+    # an empty checkpoint: every unit omitted, every destination unit zero
+    none = np.full(L * n_units, -1, np.int32)
+    out = dev(out0)
+    hla.dasc_restore_int8(torch.zeros(16, dtype=torch.int8, device="cuda"),
+                          torch.zeros(4, device="cuda"), S_ckpt, 0, dev(none), L, n_units,
+                          unit_rows, dv, dev(src[ok]), dev(dst[ok]), out, stride, S_dst)
+    want = out0.copy()
+    want[:, dst[ok]] = 0.0
+    assert np.array_equal(host(out), want)
+
+
 def _every_pair_against_oracle(hla, act_h, codes, scales, offsets, unit_index, unit_pos, R):
     """All 512 pairs of a full-size checkpoint workload: the GPU's pack against the oracle's
     (scales bit-exact, codes within one step on at most 0.1%), then the oracle's checkpoint

@@ -112,9 +112,14 @@ def _oracle(cfg, packed, offsets, unit_index, src, dst, S_dst, x64, n_acc, init,
         rest[l, dst, h] = 0.0
     for l, h, r0, r1 in zero_rows:
         rest[l, dst, h, r0:r1] = 0.0
+    return _oracle_replay(cfg, rest, dst, x64, n_acc)
+
+
+def _oracle_replay(cfg, rest, dst, x64, n_acc):
+    """The oracle's replay of each layer's drafts into the restored slots dst of `rest`."""
     S64 = rest.astype(np.float64)
     outs, scales = [], []
-    for l in range(L):
+    for l in range(cfg.L):
         Sl = np.ascontiguousarray(S64[l][dst])
         o, sc = oracle_par.replay_terms(Sl, {n: x64[n][l] for n in NAMES}, n_acc,
                                         per_channel=(cfg.decay == "vector"))
@@ -428,4 +433,164 @@ def test_restore_replay_full_size_kda_channel_rows():
         err_o = float((e / np.maximum(sc, 1e-30)).max())
         print(f"layer {l}: {int((pl >= 0).sum())} rows retained; sampled requests' state err "
               f"{err_s:.2e}, readout err {err_o:.2e} of its terms' size", flush=True)
+        assert err_s <= TOL and err_o <= TOL
+
+
+# ------------------------------------------------------------------ INT8 checkpoints
+
+def _int8_checkpoint(cfg, unit_rows, keep, seed):
+    """The oracle's INT8 pack ([dasc] App. E.1) of every slot's state over a seeded random
+    mask of units of unit_rows key channels: codes [S, R, unit_rows, dv], scales
+    [S, R, unit_rows] and the plan."""
+    hla = need_gpu()
+    n_units = cfg.H * cfg.dk // unit_rows
+    g = np.random.default_rng(seed)
+    mask = (g.random((cfg.L, n_units)) < keep).astype(np.uint8)
+    offsets, unit_index, unit_pos, R = hla.dasc_plan(mask)
+    act = np.stack([synth.initial_state(cfg, S=cfg.slots, layer=l) for l in range(cfg.L)])
+    ids = np.arange(cfg.slots, dtype=np.int32)
+    codes, scales = oracle.dasc_pack_int8(
+        act.reshape(cfg.L, cfg.slots, n_units, unit_rows, cfg.dv), offsets, unit_index, ids,
+        ids, cfg.slots)
+    return codes, scales, offsets, unit_index, unit_pos, R
+
+
+def _fused8(hla, cfg, codes_d, scales_d, unit_pos, src, dst, S_dst, xd, n_acc, out_dtype,
+            init):
+    st = torch.full((cfg.L, S_dst, cfg.H, cfg.dk, cfg.dv), init, device="cuda")
+    out = torch.full((cfg.L, len(src), cfg.K, cfg.H, cfg.dv), 5.0, device="cuda",
+                     dtype=getattr(torch, TORCH_DT[out_dtype]))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pos = dev(np.ascontiguousarray(unit_pos, np.int32).reshape(-1))
+    hla.dasc_restore_int8_replay(codes_d, scales_d, pos, dev(src), dev(dst), st, xd["q"],
+                                 xd["k"], xd["v"], xd["alpha"], xd["beta"], dev(n_acc),
+                                 1 if cfg.decay == "vector" else 0, out=out, err_flag=err)
+    return st, out, int(err.item())
+
+
+def _chain8(hla, cfg, codes_d, scales_d, unit_pos, src, dst, S_dst, xd, n_acc, out_dtype, init,
+            unit_rows):
+    """dasc_restore_int8, then replay_accepted layer by layer into the restored slots."""
+    L, H, dv = cfg.L, cfg.H, cfg.dv
+    n_units = H * cfg.dk // unit_rows
+    st = torch.full((L, S_dst, H, cfg.dk, dv), init, device="cuda")
+    out = torch.full((L, len(src), cfg.K, H, dv), 5.0, device="cuda",
+                     dtype=getattr(torch, TORCH_DT[out_dtype]))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    S_ck, R = codes_d.shape[:2]
+    src_d, dst_d, n_d = dev(src), dev(dst), dev(n_acc)
+    pos = dev(np.ascontiguousarray(unit_pos, np.int32).reshape(-1))
+    hla.dasc_restore_int8(codes_d, scales_d, S_ck, R, pos, L, n_units, unit_rows, dv, src_d,
+                          dst_d, st, S_dst * H * cfg.dk * dv * 4, S_dst, err_flag=err)
+    for l in range(L):
+        hla.replay_accepted(st[l], xd["q"][l], xd["k"][l], xd["v"][l], xd["alpha"][l],
+                            xd["beta"][l], n_d, 1 if cfg.decay == "vector" else 0, out=out[l],
+                            slot=dst_d, err_flag=err)
+    return st, out, int(err.item())
+
+
+def _oracle8(cfg, codes, scales, offsets, unit_index, src, dst, S_dst, x64, n_acc, init,
+             unit_rows):
+    """The oracle's INT8 restore (code x scale in FP32) into a state filled with `init`,
+    then its replay per layer."""
+    L, H, dk, dv = cfg.L, cfg.H, cfg.dk, cfg.dv
+    n_units = H * dk // unit_rows
+    rest = np.full((L, S_dst, H, dk, dv), init, np.float32)
+    view = rest.reshape(L, S_dst, n_units, unit_rows, dv)
+    oracle.dasc_restore_int8(codes, scales, offsets, unit_index, L, n_units, src, dst, view)
+    return _oracle_replay(cfg, rest, dst, x64, n_acc)
+
+
+@pytest.mark.parametrize("kind,dk,dv,in_dtype", [("kda", 128, 128, "f32"),
+                                                 ("gdn", 128, 64, "bf16"),
+                                                 ("kda", 64, 128, "f16")])
+@pytest.mark.parametrize("unit_rows", [1, 16, "dk"])
+def test_restore_int8_replay_matches_oracle_and_chain(kind, dk, dv, in_dtype, unit_rows):
+    """An INT8 checkpoint restored and replayed in one pass: against the oracle's INT8
+    restore then replay, and bit for bit against dasc_restore_int8 then replay_accepted."""
+    hla = need_gpu()
+    ur = dk if unit_rows == "dk" else unit_rows
+    cfg = _cfg(kind, dk, dv, in_dtype, K=8, L=2, S=5, seed=17 + ur)
+    codes, scales, offsets, unit_index, unit_pos, R = _int8_checkpoint(cfg, ur, 0.4, 40 + ur)
+    src = np.array([4, 0, 2, 1], np.int32)
+    dst = np.array([2, 5, 0, 3], np.int32)
+    n_acc = np.array([8, 0, 3, 11], np.int32)    # 11 clamps to 8
+    S_dst = 6
+    x = _drafts(cfg, len(src))
+    xd = dev_inputs(x, in_dtype)
+    codes_d, scales_d = dev(codes), dev(scales)
+    st, out, err = _fused8(hla, cfg, codes_d, scales_d, unit_pos, src, dst, S_dst, xd, n_acc,
+                           "f32", 7.0)
+    assert err == hla.DEVERR_ACCEPT
+    st2, out2, err2 = _chain8(hla, cfg, codes_d, scales_d, unit_pos, src, dst, S_dst, xd, n_acc,
+                              "f32", 7.0, ur)
+    assert err2 == hla.DEVERR_ACCEPT
+    assert torch.equal(st, st2) and torch.equal(out, out2)
+    ref_st, ref_out, scale = _oracle8(cfg, codes, scales, offsets, unit_index, src, dst, S_dst,
+                                      f64_inputs(x, in_dtype), n_acc, 7.0, ur)
+    assert _check_vs_oracle(st, out, ref_st, ref_out, scale, n_acc, cfg.K) <= TOL
+    assert (host(st)[:, [1, 4]] == 7.0).all()
+
+
+@pytest.mark.parametrize("name", ["dasc_gdn", "dasc_kda"])
+def test_restore_int8_replay_full_size(name):
+    """The two checkpoint workloads with INT8 checkpoints (the library's pack of a random
+    state): bit for bit against dasc_restore_int8 then replay_accepted over the whole 4 GiB
+    private state and every readout; against the oracle (its INT8 restore of the same codes
+    and scales, then its replay) on sampled requests."""
+    hla = need_gpu()
+    cfg = synth.CONFIGS[name]
+    L, S_, H, dk, dv, K = cfg.L, cfg.slots, cfg.H, cfg.dk, cfg.dv, cfg.K
+    if cfg.decay == "vector":
+        A, d = synth.gate_params(cfg)
+        _, mask3 = hla.dasc_static_horizon(A, d, hla.GATE_SOFTPLUS, cfg.a_s, cfg.W_max)
+        mask, ur = mask3.reshape(L, H * dk), 1
+    else:
+        mask, ur = synth.dasc_masks(cfg), dk
+    n_units = H * dk // ur
+    offsets, unit_index, unit_pos, R = hla.dasc_plan(mask)
+    gen = torch.Generator(device="cuda").manual_seed(cfg.seed)
+    act = torch.randn((L, S_, n_units, ur, dv), device="cuda", generator=gen) * 0.05
+    codes_d = torch.empty((S_, R, ur, dv), dtype=torch.int8, device="cuda")
+    scales_d = torch.empty((S_, R, ur), device="cuda")
+    ids_h = np.arange(S_, dtype=np.int32)
+    hla.dasc_pack_int8(act, S_ * H * dk * dv * 4, S_, L, n_units, ur, dv, dev(offsets),
+                       dev(unit_index), R, dev(ids_h), dev(ids_h), codes_d, scales_d, S_)
+    del act
+    g = synth.rng(cfg.seed, 97)
+    src = g.permutation(S_).astype(np.int32)
+    dst = g.permutation(S_).astype(np.int32)
+    n_acc = synth.replay_inputs(cfg, 0)["n_accept"]
+    x = _drafts(cfg, S_)
+    xd = dev_inputs(x, cfg.in_dtype)
+    print(f"{name}: {R} of {L * n_units} units of {ur} channels retained, "
+          f"{int(n_acc.sum())} accepted tokens per layer", flush=True)
+    st, out, err = _fused8(hla, cfg, codes_d, scales_d, unit_pos, src, dst, S_, xd, n_acc,
+                           "f32", 7.0)
+    assert err == 0
+    st2, out2, err2 = _chain8(hla, cfg, codes_d, scales_d, unit_pos, src, dst, S_, xd, n_acc,
+                              "f32", 7.0, ur)
+    assert err2 == 0
+    assert torch.equal(st, st2)
+    del st2
+    assert torch.equal(out, out2)
+    del out2
+    pick = np.sort(g.choice(S_, size=16, replace=False))
+    codes = codes_d[torch.from_numpy(src[pick]).long().cuda()].cpu().numpy()
+    scs = scales_d[torch.from_numpy(src[pick]).long().cuda()].cpu().numpy()
+    sub = np.arange(len(pick), dtype=np.int32)
+    x64 = f64_inputs({n: a[:, pick] for n, a in x.items()}, cfg.in_dtype)
+    rest = np.zeros((L, len(pick), H, dk, dv), np.float32)
+    oracle.dasc_restore_int8(codes, scs, offsets, unit_index, L, n_units, sub, sub,
+                             rest.reshape(L, len(pick), n_units, ur, dv))
+    ref_st, ref_out, scale = _oracle_replay(cfg, rest, sub, x64, n_acc[pick])
+    st_h = st[:, torch.from_numpy(dst[pick]).long().cuda()].cpu().numpy()
+    out_h = out[:, torch.from_numpy(pick).long().cuda()].cpu().numpy()
+    for l in range(L):
+        err_s = oracle_par.rel_err_tiles(st_h[l], ref_st[l])
+        rows = np.arange(K)[None, :] < n_acc[pick][:, None]
+        e = np.where(rows[:, :, None, None], np.abs(out_h[l] - ref_out[l]), 0.0).max(axis=-1)
+        err_o = float((e / np.maximum(scale[l], 1e-30)).max())
+        print(f"layer {l}: sampled requests' state err {err_s:.2e}, readout err {err_o:.2e} "
+              f"of its terms' size", flush=True)
         assert err_s <= TOL and err_o <= TOL
