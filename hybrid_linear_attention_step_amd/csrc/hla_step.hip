@@ -429,7 +429,8 @@ k_tokens(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
 // LDS for every head with n_b > 0: many heads start from zero, with no state read to hide
 // token loads behind, and over the whole workload staging all of them measured fastest.
 // Same lane layout and per-token function as the step, so the result is bitwise that of
-// dasc_restore followed by replay_accepted.
+// dasc_restore followed by replay_accepted.  With n_accept NULL it is a restore only (the
+// INT8 restore of sparse checkpoints by blocks of 128 rows, H then counting blocks).
 template <int DK, int DV, typename TIn, typename TOut, bool VEC, bool HU, bool Q8>
 __global__ void __launch_bounds__(2 * DV)
 k_restore_tokens(const void *__restrict__ packed, const float *__restrict__ scales, int S_ckpt,
@@ -462,6 +463,7 @@ k_restore_tokens(const void *__restrict__ packed, const float *__restrict__ scal
     const uint32_t off = (uint32_t)(row0 * DV + col0) * 4;
 
     float x[RPL][4];
+    uint32_t omitted = 0u;  // restore only: rows already written as zeros
     if constexpr (HU) {
         int pos = unit_pos[l * H + h];
         if (pos >= R_total) {  // a bad plan entry: the head starts from zero, as restored
@@ -523,6 +525,18 @@ k_restore_tokens(const void *__restrict__ packed, const float *__restrict__ scal
             }
         }
         const size_t unit0 = (size_t)src * R_total;  // the source slot's first unit
+        // A restore only (no accepted counts): the omitted rows' zeros go out ahead of any
+        // load, so the write stream starts at once (1-2% on sparse checkpoints).
+        if (!n_accept) {
+            float *hp = active_out + l * layer_stride_floats + ((size_t)dst * H + h) * (DK * DV);
+#pragma unroll
+            for (int m = 0; m < RPL; ++m)
+                if (pr[m] < 0) {
+                    omitted |= 1u << m;
+                    st_nt(reinterpret_cast<f32x4 *>(hp + (size_t)(row0 + m) * DV + col0),
+                          f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+                }
+        }
         if constexpr (Q8) {  // every retained row's codes, then its scale
             uint32_t w[RPL];
             float sc[RPL];
@@ -575,6 +589,15 @@ k_restore_tokens(const void *__restrict__ packed, const float *__restrict__ scal
         if (out && rg == 0) store_out4(out + (tok0 + (size_t)t * H) * DV + col0, o);
     }
     float *head_ptr = active_out + l * layer_stride_floats + ((size_t)dst * H + h) * (DK * DV);
+    if (!HU && !n_accept) {  // restore only: the omitted rows are written already
+#pragma unroll
+        for (int m = 0; m < RPL; ++m) {
+            if (omitted >> m & 1u) continue;
+            f32x4 t = {x[m][0], x[m][1], x[m][2], x[m][3]};
+            st_nt(reinterpret_cast<f32x4 *>(head_ptr + (size_t)(row0 + m) * DV + col0), t);
+        }
+        return;
+    }
     tile_store<RPL>(head_ptr, off, DV, x);
 }
 
