@@ -95,7 +95,8 @@ struct TokenRaw {
     float a0, b0;
 };
 
-template <int DK, int DV, typename TIn, bool VEC>
+// RD: the token's readout is wanted (q is read only then).
+template <int DK, int DV, typename TIn, bool VEC, bool RD = true>
 __device__ __forceinline__ void token_load(const TIn *q, const TIn *k, const TIn *v,
                                            const float *alpha, const float *beta, size_t tok,
                                            int row0, int col0, TokenRaw<DK, TIn, VEC> &R)
@@ -106,7 +107,7 @@ __device__ __forceinline__ void token_load(const TIn *q, const TIn *k, const TIn
 #pragma unroll
     for (int i = 0; i < TR::QW; ++i) {
         R.k[i] = kp[i];
-        R.q[i] = qp[i];
+        if constexpr (RD) R.q[i] = qp[i];
     }
     if constexpr (VEC) {
         const u32x4 *ap = reinterpret_cast<const u32x4 *>(alpha + tok * DK + row0);
@@ -157,9 +158,11 @@ __device__ __forceinline__ float raw_row(const u32x4 (&w)[QW], int m)
 // One token's update of a lane's tile.  x[m][c] is row (rg*RPL + m), column
 // (slice + 4*cg + c); k, q and a per-channel decay are read from the token's
 // raw words row by row.  Returns the readout for the lane's 4 columns (valid
-// in every lane).  Shared by the step and the replay kernels so that a replay
-// is bitwise identical to the same number of single steps.
-template <int DK, typename TIn, bool VEC>
+// in every lane) when RD; without it the readout's terms are not formed at all
+// (a third of the token's arithmetic), and the state is the same bits.  Shared
+// by the step and the replay kernels so that a replay is bitwise identical to
+// the same number of single steps.
+template <int DK, typename TIn, bool VEC, bool RD = true>
 __device__ __forceinline__ void tile_token_raw(float (&x)[DK / 8][4],
                                                const TokenRaw<DK, TIn, VEC> &R,
                                                const float (&vv)[4], float beta, float (&o)[4])
@@ -172,26 +175,30 @@ __device__ __forceinline__ void tile_token_raw(float (&x)[DK / 8][4],
     for (int m = 0; m < RPL; ++m) {
         float a = R.a0;
         if constexpr (VEC) a = raw_row<float, RPL / 4>(R.a, m);
-        const float km = raw_row<TIn, QW>(R.k, m), qm = raw_row<TIn, QW>(R.q, m);
+        const float km = raw_row<TIn, QW>(R.k, m);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             x[m][c] = x[m][c] * a;             // S' = Lambda S
             r[c] = fmaf(km, x[m][c], r[c]);    // partial (S'^T k)_j
-            p[c] = fmaf(qm, x[m][c], p[c]);    // partial (S'^T q)_j
         }
-        qk = fmaf(qm, km, qk);
+        if constexpr (RD) {
+            const float qm = raw_row<TIn, QW>(R.q, m);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) p[c] = fmaf(qm, x[m][c], p[c]);  // partial (S'^T q)_j
+            qk = fmaf(qm, km, qk);
+        }
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         r[c] = sum_lane_bits<3>(r[c]);
-        p[c] = sum_lane_bits<3>(p[c]);
+        if constexpr (RD) p[c] = sum_lane_bits<3>(p[c]);
     }
-    qk = sum_lane_bits<3>(qk);
+    if constexpr (RD) qk = sum_lane_bits<3>(qk);
     float u[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         u[c] = beta * (vv[c] - r[c]);   // u = beta (v - S'^T k)
-        o[c] = fmaf(qk, u[c], p[c]);    // o = S'^T q + (q.k) u = S^T q
+        o[c] = RD ? fmaf(qk, u[c], p[c]) : 0.0f;  // o = S'^T q + (q.k) u = S^T q
     }
 #pragma unroll
     for (int m = 0; m < RPL; ++m) {
@@ -258,20 +265,22 @@ k_delta_step(float *__restrict__ state, int n_slots, const int32_t *__restrict__
 // with the state tile's loads; the token loop then reads each token from LDS.  So the
 // tokens cost one memory round trip per workgroup instead of one each, which matters
 // most for a head that starts from zero (no state read to hide the token loads behind).
-// Token t takes WG consecutive 16-byte words: q, k, v and (per-channel decay) alpha, as
-// stored; the scalar decay and beta sit in one float2 per token after the K tokens.
+// Token t takes WG consecutive 16-byte words: q (only when readouts are wanted), k, v and
+// (per-channel decay) alpha, as stored; the scalar decay and beta sit in one float2 per
+// token after the K tokens.
 // The staging costs a workgroup barrier, which ties the head's waves together (each
 // otherwise streams its column slice on its own): with a state read to hide the token
 // loads behind, it pays from about 7 accepted tokens on (measured over 1-8), so fewer
 // are loaded token by token as in the step.
 constexpr int kStageMinTokens = 7;
 
-template <int DK, int DV, typename TIn, bool VEC>
+template <int DK, int DV, typename TIn, bool VEC, bool RD>
 struct TokenLds {
-    static constexpr int QB = DK * (int)sizeof(TIn) / 16;  // words of q (and of k)
+    static constexpr int QB = DK * (int)sizeof(TIn) / 16;  // words of k (and of q)
+    static constexpr int Q0 = RD ? QB : 0;                 // words of q staged
     static constexpr int VB = DV * (int)sizeof(TIn) / 16;  // words of v
     static constexpr int AB = VEC ? DK * 4 / 16 : 0;        // words of a vector decay
-    static constexpr int WG = 2 * QB + VB + AB;            // words per token
+    static constexpr int WG = Q0 + QB + VB + AB;           // words per token
     static size_t bytes(int K) { return (size_t)K * (WG * 16 + sizeof(float2)); }
 };
 
@@ -280,12 +289,12 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Issue the staging copies of tokens [0, nb) of workgroup (ln, h); every wave of the
 // workgroup takes 64 words per pass.  The LDS address of a wave's copy is wave-uniform.
-template <int DK, int DV, typename TIn, bool VEC>
+template <int DK, int DV, typename TIn, bool VEC, bool RD>
 __device__ __forceinline__ void stage_tokens(uint8_t *lds, int nb, size_t tok0, int H,
                                              const TIn *q, const TIn *k, const TIn *v,
                                              const float *alpha, const float *beta, int K)
 {
-    using T = TokenLds<DK, DV, TIn, VEC>;
+    using T = TokenLds<DK, DV, TIn, VEC, RD>;
     constexpr int NW = 2 * DV / 64;  // waves per workgroup
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int total = nb * T::WG;
@@ -295,15 +304,15 @@ __device__ __forceinline__ void stage_tokens(uint8_t *lds, int nb, size_t tok0, 
             const int t = f / T::WG, i = f - t * T::WG;
             const size_t tok = tok0 + (size_t)t * H;
             const uint8_t *src;
-            if (i < T::QB)
+            if (i < T::Q0)
                 src = reinterpret_cast<const uint8_t *>(q + tok * DK) + i * 16;
-            else if (i < 2 * T::QB)
-                src = reinterpret_cast<const uint8_t *>(k + tok * DK) + (i - T::QB) * 16;
-            else if (i < 2 * T::QB + T::VB)
-                src = reinterpret_cast<const uint8_t *>(v + tok * DV) + (i - 2 * T::QB) * 16;
+            else if (i < T::Q0 + T::QB)
+                src = reinterpret_cast<const uint8_t *>(k + tok * DK) + (i - T::Q0) * 16;
+            else if (i < T::Q0 + T::QB + T::VB)
+                src = reinterpret_cast<const uint8_t *>(v + tok * DV) + (i - T::Q0 - T::QB) * 16;
             else
                 src = reinterpret_cast<const uint8_t *>(alpha + tok * DK) +
-                      (i - 2 * T::QB - T::VB) * 16;
+                      (i - T::Q0 - T::QB - T::VB) * 16;
             __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(lds + (size_t)w0 * 16), 16, 0,
                                              0);
         }
@@ -316,28 +325,29 @@ __device__ __forceinline__ void stage_tokens(uint8_t *lds, int nb, size_t tok0, 
 }
 
 // Token t's per-lane inputs from LDS, in the layout token_load gives.
-template <int DK, int DV, typename TIn, bool VEC>
+template <int DK, int DV, typename TIn, bool VEC, bool RD>
 __device__ __forceinline__ void token_from_lds(const uint8_t *lds, int t, int K, int row0,
                                                int col0, TokenRaw<DK, TIn, VEC> &R)
 {
-    using T = TokenLds<DK, DV, TIn, VEC>;
+    using T = TokenLds<DK, DV, TIn, VEC, RD>;
     using TR = TokenRaw<DK, TIn, VEC>;
+    constexpr int K0 = T::Q0, V0 = T::Q0 + T::QB, A0 = V0 + T::VB;  // first words of k, v, a
     const u32x4 *w = reinterpret_cast<const u32x4 *>(lds) + (size_t)t * T::WG;
     const int r = row0 * (int)sizeof(TIn) / 16;
 #pragma unroll
     for (int i = 0; i < TR::QW; ++i) {
-        R.q[i] = w[r + i];
-        R.k[i] = w[T::QB + r + i];
+        if constexpr (RD) R.q[i] = w[r + i];
+        R.k[i] = w[K0 + r + i];
     }
     if constexpr (VEC) {
 #pragma unroll
-        for (int i = 0; i < TR::RPL / 4; ++i) R.a[i] = w[2 * T::QB + T::VB + row0 / 4 + i];
+        for (int i = 0; i < TR::RPL / 4; ++i) R.a[i] = w[A0 + row0 / 4 + i];
     }
     if constexpr (sizeof(TIn) == 2)
-        R.v2 = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint8_t *>(w + 2 * T::QB) +
+        R.v2 = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint8_t *>(w + V0) +
                                                 col0 * 2);
     else
-        R.v4 = w[2 * T::QB + col0 / 4];
+        R.v4 = w[V0 + col0 / 4];
     const float2 ab = reinterpret_cast<const float2 *>(lds + (size_t)K * T::WG * 16)[t];
     R.a0 = ab.x;
     R.b0 = ab.y;
@@ -351,7 +361,7 @@ __device__ __forceinline__ void token_from_lds(const uint8_t *lds, int t, int K,
 //                and written once, and not touched when n_b = 0;
 //   MODE_BONUS   the same, then the target model's bonus token ([B, H, .]
 //                inputs, applied also when n_b = 0), then one write.
-template <int DK, int DV, typename TIn, typename TOut, bool VEC, int MODE>
+template <int DK, int DV, typename TIn, typename TOut, bool VEC, int MODE, bool RD>
 __global__ void __launch_bounds__(2 * DV)
 k_tokens(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slot, int H, int K,
          const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
@@ -389,22 +399,22 @@ k_tokens(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
     const size_t tok0 = (size_t)b * K * H + h;  // token t of (b, h) is tok0 + t * H
     const bool staged = n >= kStageMinTokens;  // uniform over the workgroup
     if (staged) {
-        stage_tokens<DK, DV, TIn, VEC>(tok_lds, n, tok0, H, q, k, v, alpha, beta, K);
+        stage_tokens<DK, DV, TIn, VEC, RD>(tok_lds, n, tok0, H, q, k, v, alpha, beta, K);
         __builtin_amdgcn_s_waitcnt(0);  // the copies into LDS (and the tile) have landed
         __syncthreads();
     }
     for (int t = 0; t < n; ++t) {
         TokenRaw<DK, TIn, VEC> raw;
         if (staged)
-            token_from_lds<DK, DV, TIn, VEC>(tok_lds, t, K, row0, col0, raw);
+            token_from_lds<DK, DV, TIn, VEC, RD>(tok_lds, t, K, row0, col0, raw);
         else
-            token_load<DK, DV, TIn, VEC>(q, k, v, alpha, beta, tok0 + (size_t)t * H, row0, col0,
-                                         raw);
+            token_load<DK, DV, TIn, VEC, RD>(q, k, v, alpha, beta, tok0 + (size_t)t * H, row0,
+                                             col0, raw);
         float vv[4];
         token_v<TIn>(raw.v2, raw.v4, vv);
         float o[4];
-        tile_token_raw<DK, TIn, VEC>(x, raw, vv, raw.b0, o);
-        if (out && rg == 0) store_out4(out + (tok0 + (size_t)t * H) * DV + col0, o);
+        tile_token_raw<DK, TIn, VEC, RD>(x, raw, vv, raw.b0, o);
+        if (RD && out && rg == 0) store_out4(out + (tok0 + (size_t)t * H) * DV + col0, o);
     }
     if constexpr (MODE == MODE_BONUS) {
         TokenRaw<DK, TIn, VEC> raw;
@@ -431,7 +441,7 @@ k_tokens(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
 // Same lane layout and per-token function as the step, so the result is bitwise that of
 // dasc_restore followed by replay_accepted.  With n_accept NULL it is a restore only (the
 // INT8 restore of sparse checkpoints by blocks of 128 rows, H then counting blocks).
-template <int DK, int DV, typename TIn, typename TOut, bool VEC, bool HU, bool Q8>
+template <int DK, int DV, typename TIn, typename TOut, bool VEC, bool HU, bool Q8, bool RD>
 __global__ void __launch_bounds__(2 * DV)
 k_restore_tokens(const void *__restrict__ packed, const float *__restrict__ scales, int S_ckpt,
                  int R_total, const int32_t *__restrict__ unit_pos, int log2_ur, int N,
@@ -575,18 +585,18 @@ k_restore_tokens(const void *__restrict__ packed, const float *__restrict__ scal
     }
     const size_t tok0 = (size_t)ln * K * H + h;  // token t of (l, n, h) is tok0 + t * H
     if (nb > 0) {  // uniform over the workgroup
-        stage_tokens<DK, DV, TIn, VEC>(tok_lds, nb, tok0, H, q, k, v, alpha, beta, K);
+        stage_tokens<DK, DV, TIn, VEC, RD>(tok_lds, nb, tok0, H, q, k, v, alpha, beta, K);
         __builtin_amdgcn_s_waitcnt(0);  // the copies into LDS (and the tile) have landed
         __syncthreads();
     }
     for (int t = 0; t < nb; ++t) {
         TokenRaw<DK, TIn, VEC> raw;
-        token_from_lds<DK, DV, TIn, VEC>(tok_lds, t, K, row0, col0, raw);
+        token_from_lds<DK, DV, TIn, VEC, RD>(tok_lds, t, K, row0, col0, raw);
         float vv[4];
         token_v<TIn>(raw.v2, raw.v4, vv);
         float o[4];
-        tile_token_raw<DK, TIn, VEC>(x, raw, vv, raw.b0, o);
-        if (out && rg == 0) store_out4(out + (tok0 + (size_t)t * H) * DV + col0, o);
+        tile_token_raw<DK, TIn, VEC, RD>(x, raw, vv, raw.b0, o);
+        if (RD && out && rg == 0) store_out4(out + (tok0 + (size_t)t * H) * DV + col0, o);
     }
     float *head_ptr = active_out + l * layer_stride_floats + ((size_t)dst * H + h) * (DK * DV);
     if (!HU && !n_accept) {  // restore only: the omitted rows are written already
@@ -603,17 +613,30 @@ k_restore_tokens(const void *__restrict__ packed, const float *__restrict__ scal
 
 // ----------------------------------------------------------------- dispatch
 
-template <int DK, int DV, typename TIn, typename TOut, bool VEC, int MODE>
-static void launch_tokens(const StepArgs &a, int32_t *err, hipStream_t st)
+template <int DK, int DV, typename TIn, typename TOut, bool VEC, int MODE, bool RD>
+static void launch_tokens_rd(const StepArgs &a, int32_t *err, hipStream_t st)
 {
     const dim3 grid((unsigned)((size_t)a.B * a.H)), block(2 * DV);
     // no request can reach the staging threshold when K is below it: no LDS then
-    const size_t lds = a.K >= kStageMinTokens ? TokenLds<DK, DV, TIn, VEC>::bytes(a.K) : 0;
-    hipLaunchKernelGGL((k_tokens<DK, DV, TIn, TOut, VEC, MODE>), grid, block, lds, st, a.state,
-                       a.n_slots, a.slot, a.H, a.K, (const TIn *)a.q, (const TIn *)a.k,
+    const size_t lds = a.K >= kStageMinTokens ? TokenLds<DK, DV, TIn, VEC, RD>::bytes(a.K) : 0;
+    hipLaunchKernelGGL((k_tokens<DK, DV, TIn, TOut, VEC, MODE, RD>), grid, block, lds, st,
+                       a.state, a.n_slots, a.slot, a.H, a.K, (const TIn *)a.q, (const TIn *)a.k,
                        (const TIn *)a.v, a.alpha, a.beta, a.n_accept, (TOut *)a.out,
                        (const TIn *)a.qb, (const TIn *)a.kb, (const TIn *)a.vb, a.alpha_b,
                        a.beta_b, (TOut *)a.out_b, err);
+}
+
+// A replay without readouts (a NULL out) forms no readout terms and reads no q, and
+// writes nothing of its output type.  The replay + bonus keeps the drafts' terms either
+// way: without them it measured 3% slower (381 against 371 us on the checkpoint
+// workload's 512 requests), the bonus token's loads then being exposed later.
+template <int DK, int DV, typename TIn, typename TOut, bool VEC, int MODE>
+static void launch_tokens(const StepArgs &a, int32_t *err, hipStream_t st)
+{
+    if constexpr (MODE == MODE_REPLAY) {
+        if (!a.out) return launch_tokens_rd<DK, DV, TIn, float, VEC, MODE, false>(a, err, st);
+    }
+    launch_tokens_rd<DK, DV, TIn, TOut, VEC, MODE, true>(a, err, st);
 }
 
 template <int DK, int DV, typename TIn, typename TOut, bool VEC>
@@ -654,15 +677,15 @@ static int launch_dtypes(const StepArgs &a, int32_t *err, hipStream_t st)
 #undef HLA_STEP_OUT
 }
 
-template <int DK, int DV, typename TIn, typename TOut, bool VEC>
-static void launch_restore_tokens(const RestoreReplayArgs &a, int32_t *err, hipStream_t st)
+template <int DK, int DV, typename TIn, typename TOut, bool VEC, bool RD>
+static void launch_restore_tokens_rd(const RestoreReplayArgs &a, int32_t *err, hipStream_t st)
 {
     const dim3 grid((unsigned)((size_t)a.L * a.N * a.H)), block(2 * DV);
-    const size_t lds = TokenLds<DK, DV, TIn, VEC>::bytes(a.K);
+    const size_t lds = TokenLds<DK, DV, TIn, VEC, RD>::bytes(a.K);
     const int lr = log2_exact(a.unit_rows);
 #define HLA_RT_LAUNCH(HU_, Q8_)                                                               \
-    hipLaunchKernelGGL((k_restore_tokens<DK, DV, TIn, TOut, VEC, HU_, Q8_>), grid, block, lds, \
-                       st, a.packed, a.scales, a.S_ckpt, a.R_total, a.unit_pos, lr, a.N,        \
+    hipLaunchKernelGGL((k_restore_tokens<DK, DV, TIn, TOut, VEC, HU_, Q8_, RD>), grid, block,  \
+                       lds, st, a.packed, a.scales, a.S_ckpt, a.R_total, a.unit_pos, lr, a.N,   \
                        a.src_slot, a.dst_slot, a.active_out, a.layer_stride_bytes / 4, a.S_dst, \
                        a.H, a.K, (const TIn *)a.q, (const TIn *)a.k, (const TIn *)a.v, a.alpha, \
                        a.beta, a.n_accept, (TOut *)a.out, err)
@@ -675,6 +698,15 @@ static void launch_restore_tokens(const RestoreReplayArgs &a, int32_t *err, hipS
         else HLA_RT_LAUNCH(false, false);
     }
 #undef HLA_RT_LAUNCH
+}
+
+// With readouts, or without (a NULL out: their terms are never formed, nothing of the
+// output type is written).
+template <int DK, int DV, typename TIn, typename TOut, bool VEC>
+static void launch_restore_tokens(const RestoreReplayArgs &a, int32_t *err, hipStream_t st)
+{
+    if (a.out) launch_restore_tokens_rd<DK, DV, TIn, TOut, VEC, true>(a, err, st);
+    else launch_restore_tokens_rd<DK, DV, TIn, float, VEC, false>(a, err, st);
 }
 
 // The INT8 checkpoint restore by blocks of 128 rows (the fused kernel with no tokens): a

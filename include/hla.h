@@ -289,7 +289,8 @@ HLA_API int dasc_restore(const void *packed, int S_ckpt, int R_total, const int3
  * n_accept device int32 [B]; values outside [0, K] are clamped and set
  *          HLA_DEVERR_ACCEPT.
  * out      device [B, K, H, dv] of out_dtype or NULL: the readout after each
- *          replayed token; rows t >= n_b are left untouched.
+ *          replayed token; rows t >= n_b are left untouched.  With NULL the
+ *          readout is not formed and q is not read (it must still be given).
  * 1 <= K <= 16.  state, slot, err_flag as gdn_step.
  * Errors: as gdn_step, plus SHAPE for K outside [1, 16] and NULL for a
  * missing n_accept.
@@ -309,7 +310,8 @@ HLA_API int replay_accepted(float *state, int n_slots, const int32_t *slot, int 
  * bonus token's own projections, all on one read and one write of the state.
  * The bonus token is applied for every live request, also when n_b = 0.
  *
- * q .. n_accept, out  as replay_accepted (out may be NULL).
+ * q .. n_accept, out  as replay_accepted (out may be NULL: no draft
+ *                     readouts; the drafts' q is read either way).
  * q_bonus, k_bonus    device [B, H, dk]; v_bonus [B, H, dv] (in_dtype).
  * alpha_bonus         device float32 [B, H] or [B, H, dk] (decay_kind).
  * beta_bonus          device float32 [B, H].
@@ -361,7 +363,8 @@ HLA_API int replay_accepted_bonus(float *state, int n_slots, const int32_t *slot
  *             replays the same count); values outside [0, K] are clamped and set
  *             HLA_DEVERR_ACCEPT.
  * out         device [L, N, K, H, dv] of out_dtype, or NULL: the readout after
- *             each replayed token; rows t >= n_b are left untouched.
+ *             each replayed token; rows t >= n_b are left untouched.  With NULL
+ *             the readouts are not formed and q is not read.
  * 1 <= K <= 16; dk, dv in {64, 128}; layer_stride_bytes a multiple of 16 and
  * >= S_dst * H * dk * dv * 4.
  * Errors: NULL, SHAPE (including unit_rows), ALIGN, DTYPE, UNSUPPORTED, PLAN

@@ -53,9 +53,11 @@ def test_speculative_bytes_recounted():
     n = np.array([0, 3, 8, 1], np.int32)
     H, dk, dv = 2, 64, 32
     tok_in = (2 * dk + dv) * 4 + 4 + 4           # fp32 q, k, v, scalar decay, beta
+    tok_nr = (dk + dv) * 4 + 4 + 4               # no readout: q not read
     # replay: states with at least one accepted token read + written, accepted tokens'
     # inputs read and readouts written
     assert bench.replay_bytes(n, H, dk, dv, 4) == 3 * H * 2 * dk * dv * 4 + 12 * H * (tok_in + dv * 4)
+    assert bench.replay_bytes(n, H, dk, dv, 4, False) == 3 * H * 2 * dk * dv * 4 + 12 * H * tok_nr
     # verify: every state read once, every draft's inputs read and readout written
     assert bench.verify_bytes(4, 8, H, dk, dv, 4) == 4 * H * dk * dv * 4 + 4 * 8 * H * (tok_in + dv * 4)
     # replay + bonus: every state read + written, accepted inputs read, bonus in + out
@@ -67,17 +69,19 @@ def test_fused_restore_replay_bytes_recounted():
     n = np.array([0, 3, 8, 1], np.int32)
     S, R, L, H, dk, dv = 4, 5, 3, 2, 64, 32
     head = dk * dv * 4
-    tok_in = (2 * dk + dv) * 4 + 4 + 4
+    tok_in = (dk + dv) * 4 + 4 + 4               # k, v, scalar decay, beta: no readout
     # retained checkpoint heads read once, every private head written once, each layer's
     # accepted tokens' inputs read
     want = S * R * head + L * S * H * head + L * 12 * H * tok_in
+    assert bench.restore_replay_bytes(n, S, R, L, H, dk, dv, 4, readout=True) == (
+        want + L * 12 * H * (dk * 4 + dv * 4))
     assert bench.restore_replay_bytes(n, S, R, L, H, dk, dv, 4) == want
     # the separate calls move every live state (3 of 4 requests) once more per layer, in
     # and out
     two = (S * R * head + L * S * H * head) + L * bench.replay_bytes(n, H, dk, dv, 4, False)
     assert two - want == L * 3 * H * 2 * head
     # units of single key channels (R of them), per-channel decay read with each token
-    tok_kda = (2 * dk + dv) * 4 + dk * 4 + 4
+    tok_kda = (dk + dv) * 4 + dk * 4 + 4
     assert bench.restore_replay_bytes(n, S, R, L, H, dk, dv, 4, unit_rows=1,
                                       vector_decay=True) == (S * R * dv * 4 + L * S * H * head
                                                              + L * 12 * H * tok_kda)

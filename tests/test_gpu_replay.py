@@ -55,6 +55,39 @@ def test_replay_matches_oracle_with_clamping(kind, in_dtype, dk, dv, K):
 
 
 @pytest.mark.parametrize("kind", ["gdn", "kda"])
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 128), (128, 64)])
+def test_replay_without_readouts_gives_the_same_state(kind, in_dtype, dk, dv):
+    """Without readouts (out NULL) the replay skips the readout terms and q; the state
+    must be the same bits as with readouts, for requests loaded token by token and for
+    those staged in LDS (7 or more of K = 12 accepted).  The replay + bonus without draft
+    readouts: the same state and the same bonus readout as with them."""
+    hla = need_gpu()
+    cfg = _cfg(kind, dk, dv, in_dtype, B=8, K=12)
+    x = synth.replay_inputs(cfg, 2)
+    xb = synth.step_inputs(cfg, 77)
+    n_acc = dev(np.array([0, 1, 3, 6, 7, 9, 12, 12], np.int32))
+    S0 = synth.initial_state(cfg)
+    xd = dev_inputs({n: x[n] for n in ("q", "k", "v", "alpha", "beta")}, in_dtype)
+    bd = dev_inputs({n: xb[n] for n in ("q", "k", "v", "alpha", "beta")}, in_dtype)
+    vec = 1 if kind == "kda" else 0
+    with_o, without = dev(S0), dev(S0)
+    hla.replay_accepted(with_o, xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], n_acc, vec)
+    hla.replay_accepted(without, xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], n_acc, vec,
+                        want_out=False)
+    assert torch.equal(with_o, without)
+    with_o, without = dev(S0), dev(S0)
+    drafts_out = torch.empty((cfg.B, cfg.K, cfg.H, dv), device="cuda")
+    ob1 = hla.replay_accepted_bonus(with_o, xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"],
+                                    n_acc, vec, bd["q"], bd["k"], bd["v"], bd["alpha"],
+                                    bd["beta"], out=drafts_out)
+    ob2 = hla.replay_accepted_bonus(without, xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"],
+                                    n_acc, vec, bd["q"], bd["k"], bd["v"], bd["alpha"],
+                                    bd["beta"])
+    assert torch.equal(with_o, without) and torch.equal(ob1, ob2)
+
+
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
 def test_fused_replay_is_bitwise_equal_to_single_steps(kind):
     """Token t of every request is applied by one step call whose slot map pads out the
     requests with n_b <= t; the fused replay must give the same bits."""

@@ -532,6 +532,69 @@ def test_restore_int8_replay_matches_oracle_and_chain(kind, dk, dv, in_dtype, un
     assert (host(st)[:, [1, 4]] == 7.0).all()
 
 
+@pytest.mark.parametrize("kind,dk,dv,in_dtype", [("gdn", 128, 128, "bf16"),
+                                                 ("kda", 128, 128, "f32"),
+                                                 ("gdn", 64, 128, "f16"),
+                                                 ("kda", 128, 64, "bf16")])
+@pytest.mark.parametrize("unit_rows", [1, "dk"])
+@pytest.mark.parametrize("q8", [False, True])
+def test_restore_replay_without_readouts(kind, dk, dv, in_dtype, unit_rows, q8):
+    """With out NULL the fused restore + replay forms no readout terms and reads no q: the
+    private state must be the same bits as with readouts, and as the restore followed by
+    replays without readouts (FP32 and INT8 checkpoints, head and channel-row units, 0 to
+    K accepted drafts)."""
+    hla = need_gpu()
+    ur = dk if unit_rows == "dk" else unit_rows
+    cfg = _cfg(kind, dk, dv, in_dtype, K=8, L=2, S=5, seed=29 + ur)
+    L, H = cfg.L, cfg.H
+    n_units = H * dk // ur
+    src = np.array([4, 0, 2, 1, 3], np.int32)
+    dst = np.array([2, 5, 0, 3, 1], np.int32)
+    n_acc = np.array([8, 0, 3, 7, 6], np.int32)  # staged in LDS by every fused call
+    S_dst = 6
+    x = _drafts(cfg, len(src))
+    xd = dev_inputs(x, in_dtype)
+    vec = 1 if kind == "kda" else 0
+    src_d, dst_d, n_d = dev(src), dev(dst), dev(n_acc)
+    stride = S_dst * H * dk * dv * 4
+    if q8:
+        codes, scales, _, _, unit_pos, R = _int8_checkpoint(cfg, ur, 0.4, 50 + ur)
+        codes_d, scales_d = dev(codes), dev(scales)
+        pos = dev(unit_pos.reshape(-1))
+        st, _, _ = _fused8(hla, cfg, codes_d, scales_d, unit_pos, src, dst, S_dst, xd, n_acc,
+                           "f32", 7.0)
+
+        def fused_nr(s_):
+            hla.dasc_restore_int8_replay(codes_d, scales_d, pos, src_d, dst_d, s_, xd["q"],
+                                         xd["k"], xd["v"], xd["alpha"], xd["beta"], n_d, vec)
+
+        def restore(s_):
+            hla.dasc_restore_int8(codes_d, scales_d, cfg.slots, R, pos, L, n_units, ur, dv,
+                                  src_d, dst_d, s_, stride, S_dst)
+    else:
+        packed, _, _, unit_pos, R = _row_checkpoint(cfg, ur, 0.4, 50 + ur)
+        packed_d = dev(packed.view(np.float32).reshape(cfg.slots, R, ur * dv))
+        pos = dev(unit_pos.reshape(-1))
+        st, _, _ = _fused(hla, cfg, packed_d, unit_pos, src, dst, S_dst, xd, n_acc, "f32", 7.0)
+
+        def fused_nr(s_):
+            hla.dasc_restore_replay(packed_d, pos, src_d, dst_d, s_, xd["q"], xd["k"], xd["v"],
+                                    xd["alpha"], xd["beta"], n_d, vec)
+
+        def restore(s_):
+            hla.dasc_restore(packed_d, cfg.slots, R, pos, L, n_units, ur * dv * 4, src_d, dst_d,
+                             s_, stride, S_dst)
+    st_nr = torch.full_like(st, 7.0)
+    fused_nr(st_nr)
+    assert torch.equal(st_nr, st)
+    st_c = torch.full_like(st, 7.0)
+    restore(st_c)
+    for l in range(L):
+        hla.replay_accepted(st_c[l], xd["q"][l], xd["k"][l], xd["v"][l], xd["alpha"][l],
+                            xd["beta"][l], n_d, vec, slot=dst_d, want_out=False)
+    assert torch.equal(st_c, st)
+
+
 @pytest.mark.parametrize("name", ["dasc_gdn", "dasc_kda"])
 def test_restore_int8_replay_full_size(name):
     """The two checkpoint workloads with INT8 checkpoints (the library's pack of a random
