@@ -576,22 +576,13 @@ int dasc_restore_int8(const int8_t *codes, const float *scales, int S_ckpt, int 
                                                           (int64_t)unit_rows * dv * 4)},
             hla::Range{}, nullptr, L, nullptr, 0, unit_pos, n_units, src_slot, dst_slot, N);
     if (rc != HLA_OK || N == 0) return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    // A sparse checkpoint (at most 3/8 of the units retained) restores faster through
-    // the fused restore + replay kernel with no tokens: there a lane owns 16 consecutive
-    // rows, so its plan lookups are one contiguous read and a wave's stores whole lines,
-    // where this kernel spends one lookup per row.  Same decode, so the same bits.
-    if ((uint64_t)R_total * 8 <= (uint64_t)L * n_units * 3 &&
-        hla::restore_int8_by_blocks(codes, scales, S_ckpt, R_total, unit_pos, L, n_units,
-                                    unit_rows, dv, src_slot, dst_slot, N, active_out,
-                                    layer_stride_bytes, S_dst, err_flag, st))
-        return hipGetLastError() == hipSuccess ? HLA_OK : HLA_ERR_LAUNCH;
     const int lr = hla::log2_exact(unit_rows);
     const hla::FastDiv un = hla::make_fastdiv((uint32_t)n_units);
     const uint64_t rows = ((uint64_t)L * n_units) << lr;
     const int passes = hla::int8_restore_passes(unit_rows);
     const uint64_t per_block = (uint64_t)(hla::kCopyThreads / (dv / 8)) * passes;
     const unsigned bx = (unsigned)((rows + per_block - 1) / per_block);
+    hipStream_t st = static_cast<hipStream_t>(stream);
     for (int p0 = 0; p0 < N; p0 += (int)hla::kMaxGridY) {
         const unsigned by = (unsigned)std::min<int>(N - p0, (int)hla::kMaxGridY);
         const dim3 grid(bx, by), block(hla::kCopyThreads);

@@ -439,8 +439,7 @@ k_tokens(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
 // LDS for every head with n_b > 0: many heads start from zero, with no state read to hide
 // token loads behind, and over the whole workload staging all of them measured fastest.
 // Same lane layout and per-token function as the step, so the result is bitwise that of
-// dasc_restore followed by replay_accepted.  With n_accept NULL it is a restore only (the
-// INT8 restore of sparse checkpoints by blocks of 128 rows, H then counting blocks).
+// dasc_restore followed by replay_accepted.
 template <int DK, int DV, typename TIn, typename TOut, bool VEC, bool HU, bool Q8, bool RD>
 __global__ void __launch_bounds__(2 * DV)
 k_restore_tokens(const void *__restrict__ packed, const float *__restrict__ scales, int S_ckpt,
@@ -462,7 +461,7 @@ k_restore_tokens(const void *__restrict__ packed, const float *__restrict__ scal
         if (err && threadIdx.x == 0) atomicOr(err, HLA_DEVERR_SLOT);
         return;
     }
-    int nb = n_accept ? n_accept[n] : 0;  // no accepted counts: a restore only
+    int nb = n_accept[n];
     if (nb < 0 || nb > K) {
         if (err && threadIdx.x == 0 && h == 0 && l == 0) atomicOr(err, HLA_DEVERR_ACCEPT);
         nb = nb < 0 ? 0 : K;
@@ -473,7 +472,6 @@ k_restore_tokens(const void *__restrict__ packed, const float *__restrict__ scal
     const uint32_t off = (uint32_t)(row0 * DV + col0) * 4;
 
     float x[RPL][4];
-    uint32_t omitted = 0u;  // restore only: rows already written as zeros
     if constexpr (HU) {
         int pos = unit_pos[l * H + h];
         if (pos >= R_total) {  // a bad plan entry: the head starts from zero, as restored
@@ -535,18 +533,6 @@ k_restore_tokens(const void *__restrict__ packed, const float *__restrict__ scal
             }
         }
         const size_t unit0 = (size_t)src * R_total;  // the source slot's first unit
-        // A restore only (no accepted counts): the omitted rows' zeros go out ahead of any
-        // load, so the write stream starts at once (1-2% on sparse checkpoints).
-        if (!n_accept) {
-            float *hp = active_out + l * layer_stride_floats + ((size_t)dst * H + h) * (DK * DV);
-#pragma unroll
-            for (int m = 0; m < RPL; ++m)
-                if (pr[m] < 0) {
-                    omitted |= 1u << m;
-                    st_nt(reinterpret_cast<f32x4 *>(hp + (size_t)(row0 + m) * DV + col0),
-                          f32x4{0.0f, 0.0f, 0.0f, 0.0f});
-                }
-        }
         if constexpr (Q8) {  // every retained row's codes, then its scale
             uint32_t w[RPL];
             float sc[RPL];
@@ -599,15 +585,6 @@ k_restore_tokens(const void *__restrict__ packed, const float *__restrict__ scal
         if (RD && out && rg == 0) store_out4(out + (tok0 + (size_t)t * H) * DV + col0, o);
     }
     float *head_ptr = active_out + l * layer_stride_floats + ((size_t)dst * H + h) * (DK * DV);
-    if (!HU && !n_accept) {  // restore only: the omitted rows are written already
-#pragma unroll
-        for (int m = 0; m < RPL; ++m) {
-            if (omitted >> m & 1u) continue;
-            f32x4 t = {x[m][0], x[m][1], x[m][2], x[m][3]};
-            st_nt(reinterpret_cast<f32x4 *>(head_ptr + (size_t)(row0 + m) * DV + col0), t);
-        }
-        return;
-    }
     tile_store<RPL>(head_ptr, off, DV, x);
 }
 
@@ -707,36 +684,6 @@ static void launch_restore_tokens(const RestoreReplayArgs &a, int32_t *err, hipS
 {
     if (a.out) launch_restore_tokens_rd<DK, DV, TIn, TOut, VEC, true>(a, err, st);
     else launch_restore_tokens_rd<DK, DV, TIn, float, VEC, false>(a, err, st);
-}
-
-// The INT8 checkpoint restore by blocks of 128 rows (the fused kernel with no tokens): a
-// lane holds 16 consecutive rows of its block, so its plan entries are one contiguous
-// read and its stores cover whole 128-byte lines.  For sparse checkpoints of small units
-// it beats the row-per-lane restore kernel; see dasc_restore_int8.
-bool restore_int8_by_blocks(const int8_t *codes, const float *scales, int S_ckpt, int R_total,
-                            const int32_t *unit_pos, int L, int n_units, int unit_rows, int dv,
-                            const int32_t *src_slot, const int32_t *dst_slot, int N,
-                            float *active_out, int64_t layer_stride_bytes, int S_dst,
-                            int32_t *err, void *stream)
-{
-    constexpr int DK = 128;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const int64_t rows = (int64_t)n_units * unit_rows;  // per slot and layer
-    if ((dv != 64 && dv != 128) || unit_rows > DK || rows % DK != 0) return false;
-    const auto a16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-    if (!a16(codes) || !a16(scales) || !a16(unit_pos) || !a16(active_out) ||
-        layer_stride_bytes % 16 != 0)
-        return false;
-    const int64_t blocks = rows / DK;
-    if ((int64_t)L * N * blocks > (int64_t)INT_MAX) return false;
-    RestoreReplayArgs a{true,     codes,     scales,   S_ckpt,  R_total, unit_pos,
-                        L,        unit_rows, src_slot, dst_slot, N,      active_out,
-                        layer_stride_bytes,  S_dst,    (int)blocks, DK,  dv,
-                        1,        nullptr,   nullptr,  nullptr, HLA_F32, nullptr,
-                        HLA_DECAY_SCALAR,    nullptr,  nullptr, nullptr, HLA_F32};
-    if (dv == 128) launch_restore_tokens<DK, 128, float, float, false>(a, err, st);
-    else launch_restore_tokens<DK, 64, float, float, false>(a, err, st);
-    return true;
 }
 
 template <int DK, int DV>

@@ -76,13 +76,12 @@ def test_pack_and_restore_int8(unit_rows, dv, n_units, p_keep):
     (1, 64, 200),    # 200 rows per layer: not whole blocks of 128
 ])
 def test_restore_int8_sparse_checkpoints(unit_rows, dv, n_units):
-    """Checkpoints that retain at most 3/8 of their units, where the restore goes by blocks
-    of 128 rows whenever a layer's rows are whole blocks and the tables 16-byte aligned:
-    bit-exact against the oracle's restore into sentinel-filled slots, with a plan entry
-    past the packed rows (that unit zero, HLA_DEVERR_PLAN) and a pair whose destination is
-    past S_dst (skipped, HLA_DEVERR_SLOT); the same restore with unit_pos and scales at
-    4-byte but not 16-byte alignment gives the same bits; an empty checkpoint restores
-    zeros."""
+    """Sparse checkpoints (a quarter of the units retained) over unit sizes from single
+    channels to whole heads: bit-exact against the oracle's restore into sentinel-filled
+    slots, with a plan entry past the packed rows (that unit zero, HLA_DEVERR_PLAN) and a
+    pair whose destination is past S_dst (skipped, HLA_DEVERR_SLOT); the same restore with
+    unit_pos and scales at 4-byte but not 16-byte alignment gives the same bits; an empty
+    checkpoint restores zeros."""
     hla = need_gpu()
     g = np.random.default_rng(7100 + unit_rows * 10 + dv)
     L, S_ = 3, 5
