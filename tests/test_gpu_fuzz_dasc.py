@@ -172,10 +172,11 @@ def test_refresh_local_device_errors():
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_restore_replay(i):
     """The fused restore + replay on random geometry (layers, heads, head shape, unit size
-    from one key channel to a whole head, draft count, input and readout types, decay kind,
-    masks from empty to full, slot maps, accepted counts with out-of-range values): against
-    the oracle's restore then replay, and bit for bit against the library's restore
-    followed by replay_accepted per layer."""
+    from one key channel to a whole head, draft count, input and readout types or no
+    readouts, decay kind, FP32 or INT8 checkpoints, masks from empty to full, slot maps,
+    accepted counts with out-of-range values): against the oracle's restore then replay,
+    and bit for bit against the library's restore followed by replay_accepted per
+    layer."""
     import oracle_par
 
     hla = need_gpu()
@@ -196,6 +197,12 @@ def test_random_restore_replay(i):
     src, dst = _maps(g, S_ckpt, S_dst)
     N = len(src)
     packed = (g.standard_normal((S_ckpt, R, ur * dv)) * 0.05).astype(np.float32)
+    q8 = bool(g.integers(0, 2))          # an INT8 checkpoint: the state starts as code x scale
+    want_out = bool(g.integers(0, 4))    # three cases in four with readouts
+    if q8:
+        codes = g.integers(-127, 128, size=(S_ckpt, R, ur, dv)).astype(np.int8)
+        scales = (g.uniform(0.5, 2.0, size=(S_ckpt, R, ur)) * 0.05 / 127).astype(np.float32)
+        packed = (codes.astype(np.float32) * scales[..., None]).reshape(S_ckpt, R, ur * dv)
     # inputs: q, k unit vectors, stored in the input type; values the kernel reads exactly
     qk = g.standard_normal((2, L, N, K, H, dk))
     qk /= np.linalg.norm(qk, axis=-1, keepdims=True)
@@ -210,14 +217,20 @@ def test_random_restore_replay(i):
     xd.update(alpha=dev(alpha), beta=dev(beta))
     pk = dev(packed)
     pos = dev(unit_pos.reshape(-1))
+    if q8:
+        cd, sc = dev(codes), dev(scales)
 
     def fused():
         st = torch.full((L, S_dst, H, dk, dv), 3.0, device="cuda")
         out = torch.full((L, N, K, H, dv), 5.0, device="cuda", dtype=tdt[out_dt])
         err = torch.zeros(1, dtype=torch.int32, device="cuda")
-        hla.dasc_restore_replay(pk, pos, dev(src), dev(dst), st, xd["q"], xd["k"], xd["v"],
-                                xd["alpha"], xd["beta"], dev(n_acc), int(vec), out=out,
-                                err_flag=err)
+        args = (pos, dev(src), dev(dst), st, xd["q"], xd["k"], xd["v"], xd["alpha"],
+                xd["beta"], dev(n_acc), int(vec))
+        o = out if want_out else None
+        if q8:
+            hla.dasc_restore_int8_replay(cd, sc, *args, out=o, err_flag=err)
+        else:
+            hla.dasc_restore_replay(pk, *args, out=o, err_flag=err)
         return st, out, int(err.item())
 
     st, out, err = fused()
@@ -226,11 +239,19 @@ def test_random_restore_replay(i):
     st2 = torch.full((L, S_dst, H, dk, dv), 3.0, device="cuda")
     out2 = torch.full((L, N, K, H, dv), 5.0, device="cuda", dtype=tdt[out_dt])
     ub = ur * dv * 4
-    hla.dasc_restore(pk if R else dev(np.zeros(4, np.float32)), S_ckpt, R, pos, L, n_units, ub,
-                     dev(src), dev(dst), st2, S_dst * n_units * ub, S_dst)
+    if q8:
+        hla.dasc_restore_int8(cd if R else dev(np.zeros(16, np.int8)),
+                              sc if R else dev(np.zeros(4, np.float32)), S_ckpt, R, pos, L,
+                              n_units, ur, dv, dev(src), dev(dst), st2, S_dst * n_units * ub,
+                              S_dst)
+    else:
+        hla.dasc_restore(pk if R else dev(np.zeros(4, np.float32)), S_ckpt, R, pos, L,
+                         n_units, ub, dev(src), dev(dst), st2, S_dst * n_units * ub, S_dst)
     for l in range(L):
         hla.replay_accepted(st2[l], xd["q"][l], xd["k"][l], xd["v"][l], xd["alpha"][l],
-                            xd["beta"][l], dev(n_acc), int(vec), out=out2[l], slot=dev(dst))
+                            xd["beta"][l], dev(n_acc), int(vec),
+                            out=out2[l] if want_out else None, slot=dev(dst),
+                            want_out=want_out)
     assert torch.equal(st, st2) and torch.equal(out, out2)
     # the oracle
     got, o = host(st), host(out)
@@ -247,6 +268,9 @@ def test_random_restore_replay(i):
         o_ref, scale = oracle_par.replay_terms(S64, {n: x64[n][l] for n in x64}, n_acc,
                                                per_channel=vec)
         assert oracle_par.rel_err_tiles(got[l][dst], S64) <= 1e-5
+        if not want_out:
+            assert (o[l] == 5.0).all()
+            continue
         rows = np.arange(K)[None, :] < n_eff[:, None]
         e = np.where(rows[:, :, None, None], np.abs(o[l] - o_ref), 0.0).max(axis=-1)
         assert float((e / np.maximum(scale, 1e-30)).max()) <= tol_o

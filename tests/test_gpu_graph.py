@@ -136,13 +136,17 @@ def test_dasc_int8_graph_replays():
     _check_replays(launch, bufs["e"], bufs["g"])
 
 
-def test_restore_replay_graph_replays():
+@pytest.mark.parametrize("q8", [False, True])
+def test_restore_replay_graph_replays(q8):
+    """The fused restore + replay from an FP32 or an INT8 checkpoint, with readouts."""
     hla = need_gpu()
     cfg = synth.shrink(synth.CONFIGS["dasc_gdn"], H=3, dk=64, dv=64, K=4, L=2, slots=4)
     mask = synth.dasc_masks(cfg)
     _, _, unit_pos, R = hla.dasc_plan(mask)
     g = np.random.default_rng(7)
     packed = dev((g.standard_normal((cfg.slots, R, cfg.dk * cfg.dv)) * 0.05).astype(np.float32))
+    codes = dev(g.integers(-127, 128, size=(cfg.slots, R, cfg.dk, cfg.dv)).astype(np.int8))
+    scales = dev((g.uniform(0.5, 2.0, size=(cfg.slots, R, cfg.dk)) * 4e-4).astype(np.float32))
     pos = dev(unit_pos.reshape(-1))
     src = dev(np.array([2, 0, 3], np.int32))
     dst = dev(np.array([1, 3, 0], np.int32))
@@ -155,7 +159,10 @@ def test_restore_replay_graph_replays():
                       torch.zeros((cfg.L, 3, cfg.K, cfg.H, cfg.dv), device="cuda")]
 
     def launch(state, i):
-        hla.dasc_restore_replay(packed, pos, src, dst, state[0], x["q"], x["k"], x["v"],
-                                x["alpha"], x["beta"], n_acc, 0, out=state[1])
+        args = (pos, src, dst, state[0], x["q"], x["k"], x["v"], x["alpha"], x["beta"], n_acc, 0)
+        if q8:
+            hla.dasc_restore_int8_replay(codes, scales, *args, out=state[1])
+        else:
+            hla.dasc_restore_replay(packed, *args, out=state[1])
 
     _check_replays(launch, bufs["e"], bufs["g"])
