@@ -439,7 +439,8 @@ k_tokens(float *__restrict__ state, int n_slots, const int32_t *__restrict__ slo
 // LDS for every head with n_b > 0: many heads start from zero, with no state read to hide
 // token loads behind, and over the whole workload staging all of them measured fastest.
 // Same lane layout and per-token function as the step, so the result is bitwise that of
-// dasc_restore followed by replay_accepted.
+// dasc_restore (Q8: dasc_restore_int8, each retained row code x scale in FP32) followed
+// by replay_accepted.  RD: readouts are written (otherwise their terms are not formed).
 template <int DK, int DV, typename TIn, typename TOut, bool VEC, bool HU, bool Q8, bool RD>
 __global__ void __launch_bounds__(2 * DV)
 k_restore_tokens(const void *__restrict__ packed, const float *__restrict__ scales, int S_ckpt,
