@@ -127,3 +127,18 @@ def test_free_running_figures_only_for_the_recorded_source(tmp_path, monkeypatch
             assert got is None
         else:
             assert got == {"1": {"code_frac": 1e-6, "drift_gpu": 0.007, "drift_oracle": 0.007}}
+
+
+def test_input_copies_span_the_last_level_cache():
+    """Timed launches rotate over copies of their checkpoint / draft inputs: together the
+    copies span at least three times the 256 MB last-level cache, so at least twice the
+    cache is read between two reads of one copy; an input above the cache needs none."""
+    llc = 256 << 20
+    assert bench.LLC_BYTES == llc
+    for nbytes, want in [(266 << 20, 3), (528 << 20, 2), (201_326_592, 4), (2 << 30, 1),
+                         (llc, 3), (1, 3 * llc)]:
+        n = bench.n_copies(nbytes)
+        assert n == want, (nbytes, n)
+        assert n * nbytes >= 3 * llc or n == 1
+        if nbytes <= llc:
+            assert (n - 1) * nbytes >= 2 * llc
