@@ -172,10 +172,12 @@ static void checks()
                 for (int H : {1, 32, INT_MAX})
                     for (int R : {0, 64, INT_MAX})
                         for (int64_t st : strides)
-                        for (int ur : {1, 16, 128}) {
+                        for (int ur : {1, 16, 128})
+                        for (bool q8 : {false, true}) {
                             RestoreReplayArgs rr{};
-                            rr.unit_rows = ur;
-                            rr.packed = (const float *)fake(1), rr.S_ckpt = S, rr.R_total = R;
+                            rr.q8 = q8, rr.unit_rows = ur;
+                            rr.packed = fake(1), rr.S_ckpt = S, rr.R_total = R;
+                            rr.scales = q8 ? (const float *)fake(13) : nullptr;
                             rr.unit_pos = (const int32_t *)fake(2), rr.L = L;
                             rr.src_slot = (const int32_t *)fake(3);
                             rr.dst_slot = (const int32_t *)fake(4), rr.N = N;
