@@ -164,6 +164,15 @@ struct RestoreReplayArgs {
 
 int check_restore_replay(const RestoreReplayArgs &a);
 
+// The INT8 checkpoint restore (arguments validated as dasc_restore_int8's) through the
+// fused restore + replay kernel with no tokens, by blocks of 128 rows.  Returns false,
+// with nothing launched, when the geometry or the alignment does not fit that kernel.
+bool restore_int8_by_blocks(const int8_t *codes, const float *scales, int S_ckpt, int R_total,
+                            const int32_t *unit_pos, int L, int n_units, int unit_rows, int dv,
+                            const int32_t *src_slot, const int32_t *dst_slot, int N,
+                            float *active_out, int64_t layer_stride_bytes, int S_dst,
+                            int32_t *err, void *stream);
+
 // log2 of a power of two (checked by the caller).
 inline int log2_exact(int x)
 {

@@ -69,7 +69,8 @@ def test_pack_and_restore_int8(unit_rows, dv, n_units, p_keep):
 
 @pytest.mark.parametrize("unit_rows,dv,n_units", [
     (1, 128, 384),   # channel rows, three heads per layer
-    (2, 64, 192),
+    (2, 64, 192),    # units of 2-8 rows: restored by blocks of 128 rows
+    (4, 128, 96),
     (8, 128, 48),
     (32, 64, 12),
     (128, 128, 3),   # whole heads
@@ -77,11 +78,12 @@ def test_pack_and_restore_int8(unit_rows, dv, n_units, p_keep):
 ])
 def test_restore_int8_sparse_checkpoints(unit_rows, dv, n_units):
     """Sparse checkpoints (a quarter of the units retained) over unit sizes from single
-    channels to whole heads: bit-exact against the oracle's restore into sentinel-filled
+    channels to whole heads (units of 2-8 rows take the restore by blocks of 128 rows,
+    the rest the row kernel): bit-exact against the oracle's restore into sentinel-filled
     slots, with a plan entry past the packed rows (that unit zero, HLA_DEVERR_PLAN) and a
     pair whose destination is past S_dst (skipped, HLA_DEVERR_SLOT); the same restore with
-    unit_pos and scales at 4-byte but not 16-byte alignment gives the same bits; an empty
-    checkpoint restores zeros."""
+    unit_pos and scales at 4-byte but not 16-byte alignment (the row kernel) gives the same
+    bits; an empty checkpoint restores zeros."""
     hla = need_gpu()
     g = np.random.default_rng(7100 + unit_rows * 10 + dv)
     L, S_ = 3, 5
